@@ -1,0 +1,150 @@
+"""ctypes marshalling for the C oracle (``tq_oracle.c``).
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).  Every numeric step is in
+the C file; this module converts numpy arrays to pointers and error codes to
+exceptions.
+"""
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+TERNARY = 0
+BINARY = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tq_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+_ERRORS = {1: "null pointer", 2: "bad shape", 3: "group must be 128",
+           4: "unknown variant", 5: "value outside the variant's set",
+           6: "invalid code 3", 7: "out of memory"}
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code, index=None):
+        self.code = code
+        self.index = index
+        msg = _ERRORS.get(code, "error %d" % code)
+        if index is not None:
+            msg += " at flat index %d" % index
+        super().__init__(msg)
+
+
+def build(lib_path=_LIB, extra_flags=(), src=_SRC):
+    """Compile the oracle with gcc (-O2 -fopenmp, no fast-math)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+           *extra_flags, src, "-o", lib_path + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(lib_path + ".tmp", lib_path)
+    return lib_path
+
+
+_lib_cache = {}
+
+
+def load(lib_path=_LIB):
+    """Load (building first if absent) the oracle shared library."""
+    if lib_path in _lib_cache:
+        return _lib_cache[lib_path]
+    if not os.path.exists(lib_path) or (
+            lib_path == _LIB and os.path.getmtime(lib_path) < os.path.getmtime(_SRC)):
+        build(lib_path)
+    lib = ctypes.CDLL(lib_path)
+    i64, i32, ci = ctypes.c_int64, ctypes.c_int32, ctypes.c_int
+    vp = ctypes.c_void_p
+    lib.oracle_half_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_half_to_double.restype = ctypes.c_double
+    lib.oracle_codes_bytes.argtypes = [i64, i64, ci]
+    lib.oracle_codes_bytes.restype = i64
+    lib.oracle_scales_count.argtypes = [i64, i64, i32]
+    lib.oracle_scales_count.restype = i64
+    lib.oracle_pack.argtypes = [vp, i64, i64, i32, ci, vp, ctypes.POINTER(i64)]
+    lib.oracle_pack.restype = ci
+    lib.oracle_unpack.argtypes = [vp, i64, i64, i32, ci, vp, ctypes.POINTER(i64)]
+    lib.oracle_unpack.restype = ci
+    lib.oracle_gemm.argtypes = [vp, vp, vp, i64, i64, i64, i32, ci, vp, vp, ci]
+    lib.oracle_gemm.restype = ci
+    _lib_cache[lib_path] = lib
+    return lib
+
+
+def default_threads():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _ptr(a):
+    return ctypes.c_void_p(a.ctypes.data) if a is not None else None
+
+
+def half_to_double(bits, lib=None):
+    lib = lib or load()
+    return lib.oracle_half_to_double(int(bits) & 0xFFFF)
+
+
+def codes_bytes(N, K, variant, lib=None):
+    return (lib or load()).oracle_codes_bytes(N, K, variant)
+
+
+def scales_count(N, K, group=128, lib=None):
+    return (lib or load()).oracle_scales_count(N, K, group)
+
+
+def pack(t, variant=TERNARY, group=128, lib=None):
+    """t: int8 [N][K] -> uint8 codes [N][K/4] (ternary) or [N][K/8] (binary)."""
+    lib = lib or load()
+    t = np.ascontiguousarray(t, dtype=np.int8)
+    N, K = t.shape
+    nb = lib.oracle_codes_bytes(N, K, variant)
+    out = np.empty(max(nb, 0), dtype=np.uint8)
+    bad = ctypes.c_int64(-1)
+    rc = lib.oracle_pack(_ptr(t), N, K, group, variant, _ptr(out), ctypes.byref(bad))
+    if rc:
+        raise OracleError(rc, bad.value if rc == 5 else None)
+    return out.reshape(N, -1)
+
+
+def unpack(codes, N, K, variant=TERNARY, group=128, lib=None):
+    """codes -> int8 t [N][K]; raises OracleError(code=6, index) on code 3."""
+    lib = lib or load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    t = np.empty((N, K), dtype=np.int8)
+    bad = ctypes.c_int64(-1)
+    rc = lib.oracle_unpack(_ptr(codes), N, K, group, variant, _ptr(t), ctypes.byref(bad))
+    if rc:
+        raise OracleError(rc, bad.value if rc == 6 else None)
+    return t
+
+
+def gemm(codes, scales, X, N, K, variant=TERNARY, group=128, threads=1, lib=None):
+    """Y[M][N], A[M][N] in float64.  scales / X are float16 arrays (or their
+    uint16 bit patterns); X has shape [M][K]."""
+    lib = lib or load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scales)
+    s = s.view(np.uint16) if s.dtype == np.float16 else s.astype(np.uint16)
+    X = np.ascontiguousarray(X)
+    X = X.view(np.uint16) if X.dtype == np.float16 else X.astype(np.uint16)
+    if X.ndim == 1:
+        X = X.reshape(1, -1)
+    M = X.shape[0]
+    if X.shape[1] != K:
+        raise ValueError("X has %d columns, expected K=%d" % (X.shape[1], K))
+    Y = np.empty((M, N), dtype=np.float64)
+    A = np.empty((M, N), dtype=np.float64)
+    rc = lib.oracle_gemm(_ptr(codes), _ptr(s), _ptr(X), M, N, K, group, variant,
+                         _ptr(Y), _ptr(A), int(threads))
+    if rc:
+        raise OracleError(rc)
+    return Y, A
+
+
+def gemv(codes, scales, x, N, K, variant=TERNARY, group=128, threads=1, lib=None):
+    """y[N], A[N] for a single activation vector x[K]."""
+    Y, A = gemm(codes, scales, np.asarray(x).reshape(1, -1), N, K, variant, group,
+                threads, lib)
+    return Y[0], A[0]

@@ -1,0 +1,213 @@
+/*
+ * tq_oracle.c -- plain, slow, fp64 CPU oracle for the ternary / binary g128
+ * packed-weight matrix multiply.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the bench's CPU
+ * baseline call it; the product library never links, loads or runs it, and
+ * this file includes nothing from the product.  Build: gcc -O2 -fopenmp,
+ * no fast-math.
+ *
+ * What the method computes
+ * ------------------------
+ * Each weight is a trit t in {-1, 0, +1} (or a sign t in {-1, +1} for the
+ * 1-bit build) and every group of 128 weights shares one FP16 scale s_g, so
+ * the weight that takes part in the product is w_i = s_g * t_i.
+ *   - thakicloud.github.io, "Bonsai 27B: ternary and 1-bit quantization",
+ *     section "How the compression works" (w_i = s_g * t_i; one FP16 scale per
+ *     128-weight group; ternary {-1,0,+1}, binary {-1,+1}).
+ *   - aitrends.kr, "Ternary-Bonsai-27B-mlx-2bit", section "Technical
+ *     features" (the group scale is applied inside the matmul; current
+ *     kernels keep each trit in a 2-bit slot).
+ *
+ * Readings taken where the pages are silent (each stated once here):
+ *   R1  a group is 128 consecutive weights along K (the reduction axis) of
+ *       one output row;
+ *   R2  2-bit code c = t + 1 (0 -> -1, 1 -> 0, 2 -> +1); code 3 is invalid;
+ *   R3  slots are LSB-first: weight k of a row sits in byte k/4 at bits
+ *       [2(k mod 4), 2(k mod 4) + 2); rows are contiguous, row-major;
+ *   R4  binary: bit b = (t + 1) / 2, 8 weights per byte, LSB-first;
+ *   R5  scales are a separate FP16 array [N][K/128], row-major;
+ *   R6  activations FP16 row-major X[M][K], output Y[M][N] (y = W x).
+ *
+ * The product is the plain definition, evaluated in fp64:
+ *   Y[m][n] = sum_g s[n][g] * ( sum_{j<128} t[n][128g+j] * X[m][128g+j] )
+ * Every t*x is exact in fp64 and a 128-term sum of FP16 values is exact in
+ * fp64, so only the scale product and the group additions round.  The
+ * oracle also returns A[m][n] = sum_g |s[n][g]| * sum_j |t * x|, the
+ * magnitude bound used by the acceptance tolerance.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_OK = 0, OR_ERR_NULL = 1, OR_ERR_SHAPE = 2, OR_ERR_GROUP = 3,
+       OR_ERR_VARIANT = 4, OR_ERR_VALUE = 5, OR_ERR_CODE = 6, OR_ERR_NOMEM = 7 };
+enum { OR_TERNARY = 0, OR_BINARY = 1 };
+
+/* IEEE-754 binary16 bit pattern -> real value, from the format's definition:
+ * sign bit, 5-bit exponent (bias 15), 10-bit fraction; exponent 0 is the
+ * subnormal range f * 2^-24, exponent 31 is Inf / NaN. */
+double oracle_half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 31;
+    int f = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)f, -24);
+    else if (e == 31)
+        v = f ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
+/* Bytes of packed codes for an N x K weight: 4 slots per byte (ternary) or
+ * 8 per byte (binary). */
+int64_t oracle_codes_bytes(int64_t N, int64_t K, int variant)
+{
+    if (variant == OR_TERNARY) return N * K / 4;
+    if (variant == OR_BINARY) return N * K / 8;
+    return -1;
+}
+
+/* Number of FP16 scales: one per 128-weight group of every row. */
+int64_t oracle_scales_count(int64_t N, int64_t K, int32_t group)
+{
+    return N * (K / group);
+}
+
+static int check_args(int64_t N, int64_t K, int32_t group, int variant)
+{
+    if (group != 128) return OR_ERR_GROUP;
+    if (N < 1 || K < 128 || K % 128 != 0) return OR_ERR_SHAPE;
+    if (variant != OR_TERNARY && variant != OR_BINARY) return OR_ERR_VARIANT;
+    return OR_OK;
+}
+
+/* Pack trits t[N][K] (int8) into slots.  On a value outside the variant's
+ * set, returns OR_ERR_VALUE and writes the flat index of the first bad
+ * element to *bad. */
+int oracle_pack(const int8_t *t, int64_t N, int64_t K, int32_t group,
+                int variant, uint8_t *codes, int64_t *bad)
+{
+    if (!t || !codes) return OR_ERR_NULL;
+    int rc = check_args(N, K, group, variant);
+    if (rc) return rc;
+    int64_t nbytes = oracle_codes_bytes(N, K, variant);
+    for (int64_t i = 0; i < N * K; i++) {
+        int v = t[i];
+        int ok = (variant == OR_TERNARY) ? (v >= -1 && v <= 1) : (v == -1 || v == 1);
+        if (!ok) {
+            if (bad) *bad = i;
+            return OR_ERR_VALUE;
+        }
+    }
+    memset(codes, 0, (size_t)nbytes);
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            int v = t[n * K + k];
+            if (variant == OR_TERNARY) {
+                int c = v + 1;                                  /* R2 */
+                int64_t byte = n * (K / 4) + k / 4;             /* R3 */
+                codes[byte] |= (uint8_t)(c << (2 * (k % 4)));
+            } else {
+                int b = (v + 1) / 2;                            /* R4 */
+                int64_t byte = n * (K / 8) + k / 8;
+                codes[byte] |= (uint8_t)(b << (k % 8));
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* Unpack slots back to trits.  A ternary code 3 returns OR_ERR_CODE with the
+ * flat weight index of the first bad slot in *bad. */
+int oracle_unpack(const uint8_t *codes, int64_t N, int64_t K, int32_t group,
+                  int variant, int8_t *t, int64_t *bad)
+{
+    if (!codes || !t) return OR_ERR_NULL;
+    int rc = check_args(N, K, group, variant);
+    if (rc) return rc;
+    for (int64_t n = 0; n < N; n++) {
+        for (int64_t k = 0; k < K; k++) {
+            if (variant == OR_TERNARY) {
+                uint8_t byte = codes[n * (K / 4) + k / 4];
+                int c = (byte >> (2 * (k % 4))) & 3;
+                if (c == 3) {
+                    if (bad) *bad = n * K + k;
+                    return OR_ERR_CODE;
+                }
+                t[n * K + k] = (int8_t)(c - 1);
+            } else {
+                uint8_t byte = codes[n * (K / 8) + k / 8];
+                int b = (byte >> (k % 8)) & 1;
+                t[n * K + k] = (int8_t)(2 * b - 1);
+            }
+        }
+    }
+    return OR_OK;
+}
+
+/* Y[M][N] (and the bound A[M][N], if A is not NULL) from packed codes,
+ * FP16 scales [N][K/128] and FP16 activations X[M][K], all as bit patterns.
+ * Rows of W are independent, so `threads` > 1 splits the row loop across
+ * OpenMP threads; the arithmetic of each output is the same either way. */
+int oracle_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
+                int64_t M, int64_t N, int64_t K, int32_t group, int variant,
+                double *Y, double *A, int threads)
+{
+    if (!codes || !scales || !X || !Y) return OR_ERR_NULL;
+    int rc = check_args(N, K, group, variant);
+    if (rc) return rc;
+    if (M < 1) return OR_ERR_SHAPE;
+    int64_t G = K / group;
+    int64_t row_bytes = oracle_codes_bytes(1, K, variant);
+
+    /* activations decoded once */
+    double *x = (double *)malloc((size_t)(M * K) * sizeof(double));
+    if (!x) return OR_ERR_NOMEM;
+    for (int64_t i = 0; i < M * K; i++) x[i] = oracle_half_to_double(X[i]);
+
+    int status = OR_OK;
+    if (threads < 1) threads = 1;
+#pragma omp parallel num_threads(threads)
+    {
+        int8_t *t = (int8_t *)malloc((size_t)K);
+        if (!t) {
+#pragma omp atomic write
+            status = OR_ERR_NOMEM;
+        }
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; n++) {
+            if (!t) continue;
+            int64_t badi = 0;
+            int urc = oracle_unpack(codes + n * row_bytes, 1, K, group, variant, t, &badi);
+            if (urc) {
+#pragma omp atomic write
+                status = urc;
+                continue;
+            }
+            for (int64_t m = 0; m < M; m++) {
+                double acc = 0.0, bound = 0.0;
+                for (int64_t g = 0; g < G; g++) {
+                    double s = oracle_half_to_double(scales[n * G + g]);
+                    double part = 0.0, apart = 0.0;
+                    for (int64_t j = 0; j < group; j++) {
+                        double tx = (double)t[g * group + j] * x[m * K + g * group + j];
+                        part += tx;
+                        apart += fabs(tx);
+                    }
+                    acc += s * part;
+                    bound += fabs(s) * apart;
+                }
+                Y[m * N + n] = acc;
+                if (A) A[m * N + n] = bound;
+            }
+        }
+        free(t);
+    }
+    free(x);
+    return status;
+}

@@ -1,0 +1,253 @@
+"""Pins that tie the oracle to something other than itself.
+
+Each ``check_*`` takes a loaded oracle library (``oracle.load(path)``) and
+raises AssertionError on a mismatch.  ``test_oracle_pins.py`` runs them on the
+real oracle; ``test_oracle_mutants.py`` runs them on copies of the oracle with a
+planted mistake and requires that some pin fails for every mistake.
+
+What each pin rests on:
+  * IEEE binary16 decoding: numpy's float16 -> float64 conversion (library).
+  * Byte accounting: figures printed on the pages (tests/golden/page_figures.json).
+  * Slot layout: hand-derived bytes (tests/golden/layout_examples.json).
+  * The product itself: numpy float64 matmul of W = s * t built from the *input*
+    trits (library routine), exact Python-integer arithmetic, and closed forms
+    (one-hot, all-zero, all-one cases), plus a hand-evaluated worked example.
+"""
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+from binary_g128_bit_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _dense(t, s):
+    """W[n][k] = s[n][k/128] * t[n][k] from the input trits (not from unpack)."""
+    s64 = np.asarray(s, dtype=np.float16).astype(np.float64)
+    return np.repeat(s64, 128, axis=1) * t.astype(np.float64)
+
+
+# ---------------------------------------------------------------- fp16 decode
+def check_half_decode(lib):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = np.array([lib.oracle_half_to_double(int(b)) for b in bits])
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan), "NaN pattern differs"
+    assert np.array_equal(got[~nan], ref[~nan]), "fp16 decode differs from numpy"
+
+
+# ---------------------------------------------------------- byte accounting
+def check_byte_counts(lib):
+    pf = _golden("page_figures.json")
+    # information content per weight (pages: log2(3) ~ 1.585, + 16/128 bit)
+    bits_val = math.log2(3)
+    assert round(bits_val, 3) == pf["ternary_bits_per_value"]["value"]
+    ovh = pf["scale_overhead_bits"]["numerator"] / pf["scale_overhead_bits"]["denominator"]
+    assert round(bits_val + ovh, 2) == pf["ternary_bpw"]["value"]
+    assert 1 + ovh == pf["binary_bpw"]["value"]
+    assert round(16 / (bits_val + ovh), 1) == pf["ternary_reduction_vs_fp16"]["value"]
+    assert round(16 / (1 + ovh), 1) == pf["binary_reduction_vs_fp16"]["value"]
+
+    # the oracle's own storage: 2-bit slots (or 1-bit) + one fp16 per 128
+    shapes = [synth.C1, synth.GATE_UP, synth.DOWN, synth.LM_HEAD, (1024, 5120),
+              (6144, 5120), (14336, 5120), (5120, 6144), (8, 128), (3, 384)]
+    for N, K in shapes:
+        sc = lib.oracle_scales_count(N, K, 128)
+        assert sc == N * K // 128
+        tb = lib.oracle_codes_bytes(N, K, 0)
+        bb = lib.oracle_codes_bytes(N, K, 1)
+        assert 8 * (tb + 2 * sc) == 2.125 * N * K, (N, K, tb)
+        assert 8 * (bb + 2 * sc) == 1.125 * N * K, (N, K, bb)
+    # the pages' deploy size follows from 2.125 bpw on the FP16 model's weights:
+    # 54 GB at 16 bpw -> 27.0e9 weights -> 7.17 GB with 2-bit slots
+    n_weights = pf["fp16_model_gb"]["value"] * 1e9 * 8 / 16
+    N, K = 1024, 1024
+    st_bpw = 8 * (lib.oracle_codes_bytes(N, K, 0) + 2 * lib.oracle_scales_count(N, K, 128)) / (N * K)
+    deploy = n_weights * st_bpw / 8 / 1e9
+    assert round(deploy, 2) == pf["ternary_deploy_gb_2bit_slots"]["value"], deploy
+    # ideal sizes at the information bpw land within 3% of the printed ones
+    assert abs(n_weights * (bits_val + ovh) / 8e9 / pf["ternary_ideal_gb"]["value"] - 1) < 0.03
+    bin_bpw = 8 * (lib.oracle_codes_bytes(N, K, 1) + 2 * lib.oracle_scales_count(N, K, 128)) / (N * K)
+    assert abs(n_weights * bin_bpw / 8e9 / pf["binary_ideal_gb"]["value"] - 1) < 0.03
+
+
+# ------------------------------------------------------------- round trips
+def check_roundtrip_bytes(lib):
+    valid = 0
+    for b in range(256):
+        row = np.full((1, 32), b, dtype=np.uint8)        # K = 128, ternary
+        try:
+            t = oracle.unpack(row, 1, 128, oracle.TERNARY, lib=lib)
+        except oracle.OracleError as e:
+            assert e.code == 6
+            # first bad slot of the first byte
+            first = min(j for j in range(4) if (b >> (2 * j)) & 3 == 3)
+            assert e.index == first, (b, e.index)
+            continue
+        valid += 1
+        assert set(np.unique(t)) <= {-1, 0, 1}
+        back = oracle.pack(t, oracle.TERNARY, lib=lib)
+        assert np.array_equal(back, row), b
+    assert valid == 81, valid                            # 3^4 valid bytes
+    for b in range(256):
+        row = np.full((1, 16), b, dtype=np.uint8)        # K = 128, binary
+        t = oracle.unpack(row, 1, 128, oracle.BINARY, lib=lib)
+        assert set(np.unique(t)) <= {-1, 1}
+        assert np.array_equal(oracle.pack(t, oracle.BINARY, lib=lib), row), b
+    g = synth.rng(7)
+    for variant in (oracle.TERNARY, oracle.BINARY):
+        for N, K in ((1, 128), (5, 384), (16, 1024)):
+            t = synth.trits(g, N, K, variant)
+            c = oracle.pack(t, variant, lib=lib)
+            assert np.array_equal(oracle.unpack(c, N, K, variant, lib=lib), t)
+
+
+def check_golden_layout(lib):
+    lay = _golden("layout_examples.json")
+    for key, variant in (("ternary_row", oracle.TERNARY), ("binary_row", oracle.BINARY)):
+        ex = lay[key]
+        K = ex["K"]
+        t = np.full((1, K), ex["t_rest"], dtype=np.int8)
+        t[0, :len(ex["t_prefix"])] = ex["t_prefix"]
+        codes = oracle.pack(t, variant, lib=lib)[0]
+        pre = [int(h, 16) for h in ex["bytes_prefix_hex"]]
+        assert list(codes[:len(pre)]) == pre, (key, codes[:len(pre)])
+        assert all(int(b) == int(ex["byte_rest_hex"], 16) for b in codes[len(pre):]), key
+        assert np.array_equal(oracle.unpack(codes.reshape(1, -1), 1, K, variant, lib=lib), t)
+
+
+def check_worked_gemv(lib):
+    ex = _golden("layout_examples.json")["worked_gemv"]
+    N, K = ex["N"], ex["K"]
+    t = np.zeros((N, K), dtype=np.int8)
+    t[0, :128] = 1
+    t[1, 0:128:2] = -1
+    t[1, 1:128:2] = 1
+    t[1, 133] = 1
+    s = np.array([r["scales"] for r in ex["rows"]], dtype=np.float16)
+    x = np.where(np.arange(K) < 128, 1.0, 2.0).astype(np.float16)
+    y, _ = oracle.gemv(oracle.pack(t, lib=lib), s, x, N, K, lib=lib)
+    assert list(y) == ex["y"], y
+
+
+# ------------------------------------------------------------ the product
+def check_bruteforce_numpy(lib):
+    g = synth.rng(11)
+    for variant in (oracle.TERNARY, oracle.BINARY):
+        for N, K, M in ((1, 128, 1), (3, 256, 2), (8, 384, 4), (5, 128, 3)):
+            t = synth.trits(g, N, K, variant)
+            s = synth.scales(g, N, K)
+            s[0, 0] = -s[0, 0]                       # negative scale
+            if s.shape[1] > 1:
+                s[-1, -1] = np.float16(2.0 ** -20)   # subnormal scale
+            X = synth.activations(g, M, K)
+            X[0, 0] = np.float16(2.0 ** -22)         # subnormal activation
+            Y, _ = oracle.gemm(oracle.pack(t, variant, lib=lib), s, X, N, K, variant, lib=lib)
+            ref = X.astype(np.float64) @ _dense(t, s).T
+            err = np.abs(Y - ref)
+            scale = np.abs(X.astype(np.float64)) @ np.abs(_dense(t, s)).T
+            assert np.all(err <= 1e-12 * scale + 1e-300), (variant, N, K, M, err.max())
+
+
+def check_exact_integer(lib):
+    g = synth.rng(13)
+    for variant in (oracle.TERNARY, oracle.BINARY):
+        N, K, M = 4, 384, 3
+        t = synth.trits(g, N, K, variant)
+        s = np.ones((N, K // 128), dtype=np.float16)
+        X = synth.int_activations(g, M, K)
+        Y, _ = oracle.gemm(oracle.pack(t, variant, lib=lib), s, X, N, K, variant, lib=lib)
+        xi = X.astype(np.int64)
+        for m in range(M):
+            for n in range(N):
+                exact = sum(int(t[n, k]) * int(xi[m, k]) for k in range(K))
+                assert Y[m, n] == exact, (variant, m, n, Y[m, n], exact)
+
+
+def check_special_cases(lib):
+    g = synth.rng(17)
+    N, K = 6, 384
+    t = synth.trits(g, N, K, oracle.TERNARY)
+    s = synth.scales(g, N, K)
+    codes = oracle.pack(t, lib=lib)
+    sv = s.astype(np.float64)
+    # one-hot x = e_k: y[n] = s[n][k/128] * t[n][k] exactly
+    for k in (0, 1, 2, 3, 4, 127, 128, 131, 255, 256, 383):
+        x = np.zeros(K, dtype=np.float16)
+        x[k] = 1
+        y, _ = oracle.gemv(codes, s, x, N, K, lib=lib)
+        assert np.array_equal(y, sv[:, k // 128] * t[:, k]), k
+    # t == 0 -> y == 0
+    z = oracle.pack(np.zeros((N, K), np.int8), lib=lib)
+    x = synth.activations(g, 1, K)[0]
+    y, _ = oracle.gemv(z, s, x, N, K, lib=lib)
+    assert np.all(y == 0)
+    # t == +1 and s == 1 -> y == sum(x)
+    one = oracle.pack(np.ones((N, K), np.int8), lib=lib)
+    y, _ = oracle.gemv(one, np.ones_like(s), x, N, K, lib=lib)
+    assert np.all(y == np.sum(x.astype(np.float64)))
+    # x == 1 -> y[n] = sum_g s_g * (#(+1) - #(-1)) in group g
+    y, _ = oracle.gemv(codes, s, np.ones(K, np.float16), N, K, lib=lib)
+    cnt = t.reshape(N, K // 128, 128).astype(np.int64).sum(axis=2)
+    assert np.allclose(y, (sv * cnt).sum(axis=1), rtol=1e-15, atol=0)
+    # binary one-hot: y[n] = s * (+-1)
+    tb = synth.trits(g, N, K, oracle.BINARY)
+    cb = oracle.pack(tb, oracle.BINARY, lib=lib)
+    for k in (0, 7, 8, 129, 383):
+        x = np.zeros(K, dtype=np.float16)
+        x[k] = 1
+        y, _ = oracle.gemv(cb, s, x, N, K, oracle.BINARY, lib=lib)
+        assert np.array_equal(y, sv[:, k // 128] * tb[:, k]), k
+
+
+def check_bound(lib):
+    g = synth.rng(19)
+    for variant in (oracle.TERNARY, oracle.BINARY):
+        N, K, M = 5, 384, 2
+        t = synth.trits(g, N, K, variant)
+        s = synth.scales(g, N, K)
+        s[1, 1] = -s[1, 1]
+        X = synth.activations(g, M, K)
+        Y, A = oracle.gemm(oracle.pack(t, variant, lib=lib), s, X, N, K, variant, lib=lib)
+        refA = np.abs(X.astype(np.float64)) @ np.abs(_dense(t, s)).T
+        assert np.allclose(A, refA, rtol=1e-12, atol=0), variant
+        assert np.all(np.abs(Y) <= A * (1 + 1e-12))
+
+
+def check_errors(lib):
+    t = np.zeros((2, 128), np.int8)
+    for bad_t, variant, idx in ((2, oracle.TERNARY, 5), (0, oracle.BINARY, 3), (-2, oracle.TERNARY, 200)):
+        tt = np.zeros((2, 128), np.int8) if variant == oracle.TERNARY else np.ones((2, 128), np.int8)
+        tt.flat[idx] = bad_t
+        try:
+            oracle.pack(tt, variant, lib=lib)
+            raise AssertionError("pack accepted %d" % bad_t)
+        except oracle.OracleError as e:
+            assert e.code == 5 and e.index == idx, (e.code, e.index)
+    for N, K, group, variant, code in ((2, 100, 128, 0, 2), (2, 192, 128, 0, 2), (0, 128, 128, 0, 2),
+                                       (2, 128, 64, 0, 3), (2, 128, 128, 2, 4)):
+        rc = lib.oracle_pack(t.ctypes.data, N, K, group, variant,
+                             np.zeros(64, np.uint8).ctypes.data, None)
+        assert rc == code, (N, K, group, variant, rc)
+    codes = np.full((2, 32), 0x55, np.uint8)
+    codes[1, 7] = 0x55 | (3 << 4)                       # slot 2 of byte 7 of row 1
+    try:
+        oracle.unpack(codes, 2, 128, lib=lib)
+        raise AssertionError("code 3 accepted")
+    except oracle.OracleError as e:
+        assert e.code == 6 and e.index == 128 + 7 * 4 + 2, e.index
+
+
+ALL_CHECKS = [check_half_decode, check_byte_counts, check_roundtrip_bytes,
+              check_golden_layout, check_worked_gemv, check_bruteforce_numpy,
+              check_exact_integer, check_special_cases, check_bound, check_errors]

@@ -1,0 +1,60 @@
+"""Plant plausible mistakes in copies of the oracle and require that the pins
+catch every one.  Each mutant is the oracle's C source with one textual edit,
+built with gcc into a temporary directory on the CPU."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+import oracle_pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "tq_oracle.c")
+
+# (name, [(old, new), ...]); every `old` must occur in the source
+MUTANTS = [
+    ("msb_first_slots", [("c << (2 * (k % 4))", "c << (6 - 2 * (k % 4))"),
+                         ("byte >> (2 * (k % 4))", "byte >> (6 - 2 * (k % 4))")]),
+    ("code_map_sign", [("c = v + 1;", "c = 1 - v;"), ("(int8_t)(c - 1)", "(int8_t)(1 - c)")]),
+    ("binary_bit_map", [("b = (v + 1) / 2;", "b = (1 - v) / 2;"),
+                        ("(int8_t)(2 * b - 1)", "(int8_t)(1 - 2 * b)")]),
+    ("dropped_first_term", [("for (int64_t j = 0; j < group; j++)",
+                             "for (int64_t j = 1; j < group; j++)")]),
+    ("scale_first_group_only", [("scales[n * G + g]", "scales[n * G]")]),
+    ("scale_transposed", [("scales[n * G + g]", "scales[g * N + n]")]),
+    ("x_group_offset_dropped", [("x[m * K + g * group + j]", "x[m * K + j]")]),
+    ("t_group_stride", [("t[g * group + j]", "t[g * 64 + j]")]),
+    ("half_exponent_bias", [("e - 25", "e - 24")]),
+    ("half_subnormal", [("ldexp((double)f, -24)", "ldexp((double)f, -25)")]),
+    ("bound_signed", [("apart += fabs(tx);", "apart += tx;")]),
+    ("scale_abs_missing", [("bound += fabs(s) * apart;", "bound += s * apart;")]),
+    ("row_stride", [("codes + n * row_bytes", "codes + n * (row_bytes / 2)")]),
+    ("accept_code3", [("if (c == 3) {", "if (c == 4) {")]),
+]
+
+
+def _build_mutant(tmp_path, name, edits):
+    with open(SRC) as f:
+        text = f.read()
+    for old, new in edits:
+        assert old in text, (name, old)
+        text = text.replace(old, new)
+    src = tmp_path / ("%s.c" % name)
+    src.write_text(text)
+    lib_path = str(tmp_path / ("lib%s.so" % name))
+    oracle.build(lib_path, src=str(src))
+    return oracle.load(lib_path)
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc missing")
+@pytest.mark.parametrize("name,edits", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, edits):
+    lib = _build_mutant(tmp_path, name, edits)
+    caught = []
+    for check in oracle_pins.ALL_CHECKS:
+        try:
+            check(lib)
+        except Exception as e:  # noqa: BLE001 - any failure counts as caught
+            caught.append((check.__name__, type(e).__name__))
+    assert caught, "no pin caught mutant %s" % name
