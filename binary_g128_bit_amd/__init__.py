@@ -1,0 +1,173 @@
+"""Ternary / binary g128 packed-weight matmul for AMD MI355X (gfx950).
+
+Thin ctypes binding over ``libtq.so`` (C ABI in ``include/tq.h``).  The
+functions carry the C names and only marshal arguments: shapes are read off the
+arrays, pointers and the current HIP stream are passed through, and a non-zero
+status becomes a :class:`TQError`.  Every step of the computation runs in the
+library.  PyTorch is used only for device memory and streams.
+
+Build the library first: ``python -m binary_g128_bit_amd.build``.  There is no
+fallback: calling a GPU entry point without the built library raises.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+TQ_TERNARY = 0
+TQ_BINARY = 1
+GROUP = 128
+
+_STATUS = {0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_GROUP",
+           4: "TQ_ERR_VARIANT", 5: "TQ_ERR_VALUE", 6: "TQ_ERR_CODE", 7: "TQ_ERR_ALIGN",
+           8: "TQ_ERR_HIP"}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
+
+# every symbol include/tq.h declares
+EXPORTS = ("tq_codes_bytes", "tq_scales_count", "tq_pack", "tq_unpack", "tq_gemv", "tq_gemm",
+           "tq_last_error", "tq_last_error_index", "tq_version")
+
+
+class TQError(RuntimeError):
+    """A non-zero tq_status; ``.status`` is the code, ``.index`` the flat index
+    attached to TQ_ERR_VALUE / TQ_ERR_CODE (else -1)."""
+
+    def __init__(self, status, message, index=-1):
+        self.status = status
+        self.index = index
+        super().__init__("%s: %s" % (_STATUS.get(status, str(status)), message))
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libtq.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libtq.so is not built (%s); run `python -m binary_g128_bit_amd.build`"
+                           % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    L.tq_codes_bytes.argtypes = [i64, i64, i32]
+    L.tq_codes_bytes.restype = ctypes.c_size_t
+    L.tq_scales_count.argtypes = [i64, i64, i32]
+    L.tq_scales_count.restype = ctypes.c_size_t
+    L.tq_pack.argtypes = [vp, i64, i64, i32, i32, vp]
+    L.tq_pack.restype = i32
+    L.tq_unpack.argtypes = [vp, i64, i64, i32, i32, vp]
+    L.tq_unpack.restype = i32
+    L.tq_gemv.argtypes = [vp, vp, vp, vp, i64, i64, i32, i32, vp]
+    L.tq_gemv.restype = i32
+    L.tq_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
+    L.tq_gemm.restype = i32
+    L.tq_last_error.argtypes = []
+    L.tq_last_error.restype = ctypes.c_char_p
+    L.tq_last_error_index.argtypes = []
+    L.tq_last_error_index.restype = i64
+    L.tq_version.argtypes = []
+    L.tq_version.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status):
+    if status != 0:
+        L = lib()
+        raise TQError(status, L.tq_last_error().decode(), L.tq_last_error_index())
+
+
+def tq_version():
+    return lib().tq_version().decode()
+
+
+def tq_codes_bytes(N, K, variant=TQ_TERNARY):
+    return lib().tq_codes_bytes(N, K, variant)
+
+
+def tq_scales_count(N, K, group=GROUP):
+    return lib().tq_scales_count(N, K, group)
+
+
+# ------------------------------------------------------------------ host side
+def tq_pack(t, variant=TQ_TERNARY, group=GROUP):
+    """int8 t [N][K] (numpy) -> uint8 codes [N][K/4] (ternary) or [N][K/8]."""
+    t = np.ascontiguousarray(t, dtype=np.int8)
+    if t.ndim != 2:
+        raise ValueError("t must be 2-D [N][K]")
+    N, K = t.shape
+    per = 4 if variant == TQ_TERNARY else 8
+    out = np.empty((N, max(K // per, 1)), dtype=np.uint8)
+    _check(lib().tq_pack(t.ctypes.data, N, K, group, variant, out.ctypes.data))
+    return out
+
+
+def tq_unpack(codes, N, K, variant=TQ_TERNARY, group=GROUP):
+    """uint8 codes -> int8 t [N][K] (numpy)."""
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    need = lib().tq_codes_bytes(N, K, variant)
+    if need and codes.size < need:
+        raise ValueError("codes holds %d bytes, %d needed" % (codes.size, need))
+    t = np.empty((N, K), dtype=np.int8)
+    _check(lib().tq_unpack(codes.ctypes.data, N, K, group, variant, t.ctypes.data))
+    return t
+
+
+# ---------------------------------------------------------------- device side
+def _dev(tensor, name, dtypes):
+    if not tensor.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if tensor.dtype not in dtypes:
+        raise ValueError("%s has dtype %s, expected one of %s" % (name, tensor.dtype, dtypes))
+    if not tensor.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return tensor.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _shape_checks(codes, scales, K, variant):
+    import torch  # noqa: F401
+    N = scales.shape[0]
+    if scales.dim() != 2 or scales.shape[1] * GROUP != K:
+        raise ValueError("scales must be [N][K/128] with K=%d" % K)
+    need = lib().tq_codes_bytes(N, K, variant)
+    if codes.numel() != need:
+        raise ValueError("codes holds %d bytes, %d needed for N=%d K=%d" % (codes.numel(), need, N, K))
+    return N
+
+
+def tq_gemv(codes, scales, x, y=None, variant=TQ_TERNARY, group=GROUP, stream=None):
+    """y[N] = W x on the current stream.  codes uint8, scales float16 [N][K/128],
+    x float16 [K], y float32 [N] (allocated if None)."""
+    import torch
+    K = x.shape[-1]
+    N = _shape_checks(codes, scales, K, variant)
+    if y is None:
+        y = torch.empty(N, dtype=torch.float32, device=x.device)
+    half = (torch.float16, torch.int16)
+    _check(lib().tq_gemv(_dev(codes, "codes", (torch.uint8,)), _dev(scales, "scales", half),
+                         _dev(x, "x", half), _dev(y, "y", (torch.float32,)), N, K, group, variant,
+                         _stream(stream)))
+    return y
+
+
+def tq_gemm(codes, scales, X, Y=None, variant=TQ_TERNARY, group=GROUP, stream=None):
+    """Y[M][N] = X W^T on the current stream.  X float16 [M][K]."""
+    import torch
+    M, K = X.shape
+    N = _shape_checks(codes, scales, K, variant)
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    half = (torch.float16, torch.int16)
+    _check(lib().tq_gemm(_dev(codes, "codes", (torch.uint8,)), _dev(scales, "scales", half),
+                         _dev(X, "X", half), _dev(Y, "Y", (torch.float32,)), M, N, K, group,
+                         variant, _stream(stream)))
+    return Y

@@ -1,0 +1,51 @@
+// C ABI entry points for the device matmuls: argument validation (host only,
+// before any HIP call) and dispatch to the kernels.  The operation is the
+// pages' w_i = s_g * t_i product with one FP16 scale per 128 weights
+// (thakicloud.github.io, "Bonsai 27B: ternary and 1-bit quantization",
+// "How the compression works"), evaluated from the packed slots.
+#include <hip/hip_runtime_api.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+int32_t gemv_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
+                     int64_t N, int64_t K, int32_t variant, hipStream_t stream);
+int32_t gemm_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
+                     int64_t M, int64_t N, int64_t K, int32_t variant, hipStream_t stream);
+
+namespace {
+int32_t check_device_args(const void *codes, const void *scales, const void *x, const void *y,
+                          int64_t M, int64_t N, int64_t K, int32_t group, int32_t variant) {
+    if (!codes || !scales || !x || !y) return fail(TQ_ERR_NULL, "NULL pointer argument");
+    if (int32_t rc = check_shape(M, N, K, group, variant)) return rc;
+    if (!aligned(codes, 16)) return fail(TQ_ERR_ALIGN, "codes must be 16-byte aligned");
+    if (!aligned(x, 16)) return fail(TQ_ERR_ALIGN, "activations must be 16-byte aligned");
+    if (!aligned(scales, 2)) return fail(TQ_ERR_ALIGN, "scales must be 2-byte aligned");
+    if (!aligned(y, 4)) return fail(TQ_ERR_ALIGN, "output must be 4-byte aligned");
+    return TQ_OK;
+}
+}  // namespace
+}  // namespace tq
+
+extern "C" {
+
+int32_t tq_gemv(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
+                int64_t N, int64_t K, int32_t group, int32_t variant, void *stream) {
+    tq::clear_error();
+    if (int32_t rc = tq::check_device_args(codes, scales, x, y, 1, N, K, group, variant)) return rc;
+    return tq::gemv_enqueue(codes, scales, x, y, N, K, variant,
+                            static_cast<hipStream_t>(stream));
+}
+
+int32_t tq_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
+                int64_t M, int64_t N, int64_t K, int32_t group, int32_t variant, void *stream) {
+    tq::clear_error();
+    if (int32_t rc = tq::check_device_args(codes, scales, X, Y, M, N, K, group, variant)) return rc;
+    if (M == 1)
+        return tq::gemv_enqueue(codes, scales, X, Y, N, K, variant,
+                                static_cast<hipStream_t>(stream));
+    return tq::gemm_enqueue(codes, scales, X, Y, M, N, K, variant,
+                            static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

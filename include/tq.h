@@ -1,0 +1,125 @@
+/*
+ * tq.h -- C ABI of the ternary / binary g128 packed-weight matmul for
+ * AMD MI355X (gfx950).
+ *
+ * The operation (thakicloud.github.io, "Bonsai 27B: ternary and 1-bit
+ * quantization", section "How the compression works"): every weight is a
+ * code t in {-1, 0, +1} (ternary) or {-1, +1} (binary, the 1-bit build), and
+ * each group of 128 weights shares one FP16 scale s_g, so w_i = s_g * t_i.
+ * The kernels read the packed slots directly and apply the group scale
+ * inside the matmul instead of expanding the weights to FP16 in memory
+ * (aitrends.kr, "Ternary-Bonsai-27B-mlx-2bit", section "Technical
+ * features": trits live in 2-bit slots; the scale is applied in the matmul).
+ *
+ * Storage format (the pages name the slots but not their layout; the layout
+ * below is this library's documented reading):
+ *   - W is N x K (out x in), y = W x.  A group is 128 consecutive weights of
+ *     one row along K.  K must be a positive multiple of 128; group must be 128.
+ *   - Ternary codes: uint8 [N][K/4].  Code c = t + 1 (0 -> -1, 1 -> 0,
+ *     2 -> +1), 4 per byte, LSB-first: weight k of a row lives in byte k/4 at
+ *     bits [2(k%4), 2(k%4)+2).  Code 3 is invalid.
+ *   - Binary codes: uint8 [N][K/8].  Bit b = (t + 1)/2, weight k at bit k%8
+ *     of byte k/8.
+ *   - Scales: IEEE binary16 bit patterns, uint16 [N][K/128], row-major, any
+ *     finite value (negative and subnormal allowed).
+ *   - Activations: binary16 bit patterns, x[K] or X[M][K] row-major.
+ *   - Output: float32 y[N] or Y[M][N] row-major; overwritten, never
+ *     accumulated into.
+ *
+ * Conventions for every entry point:
+ *   - Ownership: the caller owns every buffer; the library keeps no pointer
+ *     after the call returns and allocates no device memory.
+ *   - Streams: `stream` is a hipStream_t (NULL = the default stream).  GPU
+ *     work is enqueued asynchronously on it; buffers must stay valid until
+ *     the stream has passed the call.  Launch failures are reported at once
+ *     (TQ_ERR_HIP); faults inside a kernel surface at the caller's next
+ *     synchronisation.
+ *   - Validation happens on the host, before any HIP call, in this order:
+ *     NULL pointer, shape, group, variant, alignment.  No work is enqueued
+ *     when a call returns an error.  tq_last_error() then describes it.
+ *   - Device inputs are not inspected: codes passed to the GPU entry points
+ *     must be valid (a ternary code 3 gives an unspecified result, never a
+ *     fault).  tq_pack never produces code 3.
+ *   - Outputs must not alias inputs.  Functions are reentrant; the only
+ *     library state is the calling thread's last-error record.
+ *   - Byte offsets are 64-bit (N*K reaches 1.27e9 for a 248320 x 5120 head).
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* weight variants */
+#define TQ_TERNARY 0 /* t in {-1,0,+1}, 2-bit slots, 2.125 bits/weight stored */
+#define TQ_BINARY 1  /* t in {-1,+1},   1-bit slots, 1.125 bits/weight stored */
+
+/* status codes */
+#define TQ_OK 0
+#define TQ_ERR_NULL 1    /* a required pointer is NULL                          */
+#define TQ_ERR_SHAPE 2   /* M or N < 1, K < 128, K % 128 != 0, or too large     */
+#define TQ_ERR_GROUP 3   /* group != 128                                         */
+#define TQ_ERR_VARIANT 4 /* variant is neither TQ_TERNARY nor TQ_BINARY         */
+#define TQ_ERR_VALUE 5   /* tq_pack: a t outside the variant's set              */
+#define TQ_ERR_CODE 6    /* tq_unpack: a ternary code 3                          */
+#define TQ_ERR_ALIGN 7   /* a device pointer is not aligned as required          */
+#define TQ_ERR_HIP 8     /* the HIP runtime rejected a launch                    */
+
+/* Size of the packed code array: N*K/4 bytes (ternary) or N*K/8 (binary).
+ * Returns 0 for an invalid shape or variant. */
+size_t tq_codes_bytes(int64_t N, int64_t K, int32_t variant);
+
+/* Number of FP16 scales: N*K/group.  Returns 0 for an invalid shape/group. */
+size_t tq_scales_count(int64_t N, int64_t K, int32_t group);
+
+/* Host -> host.  Pack t (int8 [N][K], row-major) into `codes`
+ * (tq_codes_bytes(N,K,variant) bytes, fully overwritten).  Scales are not
+ * touched: they pass through unchanged.  A value outside the variant's set
+ * returns TQ_ERR_VALUE; tq_last_error_index() gives its flat index n*K+k and
+ * `codes` is left in an unspecified state. */
+int32_t tq_pack(const int8_t *t, int64_t N, int64_t K, int32_t group,
+                int32_t variant, uint8_t *codes);
+
+/* Host -> host.  Inverse of tq_pack: writes t (int8 [N][K]).  A ternary
+ * code 3 returns TQ_ERR_CODE; tq_last_error_index() gives the flat weight
+ * index of the first such slot. */
+int32_t tq_unpack(const uint8_t *codes, int64_t N, int64_t K, int32_t group,
+                  int32_t variant, int8_t *t);
+
+/* Device.  y[n] = sum_g s[n][g] * sum_{j<128} t[n][128g+j] * x[128g+j],
+ * accumulated in fp32 (batch-1 decode GEMV).
+ *   codes  : device, tq_codes_bytes(N,K,variant) bytes, 16-byte aligned
+ *   scales : device, uint16 [N][K/128] (fp16 bits), 2-byte aligned
+ *   x      : device, uint16 [K] (fp16 bits), 16-byte aligned
+ *   y      : device, float [N], 4-byte aligned; overwritten
+ * Limits: 1 <= N < 2^31, 128 <= K <= 65536. */
+int32_t tq_gemv(const uint8_t *codes, const uint16_t *scales, const uint16_t *x,
+                float *y, int64_t N, int64_t K, int32_t group, int32_t variant,
+                void *stream);
+
+/* Device.  Y[m][n] = sum_g s[n][g] * sum_j t[n][128g+j] * X[m][128g+j]
+ * for m < M (small-batch GEMM: speculative-verify and prefill-chunk widths).
+ * X is uint16 [M][K] (16-byte aligned), Y is float [M][N]; other arguments as
+ * tq_gemv.  M == 1 is the GEMV.  Limits: 1 <= M <= 65536, N and K as tq_gemv. */
+int32_t tq_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
+                float *Y, int64_t M, int64_t N, int64_t K, int32_t group,
+                int32_t variant, void *stream);
+
+/* Text of the calling thread's last error ("" if none). */
+const char *tq_last_error(void);
+
+/* Flat index attached to the last TQ_ERR_VALUE / TQ_ERR_CODE, else -1. */
+int64_t tq_last_error_index(void);
+
+/* Library version string. */
+const char *tq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

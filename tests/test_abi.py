@@ -1,0 +1,101 @@
+"""The C-ABI library loads without a GPU, exports every symbol include/tq.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import binary_g128_bit_amd as tq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = tq.lib()
+    names = _declared()
+    assert names, "no declarations parsed"
+    for name in names:
+        assert hasattr(L, name), name
+    assert sorted(tq.EXPORTS) == names
+
+
+def test_version_and_sizes():
+    assert "gfx950" in tq.tq_version()
+    assert tq.tq_codes_bytes(17408, 5120, tq.TQ_TERNARY) == 17408 * 5120 // 4
+    assert tq.tq_codes_bytes(17408, 5120, tq.TQ_BINARY) == 17408 * 5120 // 8
+    assert tq.tq_scales_count(5120, 17408) == 5120 * 136
+    assert tq.tq_codes_bytes(4, 100, tq.TQ_TERNARY) == 0
+    assert tq.tq_codes_bytes(4, 128, 7) == 0
+    assert tq.tq_scales_count(4, 128, 64) == 0
+
+
+FAKE = 0x7f0000000000  # 16-byte aligned address that is never dereferenced
+
+
+@pytest.mark.parametrize("args,status", [
+    # (codes, scales, x, y, M, N, K, group, variant)
+    ((0, FAKE, FAKE, FAKE, 1, 8, 128, 128, 0), 1),
+    ((FAKE, FAKE, FAKE, 0, 1, 8, 128, 128, 0), 1),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 0, 128, 128, 0), 2),
+    ((FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 128, 0), 2),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 100, 128, 0), 2),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 0, 128, 0), 2),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 131072, 128, 0), 2),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 256, 64, 0), 3),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 256, 128, 2), 4),
+    ((FAKE + 8, FAKE, FAKE, FAKE, 1, 8, 256, 128, 0), 7),
+    ((FAKE, FAKE, FAKE + 2, FAKE, 1, 8, 256, 128, 0), 7),
+    ((FAKE, FAKE + 1, FAKE, FAKE, 1, 8, 256, 128, 0), 7),
+    ((FAKE, FAKE, FAKE, FAKE + 2, 1, 8, 256, 128, 0), 7),
+])
+def test_device_entry_points_validate_on_host(args, status):
+    L = tq.lib()
+    codes, scales, x, y, M, N, K, group, variant = args
+    p = ctypes.c_void_p
+    rc = L.tq_gemm(p(codes), p(scales), p(x), p(y), M, N, K, group, variant, None)
+    assert rc == status, L.tq_last_error()
+    assert L.tq_last_error()
+    if M == 1:
+        rc = L.tq_gemv(p(codes), p(scales), p(x), p(y), N, K, group, variant, None)
+        assert rc == status
+
+
+def test_pack_errors():
+    t = np.zeros((2, 128), np.int8)
+    t[1, 5] = 2
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_pack(t)
+    assert e.value.status == 5 and e.value.index == 133
+    tb = np.ones((2, 128), np.int8)
+    tb[0, 9] = 0
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_pack(tb, tq.TQ_BINARY)
+    assert e.value.status == 5 and e.value.index == 9
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_pack(np.zeros((2, 100), np.int8))
+    assert e.value.status == 2
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_pack(np.zeros((2, 128), np.int8), 3)
+    assert e.value.status == 4
+    L = tq.lib()
+    assert L.tq_pack(None, 2, 128, 128, 0, None) == 1
+    assert L.tq_pack(t.ctypes.data, 2, 128, 64, 0, t.ctypes.data) == 3
+
+
+def test_unpack_rejects_code3_with_index():
+    codes = np.full((3, 64), 0x55, np.uint8)       # N=3, K=256
+    codes[2, 10] = 0x55 | (3 << 6)                  # slot 3 of byte 10 in row 2
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_unpack(codes, 3, 256)
+    assert e.value.status == 6
+    assert e.value.index == 2 * 256 + 10 * 4 + 3
+    assert "code 3" in str(e.value)

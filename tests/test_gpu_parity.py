@@ -1,0 +1,208 @@
+"""HIP path against the oracle, through the C ABI (needs an MI355X).
+
+Bars: bit-exact on the integer-exact sets (integer activations in [-8, 8],
+power-of-two scales: every partial sum is exact in fp32, so any summation order
+gives the oracle's value); elsewhere |y - y_ref| <= 2e-3 * A + 1e-5 per element
+with A = sum |s * t * x| from the oracle.
+"""
+import numpy as np
+import pytest
+
+import binary_g128_bit_amd as tq
+import oracle
+from binary_g128_bit_amd import synth
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+TERN, BIN = tq.TQ_TERNARY, tq.TQ_BINARY
+THREADS = oracle.default_threads()
+
+
+def up(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def gpu_gemm(codes, s, X, variant, N, K):
+    """Y[M][N] through tq_gemv (M == 1) or tq_gemm."""
+    cd, sd, Xd = up(codes), up(s), up(X)
+    if X.shape[0] == 1:
+        y = tq.tq_gemv(cd, sd, Xd[0], variant=variant)
+        Y = y.reshape(1, N)
+    else:
+        Y = tq.tq_gemm(cd, sd, Xd, variant=variant)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy()
+
+
+def assert_tol(Y, Yref, A, what=""):
+    err = np.abs(Y.astype(np.float64) - Yref)
+    bound = 2e-3 * A + 1e-5
+    bad = err > bound
+    assert not bad.any(), "%s: %d bad, worst err %.3g vs bound %.3g; max err/A %.3g" % (
+        what, bad.sum(), err[bad].max(), bound[bad][np.argmax(err[bad])], (err / np.maximum(A, 1e-30)).max())
+
+
+def case(seed, N, K, M, variant, exact):
+    t, s, X = synth.problem(seed, N, K, M, variant, exact)
+    codes = tq.tq_pack(t, variant)
+    return codes, s, X
+
+
+SHAPES = [(1, 128), (7, 256), (33, 384), (100, 640), (1000, 1024), (257, 5120),
+          (65, 17408), (3, 30720), (129, 6144)]
+
+
+@pytest.mark.parametrize("variant", [TERN, BIN])
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_gemv_integer_exact(N, K, variant):
+    codes, s, X = case(7000 + N + K, N, K, 1, variant, exact=True)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, _ = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert np.array_equal(Y.astype(np.float64), Yref)
+
+
+@pytest.mark.parametrize("variant", [TERN, BIN])
+@pytest.mark.parametrize("N,K", SHAPES)
+def test_gemv_random(N, K, variant):
+    codes, s, X = case(8000 + N + K, N, K, 1, variant, exact=False)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, A = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert_tol(Y, Yref, A, "N=%d K=%d" % (N, K))
+
+
+def test_gemv_c1_ternary():
+    N, K = synth.C1
+    codes, s, X = case(synth.seed_for(1, 0), N, K, 1, TERN, exact=False)
+    Y = gpu_gemm(codes, s, X, TERN, N, K)
+    Yref, A = oracle.gemm(codes, s, X, N, K, TERN, threads=THREADS)
+    assert_tol(Y, Yref, A, "C1")
+
+
+# the decode shapes of the 27B-like stack, at full size
+STACK_SHAPES = [synth.GATE_UP, synth.DOWN, (6144, 5120), (1024, 5120), (5120, 6144),
+                (14336, 5120),
+                # input-shared fusions: [gate; up], [q; k; v], [lin_qkv; lin_z]
+                (34816, 5120), (8192, 5120), (20480, 5120)]
+
+
+@pytest.mark.parametrize("variant", [TERN, BIN])
+@pytest.mark.parametrize("N,K", STACK_SHAPES)
+def test_gemv_full_size(N, K, variant):
+    codes, s, X = case(synth.seed_for(2, N % 97 + K % 89), N, K, 1, variant, exact=False)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, A = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert_tol(Y, Yref, A, "full %dx%d" % (N, K))
+    # integer-exact at the same shape: bit for bit
+    codes, s, X = case(synth.seed_for(2, 50 + N % 97), N, K, 1, variant, exact=True)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, _ = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert np.array_equal(Y.astype(np.float64), Yref)
+
+
+def test_gemv_special_values():
+    """Negative and subnormal scales, subnormal and zero activations, all-zero
+    and all-one trits."""
+    N, K = 64, 1024
+    g = synth.rng(31)
+    t = synth.trits(g, N, K, TERN)
+    t[0] = 0
+    t[1] = 1
+    t[2] = -1
+    s = synth.scales(g, N, K)
+    s[3] = -s[3]
+    s[4, :] = np.float16(2.0 ** -20)
+    X = synth.activations(g, 1, K)
+    X[0, :64] = np.float16(2.0 ** -24) * np.arange(64)
+    X[0, 200:300] = 0
+    codes = tq.tq_pack(t)
+    Y = gpu_gemm(codes, s, X, TERN, N, K)
+    Yref, A = oracle.gemm(codes, s, X, N, K, TERN)
+    assert_tol(Y, Yref, A, "special")
+    # all-zero trits: only the rounding residue of the per-group offsets remains
+    assert abs(Y[0, 0]) <= 1e-6
+
+
+@pytest.mark.parametrize("p_zero", [0.9, 0.99, 1.0])
+def test_gemv_sparse_rows(p_zero):
+    """Mostly-zero trits make sum |s t x| small; the error must shrink with it."""
+    N, K = 512, 5120
+    g = synth.rng(int(p_zero * 1000))
+    t = synth.trits(g, N, K, TERN)
+    t[g.random((N, K)) < p_zero] = 0
+    s = synth.scales(g, N, K)
+    X = synth.activations(g, 1, K)
+    codes = tq.tq_pack(t)
+    Y = gpu_gemm(codes, s, X, TERN, N, K)
+    Yref, A = oracle.gemm(codes, s, X, N, K, TERN)
+    assert_tol(Y, Yref, A, "sparse %.2f" % p_zero)
+
+
+def test_gemv_deterministic_and_canaries():
+    N, K = synth.DOWN
+    codes, s, X = case(9100, N, K, 1, TERN, exact=False)
+    cd, sd, xd = up(codes), up(s), up(X[0])
+    pad = 64
+    ybig = torch.full((N + 2 * pad,), float("nan"), device="cuda")
+    y = ybig[pad:pad + N]
+    tq.tq_gemv(cd, sd, xd, y)
+    torch.cuda.synchronize()
+    first = y.clone()
+    for _ in range(3):
+        tq.tq_gemv(cd, sd, xd, y)
+    torch.cuda.synchronize()
+    assert torch.equal(first, y)
+    assert torch.isnan(ybig[:pad]).all() and torch.isnan(ybig[pad + N:]).all()
+    assert not torch.isnan(y).any()
+
+
+def test_gemv_rejects_misaligned_device_pointer():
+    N, K = 16, 256
+    codes, s, X = case(9200, N, K, 1, TERN, exact=False)
+    xbuf = torch.zeros(K + 8, dtype=torch.float16, device="cuda")
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_gemv(up(codes), up(s), xbuf[1:1 + K])
+    assert e.value.status == 7
+
+
+@pytest.mark.parametrize("variant", [TERN, BIN])
+@pytest.mark.parametrize("M", [2, 4, 8, 16, 64])
+@pytest.mark.parametrize("N,K", [(33, 384), (300, 1024), (65, 5120)])
+def test_gemm_small(M, N, K, variant):
+    codes, s, X = case(9300 + M + N + K, N, K, M, variant, exact=True)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, _ = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert np.array_equal(Y.astype(np.float64), Yref)
+    codes, s, X = case(9400 + M + N + K, N, K, M, variant, exact=False)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, A = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert_tol(Y, Yref, A, "gemm M=%d" % M)
+
+
+def _sampled_rows(N, n, seed):
+    g = synth.rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, N - 1], g.integers(0, N, n)]))
+    return rows
+
+
+@pytest.mark.parametrize("M", [4, 16, 64, 512])
+@pytest.mark.parametrize("N,K", [synth.GATE_UP, synth.DOWN])
+def test_gemm_full_size_sampled(M, N, K):
+    """Speculative-verify / prefill widths on the MLP shapes: the full GEMM on
+    the GPU, the oracle on sampled output rows."""
+    codes, s, X = case(synth.seed_for(4, M + N % 7), N, K, M, TERN, exact=False)
+    Y = gpu_gemm(codes, s, X, TERN, N, K)
+    rows = _sampled_rows(N, 256 if M <= 64 else 64, M)
+    Yref, A = oracle.gemm(codes[rows], s[rows], X, len(rows), K, TERN, threads=THREADS)
+    assert_tol(Y[:, rows], Yref, A, "gemm M=%d %dx%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [1, 8])
+def test_lm_head_sampled(M):
+    """Ternary LM head 5120 -> 248320 at batch 1 and 8."""
+    N, K = synth.LM_HEAD
+    codes, s, X = case(synth.seed_for(5, M), N, K, M, TERN, exact=False)
+    Y = gpu_gemm(codes, s, X, TERN, N, K)
+    rows = _sampled_rows(N, 512, 77 + M)
+    Yref, A = oracle.gemm(codes[rows], s[rows], X, len(rows), K, TERN, threads=THREADS)
+    assert_tol(Y[:, rows], Yref, A, "lm head M=%d" % M)
