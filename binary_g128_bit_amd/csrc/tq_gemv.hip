@@ -14,15 +14,19 @@
 //   M: a code moved to bits [8,10) under an exponent field of 1 is the FP16
 //      2^-14 * (1 + c/4): an offset only four times the code's unit.
 // One shifted copy of a code dword serves one E pair and one M pair (slot p
-// in the low half, slot p + 8 in the high half), so 16 weights cost 3 shifts,
-// 8 masks and 8 v_dot2_f32_f16 into two fp32 accumulators.  Per group the
-// offsets of the M pairs and sum x (t = c - 1) are removed with one constant
-// computed while x is staged:  sum t*x = aE*2^14 + aM*2^16 - (sum x + 4 S_M),
-// where S_M sums x over the M slots.  Rounding stays proportional to the
-// terms summed: the largest offset is 4x the code unit, so a row of zero
-// trits leaves only a residue of order 2^-22 * sum |s * x|.  The 1-bit
-// variant uses the same E slot (bit 10) plus two M slots (bits 9 and 8) and
-// forms 2 * sum b*x - sum x.
+// in the low half, slot p + 8 in the high half); a 64-bit shift moves two
+// code dwords at once (the bits it carries across the dword boundary land
+// where no mask looks).  The activations of E slots are staged pre-scaled by
+// 1/4, so both kinds of products come out in units of 2^-16 and accumulate
+// together; per 16-byte chunk the offsets of the M slots and sum x (t = c - 1)
+// are removed by seeding the accumulator with -(sum x + 4 S_M) * 2^-16, a
+// constant computed while x is staged (S_M sums x over the M slots), and the
+// row total is scaled by 2^16 once.  Rounding stays proportional to the terms
+// summed: the largest offset is 4x the code unit, so a row of zero trits
+// leaves only a residue of order 2^-22 * sum |s * x|.  The 1-bit variant uses
+// the same E slot (bit 10) and two M slots (bits 9 and 8, activations
+// pre-scaled by 1/4 and 1/2), seeds with -(sum x + 4 S_9 + 8 S_8) * 2^-17 and
+// scales by 2^17, which forms 2 * sum b*x - sum x = sum t*x.
 //
 // Work split.  A wave owns 64/LPR row slots of LPR lanes each; lane j of a
 // slot takes groups j, j+LPR, j+2*LPR, ... of its RPL rows.  Each lane first
@@ -41,9 +45,7 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
-constexpr int kXStride = 68;  // dwords per group in LDS: 64 pairs + 4 pad (bank spread)
+constexpr size_t kMaxLds = 163840;  // bytes of LDS one gfx950 workgroup may use
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
@@ -63,44 +65,67 @@ struct Masks {
 
 constexpr uint32_t kExp1 = 0x04000400u;  // exponent field 1 in both halves
 
-// 16 ternary codes of dword d against pairs xp[p] = (x[p], x[p+8]).
-// aE gets c * 2^-14 * x for slots 1, 3, 5, 7; aM gets 2^-14 (1 + c/4) x for
-// slots 0, 2, 4, 6.
-__device__ __forceinline__ void tern_acc16(uint32_t d, const uint32_t *xp, float &aE, float &aM,
+typedef uint64_t u64;
+
+// 32 ternary codes (dwords d0, d1) against pairs xp[p] = (x[p], x[p+8]) of
+// each dword's 16 weights (E pairs pre-scaled by 1/4).  aE takes slots
+// 1, 3, 5, 7 (E), aM slots 0, 2, 4, 6 (M), both in units of 2^-16.
+__device__ __forceinline__ void tern_acc32(uint32_t d0, uint32_t d1, const uint32_t *xp0,
+                                           const uint32_t *xp1, float &aE, float &aM,
                                            const Masks &k) {
-    aE = dot2(d & 0x0C000C00u, xp[5], aE);
-    aM = dot2((d & k.m8) | kExp1, xp[4], aM);
-    const uint32_t l4 = d << 4, l8 = d << 8, r4 = d >> 4;
-    aE = dot2(l4 & 0x0C000C00u, xp[3], aE);
-    aM = dot2((l4 & k.m8) | kExp1, xp[2], aM);
-    aE = dot2(l8 & 0x0C000C00u, xp[1], aE);
-    aM = dot2((l8 & k.m8) | kExp1, xp[0], aM);
-    aE = dot2(r4 & 0x0C000C00u, xp[7], aE);
-    aM = dot2((r4 & k.m8) | kExp1, xp[6], aM);
+    const u64 dd = ((u64)d1 << 32) | d0;
+    const u64 l4 = dd << 4, l8 = dd << 8, r4 = dd >> 4;
+    const uint32_t c0[4] = {d0, (uint32_t)l4, (uint32_t)l8, (uint32_t)r4};
+    const uint32_t c1[4] = {d1, (uint32_t)(l4 >> 32), (uint32_t)(l8 >> 32), (uint32_t)(r4 >> 32)};
+    // copy q brings E slot pe[q] and M slot pm[q] to bits [10,12) / [8,10)
+    constexpr int pe[4] = {5, 3, 1, 7}, pm[4] = {4, 2, 0, 6};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        aE = dot2(c0[q] & 0x0C000C00u, xp0[pe[q]], aE);
+        aM = dot2((c0[q] & k.m8) | kExp1, xp0[pm[q]], aM);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        aE = dot2(c1[q] & 0x0C000C00u, xp1[pe[q]], aE);
+        aM = dot2((c1[q] & k.m8) | kExp1, xp1[pm[q]], aM);
+    }
 }
 
-// 32 binary bits of dword d against pairs xp[p] = (x[p], x[p+16]).
-// aE: b * 2^-14 (bit at 10); a9: 2^-14 (1 + b/2) (bit at 9); a8: 2^-14 (1 + b/4).
+// 64 binary bits (dwords d0, d1) against pairs xp[p] = (x[p], x[p+16]) of
+// each dword's 32 weights.  aE: bit at 10, b * 2^-14 (x pre-scaled by 1/4);
+// a9: bit at 9, 2^-14 (1 + b/2) (x by 1/2); a8: bit at 8, 2^-14 (1 + b/4).
 // Copies d << s for s in {0, 3, 6, 9, -3, -6} bring bits 10-s, 9-s, 8-s there.
-__device__ __forceinline__ void bin_acc32(uint32_t d, const uint32_t *xp, float &aE, float &a9,
-                                          float &a8, const Masks &k) {
-    const uint32_t c0 = d, c3 = d << 3, c6 = d << 6, c9 = d << 9, r3 = d >> 3, r6 = d >> 6;
-    aE = dot2(c0 & 0x04000400u, xp[10], aE);
-    a9 = dot2((c0 & k.m9) | kExp1, xp[9], a9);
-    a8 = dot2((c0 & k.b8) | kExp1, xp[8], a8);
-    aE = dot2(c3 & 0x04000400u, xp[7], aE);
-    a9 = dot2((c3 & k.m9) | kExp1, xp[6], a9);
-    a8 = dot2((c3 & k.b8) | kExp1, xp[5], a8);
-    aE = dot2(c6 & 0x04000400u, xp[4], aE);
-    a9 = dot2((c6 & k.m9) | kExp1, xp[3], a9);
-    a8 = dot2((c6 & k.b8) | kExp1, xp[2], a8);
-    aE = dot2(c9 & 0x04000400u, xp[1], aE);
-    a9 = dot2((c9 & k.m9) | kExp1, xp[0], a9);
-    aE = dot2(r3 & 0x04000400u, xp[13], aE);
-    a9 = dot2((r3 & k.m9) | kExp1, xp[12], a9);
-    a8 = dot2((r3 & k.b8) | kExp1, xp[11], a8);
-    a9 = dot2((r6 & k.m9) | kExp1, xp[15], a9);
-    a8 = dot2((r6 & k.b8) | kExp1, xp[14], a8);
+__device__ __forceinline__ void bin_acc64(uint32_t d0, uint32_t d1, const uint32_t *xp0,
+                                          const uint32_t *xp1, float &aE, float &aM,
+                                          const Masks &k) {
+    const u64 dd = ((u64)d1 << 32) | d0;
+    const u64 sh[5] = {dd << 3, dd << 6, dd << 9, dd >> 3, dd >> 6};
+    const uint32_t *xps[2] = {xp0, xp1};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t *xp = xps[h];
+        const uint32_t c0 = h ? d1 : d0;
+        uint32_t c[5];
+#pragma unroll
+        for (int i = 0; i < 5; ++i) c[i] = h ? (uint32_t)(sh[i] >> 32) : (uint32_t)sh[i];
+        const uint32_t c3 = c[0], c6 = c[1], c9 = c[2], r3 = c[3], r6 = c[4];
+        aE = dot2(c0 & 0x04000400u, xp[10], aE);
+        aM = dot2((c0 & k.m9) | kExp1, xp[9], aM);
+        aE = dot2((c0 & k.b8) | kExp1, xp[8], aE);
+        aM = dot2(c3 & 0x04000400u, xp[7], aM);
+        aE = dot2((c3 & k.m9) | kExp1, xp[6], aE);
+        aM = dot2((c3 & k.b8) | kExp1, xp[5], aM);
+        aE = dot2(c6 & 0x04000400u, xp[4], aE);
+        aM = dot2((c6 & k.m9) | kExp1, xp[3], aM);
+        aE = dot2((c6 & k.b8) | kExp1, xp[2], aE);
+        aM = dot2(c9 & 0x04000400u, xp[1], aM);
+        aE = dot2((c9 & k.m9) | kExp1, xp[0], aE);
+        aM = dot2(r3 & 0x04000400u, xp[13], aM);
+        aE = dot2((r3 & k.m9) | kExp1, xp[12], aE);
+        aM = dot2((r3 & k.b8) | kExp1, xp[11], aM);
+        aE = dot2((r6 & k.m9) | kExp1, xp[15], aE);
+        aM = dot2((r6 & k.b8) | kExp1, xp[14], aM);
+    }
 }
 
 template <int CTRL>
@@ -122,17 +147,21 @@ __device__ __forceinline__ float seg_sum(float v) {
 }
 
 // x staging.  Ternary unit: 16 weights -> 8 pairs (p, p+8); binary unit:
-// 32 weights -> 16 pairs (p, p+16).  The UPG units of a group sit in
-// consecutive lanes, so their partial constants reduce with seg_sum.  LDS
-// holds, per group, 64 pair dwords, then the group constant (a float) at [64].
+// 32 weights -> 16 pairs (p, p+16).  Four consecutive units make one 16-byte
+// code chunk (64 ternary or 128 binary weights).  In LDS every chunk has a
+// slot of CHUNK_DW dwords: its pairs, then its constant (a float), then pad,
+// so chunk c of a row sits at c * CHUNK_DW and the compute loop addresses
+// every chunk with an immediate offset.  Slots past the last real chunk (a
+// ragged row shape) hold zeros, which makes their contribution exactly 0.
 template <int VARIANT>
 struct XUnit {
     static constexpr int UNIT = VARIANT == TQ_TERNARY ? 16 : 32;
-    static constexpr int UPG = 128 / UNIT;
-    static constexpr int V4 = UNIT / 8;  // 16-byte loads per unit
+    static constexpr int PAIRS = 4 * UNIT / 2;        // pair dwords per chunk
+    static constexpr int CHUNK_DW = PAIRS + 4;        // 36 or 68: 16-byte aligned, bank-spread
+    static constexpr int V4 = UNIT / 8;               // 16-byte loads per unit
     u32x4 v[V4];
 
-    // FP16 pair (w, w) weighting pair p in the per-group constant
+    // FP16 pair (w, w) weighting pair p in the chunk constant
     static __device__ __forceinline__ uint32_t zweight(int p) {
         if constexpr (VARIANT == TQ_TERNARY) {
             return (p & 1) ? 0x3C003C00u : 0x45004500u;  // 1 : 5
@@ -142,228 +171,341 @@ struct XUnit {
         }
     }
 
+    // accumulator units: 2^-16 (ternary) or 2^-17 (binary, which also folds the 2 of 2b - 1)
+    static constexpr float kSeedScale = VARIANT == TQ_TERNARY ? 1.52587890625e-05f : 7.62939453125e-06f;
+    static constexpr float kRowScale = VARIANT == TQ_TERNARY ? 65536.0f : 131072.0f;
+
+    // pair p as staged: E slots times 1/4, binary bit-9 slots times 1/2
+    static __device__ __forceinline__ uint32_t prescale(int p, uint32_t v) {
+        bool e, h;
+        if constexpr (VARIANT == TQ_TERNARY) {
+            e = p & 1;
+            h = false;
+        } else {
+            e = p % 3 == 1;
+            h = p % 3 == 0;
+        }
+        if (!e && !h) return v;
+        const half2_t f = e ? half2_t{(_Float16)0.25f, (_Float16)0.25f} : half2_t{(_Float16)0.5f, (_Float16)0.5f};
+        return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v) * f);
+    }
+
     __device__ __forceinline__ void load(const uint16_t *__restrict__ x, int u) {
         const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (size_t)u * UNIT);
 #pragma unroll
         for (int i = 0; i < V4; ++i) v[i] = src[i];
     }
 
-    __device__ __forceinline__ void store(uint32_t *xs, int u) const {
-        const int g = u / UPG, ug = u % UPG;
+    // Writes unit u (zeros when !real) into its chunk slot; the lane holding a
+    // chunk's first unit writes the chunk constant.  The four units of a chunk
+    // are four aligned consecutive lanes, so the constant reduces with seg_sum.
+    __device__ __forceinline__ void store(uint32_t *xs, int u, bool real) const {
         uint32_t xp[UNIT / 2];
         // low halves x[0..UNIT/2), high halves x[UNIT/2..UNIT)
 #pragma unroll
         for (int i = 0; i < UNIT / 4; ++i) {
             const uint32_t l = v[i / 4][i % 4], h = v[V4 / 2 + i / 4][i % 4];
-            xp[2 * i] = (l & 0xFFFFu) | (h << 16);
-            xp[2 * i + 1] = (l >> 16) | (h & 0xFFFF0000u);
+            xp[2 * i] = real ? (l & 0xFFFFu) | (h << 16) : 0u;
+            xp[2 * i + 1] = real ? (l >> 16) | (h & 0xFFFF0000u) : 0u;
         }
-        // per-group constant: sum over the pairs of w_p * (x[p] + x[p+UNIT/2]) where
-        // w = 1 for E slots and 1 + 4 (ternary M), 1 + 4 (binary bit 9) or
-        // 1 + 8 (binary bit 8) for the offset-carrying slots
+        // seed: -(sum over the pairs of w_p * (x[p] + x[p+UNIT/2])) * 2^-F with
+        // w = 1 for E slots, 1 + 4 (ternary M, binary bit 9), 1 + 8 (binary bit 8)
         float z = 0.0f;
 #pragma unroll
         for (int i = 0; i < UNIT / 2; ++i) z = dot2(xp[i], zweight(i), z);
-        uint32_t *dst = xs + g * kXStride + ug * (UNIT / 2);
+        // E slots (and binary bit-9 slots) are stored pre-scaled to unit 2^-16
+#pragma unroll
+        for (int i = 0; i < UNIT / 2; ++i) xp[i] = prescale(i, xp[i]);
+        uint32_t *slot = xs + (u >> 2) * CHUNK_DW;
+        uint32_t *dst = slot + (u & 3) * (UNIT / 2);
 #pragma unroll
         for (int i = 0; i < UNIT / 8; ++i)
             reinterpret_cast<u32x4 *>(dst)[i] = u32x4{xp[4 * i], xp[4 * i + 1], xp[4 * i + 2], xp[4 * i + 3]};
-        z = seg_sum<UPG>(z);
-        if (ug == 0) xs[g * kXStride + 64] = __builtin_bit_cast(uint32_t, z);
+        z = seg_sum<4>(z) * -kSeedScale;
+        if ((u & 3) == 0) slot[PAIRS] = __builtin_bit_cast(uint32_t, z);
     }
 };
 
-template <int VARIANT, int LPR, int GPL, int RPL>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(const uint8_t *__restrict__ codes,
-                                                        const uint16_t *__restrict__ scales,
-                                                        const uint16_t *__restrict__ x,
-                                                        float *__restrict__ y, int N, int K) {
+// Decode and dot one 16-byte chunk position for RPL rows and fold it into
+// their accumulators: acc[r] += s[r] * (sum of row r's chunk products, in the
+// accumulator unit).  xg is the chunk's LDS slot, read once for all RPL rows.
+template <int VARIANT, int RPL>
+__device__ __forceinline__ void chunk_dot(const u32x4 (&c)[RPL], const uint32_t *xg,
+                                          const uint32_t (&sbits)[RPL], float (&acc)[RPL],
+                                          const Masks &km) {
+    using XU = XUnit<VARIANT>;
+    const float seed = __builtin_bit_cast(float, xg[XU::PAIRS]);
+    float aE[RPL], aM[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        aE[r] = 0.0f;
+        aM[r] = seed;
+    }
+#pragma unroll
+    for (int d = 0; d < 4; d += 2) {
+        if constexpr (VARIANT == TQ_TERNARY) {
+            const u32x4 q0 = reinterpret_cast<const u32x4 *>(xg + 8 * d)[0];
+            const u32x4 q1 = reinterpret_cast<const u32x4 *>(xg + 8 * d)[1];
+            const u32x4 q2 = reinterpret_cast<const u32x4 *>(xg + 8 * d)[2];
+            const u32x4 q3 = reinterpret_cast<const u32x4 *>(xg + 8 * d)[3];
+            const uint32_t xp0[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+            const uint32_t xp1[8] = {q2[0], q2[1], q2[2], q2[3], q3[0], q3[1], q3[2], q3[3]};
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) tern_acc32(c[r][d], c[r][d + 1], xp0, xp1, aE[r], aM[r], km);
+        } else {
+            uint32_t xp0[16], xp1[16];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const u32x4 qa = reinterpret_cast<const u32x4 *>(xg + 16 * d)[v];
+                const u32x4 qb = reinterpret_cast<const u32x4 *>(xg + 16 * d + 16)[v];
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    xp0[4 * v + w] = qa[w];
+                    xp1[4 * v + w] = qb[w];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) bin_acc64(c[r][d], c[r][d + 1], xp0, xp1, aE[r], aM[r], km);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPL; ++r)
+        acc[r] = __builtin_fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)sbits[r]), aE[r] + aM[r],
+                                acc[r]);
+}
+
+// One row block = RPL * 64/LPR consecutive rows handled by one wave: LPR lanes
+// per row, lane (seg, j) takes rows seg, seg + 64/LPR, ... of the block and in
+// each the 16-byte chunks j, j+LPR, ..., so consecutive lanes read consecutive
+// 16 bytes.  When LPR*NU exceeds the chunks of a row (RAGGED), chunk and scale
+// indices are clamped into the row; those slots' x is zero, so they contribute
+// nothing.  Otherwise every chunk is the row base plus a compile-time offset.
+// Scales are loaded first and kept zero-extended, one per register.
+template <int VARIANT, int LPR, int NU, int RPL, bool RAGGED>
+__device__ __forceinline__ void load_block(const uint8_t *__restrict__ codes,
+                                           const uint16_t *__restrict__ scales, const int (&row)[RPL],
+                                           int j, int CPR, int G, u32x4 (&c)[NU][RPL],
+                                           uint32_t (&s)[NU][RPL]) {
+    constexpr int CPG = VARIANT == TQ_TERNARY ? 2 : 1;  // 16-byte chunks per group
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const uint16_t *sp = scales + (size_t)row[r] * G;
+#pragma unroll
+        for (int i = 0; i < NU; ++i)
+            s[i][r] = RAGGED ? sp[min(j + i * LPR, CPR - 1) / CPG] : sp[j / CPG + i * (LPR / CPG)];
+    }
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const u32x4 *rp = reinterpret_cast<const u32x4 *>(codes + (size_t)row[r] * CPR * 16);
+#pragma unroll
+        for (int i = 0; i < NU; ++i)
+            c[i][r] = __builtin_nontemporal_load(rp + (RAGGED ? min(j + i * LPR, CPR - 1) : j + i * LPR));
+    }
+}
+
+// This lane's share of a block: per row, the sum over its chunks reduced over
+// the row's LPR lanes, times the accumulator's power-of-two unit.  The
+// scheduling barrier keeps one chunk's activations live at a time.
+template <int VARIANT, int LPR, int NU, int RPL>
+__device__ __forceinline__ void block_dot(const u32x4 (&c)[NU][RPL], const uint32_t (&s)[NU][RPL],
+                                          const uint32_t *xj, const Masks &km, float (&out)[RPL]) {
+    float acc[RPL];
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        chunk_dot<VARIANT, RPL>(c[i], xj + i * LPR * XUnit<VARIANT>::CHUNK_DW, s[i], acc, km);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) out[r] = seg_sum<LPR>(acc[r]) * XUnit<VARIANT>::kRowScale;
+}
+
+// Persistent GEMV.  Each workgroup stages x once, then its waves walk the
+// workgroup's contiguous range of row blocks round-robin, prefetching the
+// next block while decoding the current one (two register sets, ping-pong).
+template <int VARIANT, int LPR, int NU, int RPL, int WAVES, bool RAGGED>
+__global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restrict__ codes,
+                                                          const uint16_t *__restrict__ scales,
+                                                          const uint16_t *__restrict__ x,
+                                                          float *__restrict__ y, int N, int K) {
     extern __shared__ uint32_t xs[];
     using XU = XUnit<VARIANT>;
-    constexpr int RS = 64 / LPR;                       // row slots per wave
-    constexpr int DW = VARIANT == TQ_TERNARY ? 8 : 4;  // code dwords per group
-    // units of x each thread stages; held in registers when few enough
-    constexpr int XMAX = (LPR * GPL * XU::UPG + kThreads - 1) / kThreads;
-    constexpr bool XREG = XMAX <= 5;
-    const int G = K >> 7;
-    const int nunits = G * XU::UPG;
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int RS = 64 / LPR;                        // rows per wave slot
+    constexpr int RB = RS * RPL;                        // rows per block
+    constexpr int CAP = LPR * NU;                       // chunk slots per row
+    constexpr int XMAX = (CAP * 4 + THREADS - 1) / THREADS;
+    const int G = K >> 7, CPR = G * (VARIANT == TQ_TERNARY ? 2 : 1);
+    const int nunits = CPR * 4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int seg = lane / LPR, j = lane % LPR;
+    const int nblocks = (N + RB - 1) / RB;
+    const int b_begin = (int)(((long long)blockIdx.x * nblocks) / gridDim.x);
+    const int b_end = (int)(((long long)(blockIdx.x + 1) * nblocks) / gridDim.x);
     const Masks km;
-    const int row0 = (blockIdx.x * kWaves + wave) * (RS * RPL) + seg;
-    const size_t row_bytes = (size_t)K / (VARIANT == TQ_TERNARY ? 4 : 8);
+    auto rows_of = [&](int bb, int (&row)[RPL]) {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) row[r] = min(bb * RB + r * RS + seg, N - 1);
+    };
 
-    // All global loads below are unconditional (indices clamped into range) so
-    // that the wait counters can be tracked exactly: each use waits only for
-    // the loads it needs, never for the whole stream.
-    // 1. x loads for staging first (L2-resident, short latency)
-    XU xu[XREG ? XMAX : 1];
-    if constexpr (XREG) {
+    // 1. x loads for staging, then the first block's codes and scales
+    XU xu[XMAX];
 #pragma unroll
-        for (int k = 0; k < XMAX; ++k) xu[k].load(x, min((int)threadIdx.x + k * kThreads, nunits - 1));
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep the x loads ahead of the code loads
+    for (int k = 0; k < XMAX; ++k)
+        xu[k].load(x, min(min((int)threadIdx.x + k * THREADS, CAP * 4 - 1), nunits - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 ca[NU][RPL], cb[NU][RPL];
+    uint32_t sa[NU][RPL], sb[NU][RPL];
+    int b = b_begin + wave;
+    int row[RPL];
+    rows_of(min(b, b_end - 1), row);
+    load_block<VARIANT, LPR, NU, RPL, RAGGED>(codes, scales, row, j, CPR, G, ca, sa);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // 2. every code and scale load of this lane; groups past G get scale 0
-    uint32_t cw[GPL][RPL][DW];
-    uint32_t sb[GPL][RPL];
+    // 2. permuted x and chunk constants into LDS (zero slots past the row).
+    // Threads past the last slot redo the last unit (identical data; only the
+    // first unit of a chunk writes its constant): an unconditional store keeps
+    // the x loads from being sunk below the code stream.
 #pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-        const int g = min(j + i * LPR, G - 1);
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) {
-            const int row = min(row0 + r * RS, N - 1);
-            const u32x4 *p = reinterpret_cast<const u32x4 *>(codes + (size_t)row * row_bytes +
-                                                             (size_t)g * (DW * 4));
-#pragma unroll
-            for (int v = 0; v < DW / 4; ++v) {
-                const u32x4 q = __builtin_nontemporal_load(p + v);
-#pragma unroll
-                for (int w = 0; w < 4; ++w) cw[i][r][4 * v + w] = q[w];
-            }
-            sb[i][r] = scales[(size_t)row * G + g];
-        }
-    }
-    __builtin_amdgcn_sched_barrier(0);  // staging must not be hoisted above the code loads
-
-    // 3. permute x into LDS with the per-group constants
-    if constexpr (XREG) {
-        // lanes past the last unit re-store that unit's identical data; its group
-        // constant is written only by the lane holding the group's first unit
-#pragma unroll
-        for (int k = 0; k < XMAX; ++k) xu[k].store(xs, min((int)threadIdx.x + k * kThreads, nunits - 1));
-    } else {
-        for (int u = threadIdx.x; u < nunits; u += kThreads) {
-            xu[0].load(x, u);
-            xu[0].store(xs, u);
-        }
+    for (int k = 0; k < XMAX; ++k) {
+        const int u = min((int)threadIdx.x + k * THREADS, CAP * 4 - 1);
+        xu[k].store(xs, u, u < nunits);
     }
     __syncthreads();
 
-    // 4. decode, dot, scale -- group by group as the codes land
-    float yacc[RPL];
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) yacc[r] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-        const bool live = j + i * LPR < G;
-        const uint32_t *xg = xs + min(j + i * LPR, G - 1) * kXStride;
-        const float z = __builtin_bit_cast(float, xg[64]);
-        float aE[RPL], aM[RPL], a8[RPL];
+    // 3. ping-pong over this wave's blocks
+    const uint32_t *xj = xs + j * XU::CHUNK_DW;
+    float out[RPL];
+    for (; b < b_end; b += 2 * WAVES) {
+        const int b2 = b + WAVES;
+        if (b2 < b_end) {
+            rows_of(b2, row);
+            load_block<VARIANT, LPR, NU, RPL, RAGGED>(codes, scales, row, j, CPR, G, cb, sb);
+        }
+        block_dot<VARIANT, LPR, NU, RPL>(ca, sa, xj, km, out);
 #pragma unroll
         for (int r = 0; r < RPL; ++r) {
-            aE[r] = 0.0f;
-            if constexpr (VARIANT == TQ_TERNARY) {
-                aM[r] = -z * 1.52587890625e-05f;  // -z * 2^-16
-                a8[r] = 0.0f;
-            } else {
-                aM[r] = 0.0f;
-                a8[r] = -z * 7.62939453125e-06f;  // -z * 2^-17
-            }
+            const int rr = b * RB + r * RS + seg;
+            if (j == 0 && rr < N) y[rr] = out[r];
         }
-        if constexpr (VARIANT == TQ_TERNARY) {
-#pragma unroll
-            for (int d = 0; d < 8; ++d) {
-                const u32x4 lo = reinterpret_cast<const u32x4 *>(xg + 8 * d)[0];
-                const u32x4 hi = reinterpret_cast<const u32x4 *>(xg + 8 * d)[1];
-                const uint32_t xp[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-#pragma unroll
-                for (int r = 0; r < RPL; ++r) tern_acc16(cw[i][r][d], xp, aE[r], aM[r], km);
-            }
-        } else {
-#pragma unroll
-            for (int d = 0; d < 4; ++d) {
-                uint32_t xp[16];
-#pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const u32x4 q = reinterpret_cast<const u32x4 *>(xg + 16 * d)[v];
-#pragma unroll
-                    for (int w = 0; w < 4; ++w) xp[4 * v + w] = q[w];
-                }
-#pragma unroll
-                for (int r = 0; r < RPL; ++r) bin_acc32(cw[i][r][d], xp, aE[r], aM[r], a8[r], km);
-            }
+        if (b2 >= b_end) break;
+        const int b3 = b2 + WAVES;
+        if (b3 < b_end) {
+            rows_of(b3, row);
+            load_block<VARIANT, LPR, NU, RPL, RAGGED>(codes, scales, row, j, CPR, G, ca, sa);
         }
+        block_dot<VARIANT, LPR, NU, RPL>(cb, sb, xj, km, out);
 #pragma unroll
         for (int r = 0; r < RPL; ++r) {
-            float t;
-            if constexpr (VARIANT == TQ_TERNARY) {
-                t = __builtin_fmaf(aM[r], 65536.0f, aE[r] * 16384.0f);  // aE 2^14 + aM 2^16
-            } else {
-                t = __builtin_fmaf(aM[r], 65536.0f, aE[r] * 32768.0f);  // aE 2^15 + a9 2^16
-                t = __builtin_fmaf(a8[r], 131072.0f, t);                 //   + a8 2^17
-            }
-            const float s = live ? (float)__builtin_bit_cast(_Float16, (uint16_t)sb[i][r]) : 0.0f;
-            yacc[r] = __builtin_fmaf(s, t, yacc[r]);
+            const int rr = b2 * RB + r * RS + seg;
+            if (j == 0 && rr < N) y[rr] = out[r];
         }
-    }
-
-    // 5. reduce across the LPR lanes of each row slot and store
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-        const float v = seg_sum<LPR>(yacc[r]);
-        const int row = row0 + r * RS;
-        if (j == 0 && row < N) y[row] = v;
     }
 }
 
 struct Config {
-    int lpr, gpl, rpl;
+    int lpr, nu;
 };
 
-// Smallest lanes-per-row x groups-per-lane capacity that covers G groups.
-Config pick(int G) {
-    static const Config table[] = {{8, 1, 1}, {8, 2, 1}, {8, 4, 1}, {8, 5, 1}, {8, 6, 1},
-                                   {16, 4, 1}, {32, 5, 1}, {64, 4, 1}};
-    for (const Config &c : table)
-        if (c.lpr * c.gpl >= G) return c;
-    return {0, 0, 0};
+// Lanes-per-row x chunks-per-lane shapes, smallest capacity first.
+constexpr Config kConfigs[] = {{8, 1},  {16, 1}, {8, 2},  {16, 2}, {16, 3}, {8, 5},
+                               {16, 4}, {16, 5}, {32, 3}, {16, 6}, {32, 4}, {32, 5},
+                               {32, 6}, {64, 4}, {64, 5}, {64, 6}, {64, 8}, {64, 12},
+                               {64, 16}};
+
+// The shape with the least capacity that covers CPR chunks; among equal
+// capacities the one with fewer chunks per lane.
+Config pick(int cpr) {
+    Config best{0, 0};
+    for (const Config &c : kConfigs) {
+        const int cap = c.lpr * c.nu;
+        if (cap < cpr) continue;
+        if (!best.lpr || cap < best.lpr * best.nu || (cap == best.lpr * best.nu && c.nu < best.nu))
+            best = c;
+    }
+    return best;
 }
 
-template <int VARIANT, int LPR, int GPL, int RPL>
+// Rows per lane and waves per workgroup for a shape: two rows per lane halve
+// the LDS reads per weight; the wave count keeps two register sets of codes
+// within the VGPRs a lane may use (512 / waves-per-SIMD).
+template <int NU>
+struct Tiling {
+    static constexpr int RPL = NU <= 6 ? 2 : 1;
+    static constexpr int WAVES = NU <= 6 ? 12 : (NU <= 8 ? 16 : 8);
+};
+
+template <int VARIANT, int LPR, int NU>
+constexpr size_t lds_bytes() {
+    return (size_t)LPR * NU * XUnit<VARIANT>::CHUNK_DW * sizeof(uint32_t);
+}
+
+// Compute units of the current device, cached per device.
+int device_cus() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+template <int VARIANT, int LPR, int NU>
 hipError_t launch(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y, int N,
                   int K, hipStream_t stream) {
-    constexpr int rows_per_block = kWaves * (64 / LPR) * RPL;
-    const int G = K / 128;
-    const size_t lds = (size_t)G * kXStride * sizeof(uint32_t);
-    const unsigned blocks = (unsigned)((N + rows_per_block - 1) / rows_per_block);
-    hipLaunchKernelGGL((gemv_kernel<VARIANT, LPR, GPL, RPL>), dim3(blocks), dim3(kThreads), lds,
-                       stream, codes, scales, x, y, N, K);
+    constexpr int RPL = Tiling<NU>::RPL, WAVES = Tiling<NU>::WAVES;
+    constexpr int rows_per_block = (64 / LPR) * RPL;
+    const int nblocks = (N + rows_per_block - 1) / rows_per_block;
+    // one workgroup per CU, but never more workgroups than waves' worth of blocks
+    const int grid = max(1, min(device_cus(), (nblocks + WAVES - 1) / WAVES));
+    constexpr size_t lds = lds_bytes<VARIANT, LPR, NU>();
+    const int cpr = (K / 128) * (VARIANT == TQ_TERNARY ? 2 : 1);
+    if (cpr == LPR * NU)
+        hipLaunchKernelGGL((gemv_kernel<VARIANT, LPR, NU, RPL, WAVES, false>), dim3(grid),
+                           dim3(64 * WAVES), lds, stream, codes, scales, x, y, N, K);
+    else
+        hipLaunchKernelGGL((gemv_kernel<VARIANT, LPR, NU, RPL, WAVES, true>), dim3(grid),
+                           dim3(64 * WAVES), lds, stream, codes, scales, x, y, N, K);
     return hipGetLastError();
 }
 
 template <int VARIANT>
 hipError_t dispatch(const Config &c, const uint8_t *codes, const uint16_t *scales,
-                    const uint16_t *x, float *y, int N, int K, hipStream_t s) {
-#define TQ_CASE(L, Gp, R)                                   \
-    if (c.lpr == L && c.gpl == Gp && c.rpl == R)             \
-        return launch<VARIANT, L, Gp, R>(codes, scales, x, y, N, K, s);
-    TQ_CASE(8, 1, 1)
-    TQ_CASE(8, 2, 1)
-    TQ_CASE(8, 4, 1)
-    TQ_CASE(8, 5, 1)
-    TQ_CASE(8, 6, 1)
-    TQ_CASE(16, 4, 1)
-    TQ_CASE(32, 5, 1)
-    TQ_CASE(64, 4, 1)
+                    const uint16_t *x, float *y, int N, int K, hipStream_t s, size_t *lds) {
+#define TQ_CASE(L, U)                                                       \
+    if (c.lpr == L && c.nu == U) {                                          \
+        *lds = lds_bytes<VARIANT, L, U>();                                  \
+        if (*lds > kMaxLds) return hipErrorInvalidValue;                    \
+        return launch<VARIANT, L, U>(codes, scales, x, y, N, K, s);        \
+    }
+    TQ_CASE(8, 1) TQ_CASE(16, 1) TQ_CASE(8, 2) TQ_CASE(16, 2) TQ_CASE(16, 3) TQ_CASE(8, 5)
+    TQ_CASE(16, 4) TQ_CASE(16, 5) TQ_CASE(32, 3) TQ_CASE(16, 6) TQ_CASE(32, 4) TQ_CASE(32, 5)
+    TQ_CASE(32, 6) TQ_CASE(64, 4) TQ_CASE(64, 5) TQ_CASE(64, 6) TQ_CASE(64, 8) TQ_CASE(64, 12)
+    TQ_CASE(64, 16)
 #undef TQ_CASE
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// Largest K whose staged x fits the 64 KiB of LDS a workgroup may use.
-constexpr int64_t kGemvMaxK = (65536 / (kXStride * 4)) * 128;
-
 int32_t gemv_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
                      int64_t N, int64_t K, int32_t variant, hipStream_t stream) {
-    if (K > kGemvMaxK)
-        return fail(TQ_ERR_SHAPE, "K=%lld above the GEMV limit %lld", (long long)K,
-                    (long long)kGemvMaxK);
-    const Config c = pick((int)(K / 128));
+    const int cpr = (int)(K / 128) * (variant == TQ_TERNARY ? 2 : 1);
+    const Config c = pick(cpr);
+    if (!c.lpr)
+        return fail(TQ_ERR_SHAPE, "K=%lld is above the GEMV limit", (long long)K);
+    size_t lds = 0;
     hipError_t e = variant == TQ_TERNARY
-                       ? dispatch<TQ_TERNARY>(c, codes, scales, x, y, (int)N, (int)K, stream)
-                       : dispatch<TQ_BINARY>(c, codes, scales, x, y, (int)N, (int)K, stream);
+                       ? dispatch<TQ_TERNARY>(c, codes, scales, x, y, (int)N, (int)K, stream, &lds)
+                       : dispatch<TQ_BINARY>(c, codes, scales, x, y, (int)N, (int)K, stream, &lds);
+    if (lds > kMaxLds)
+        return fail(TQ_ERR_SHAPE, "K=%lld needs %zu bytes of LDS, above %zu", (long long)K, lds,
+                    kMaxLds);
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "GEMV launch failed: %s", hipGetErrorString(e));
     return TQ_OK;
 }

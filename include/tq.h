@@ -96,7 +96,8 @@ int32_t tq_unpack(const uint8_t *codes, int64_t N, int64_t K, int32_t group,
  *   scales : device, uint16 [N][K/128] (fp16 bits), 2-byte aligned
  *   x      : device, uint16 [K] (fp16 bits), 16-byte aligned
  *   y      : device, float [N], 4-byte aligned; overwritten
- * Limits: 1 <= N < 2^31, 128 <= K <= 65536. */
+ * Limits: 1 <= N < 2^31, 128 <= K <= 65536 (a workgroup keeps the whole
+ * permuted activation vector in LDS); a larger K returns TQ_ERR_SHAPE. */
 int32_t tq_gemv(const uint8_t *codes, const uint16_t *scales, const uint16_t *x,
                 float *y, int64_t N, int64_t K, int32_t group, int32_t variant,
                 void *stream);

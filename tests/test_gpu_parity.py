@@ -50,7 +50,7 @@ def case(seed, N, K, M, variant, exact):
 
 
 SHAPES = [(1, 128), (7, 256), (33, 384), (100, 640), (1000, 1024), (257, 5120),
-          (65, 17408), (3, 30720), (129, 6144)]
+          (65, 17408), (3, 29952), (129, 6144), (5, 65536)]
 
 
 @pytest.mark.parametrize("variant", [TERN, BIN])
@@ -154,6 +154,16 @@ def test_gemv_deterministic_and_canaries():
     assert torch.equal(first, y)
     assert torch.isnan(ybig[:pad]).all() and torch.isnan(ybig[pad + N:]).all()
     assert not torch.isnan(y).any()
+
+
+def test_gemv_rejects_k_above_limit():
+    N, K = 4, 65536 + 128
+    codes = torch.zeros(N * K // 4, dtype=torch.uint8, device="cuda")
+    s = torch.zeros((N, K // 128), dtype=torch.float16, device="cuda")
+    x = torch.zeros(K, dtype=torch.float16, device="cuda")
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_gemv(codes, s, x)
+    assert e.value.status == 2
 
 
 def test_gemv_rejects_misaligned_device_pointer():
