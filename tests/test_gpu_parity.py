@@ -216,3 +216,58 @@ def test_lm_head_sampled(M):
     rows = _sampled_rows(N, 512, 77 + M)
     Yref, A = oracle.gemm(codes[rows], s[rows], X, len(rows), K, TERN, threads=THREADS)
     assert_tol(Y[:, rows], Yref, A, "lm head M=%d" % M)
+
+
+@pytest.mark.parametrize("variant", [TERN, BIN])
+@pytest.mark.parametrize("M,N,K", [(3, 1, 128), (17, 70, 128), (31, 129, 256), (33, 64, 640),
+                                   (100, 200, 2176), (5, 1000, 29952), (2, 77, 65536)])
+def test_gemm_ragged(M, N, K, variant):
+    """Ragged activation and weight tiles, K of one group (most waves of a
+    workgroup idle) and the largest K."""
+    codes, s, X = case(9700 + M + N + K, N, K, M, variant, exact=True)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, _ = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert np.array_equal(Y.astype(np.float64), Yref)
+    codes, s, X = case(9800 + M + N + K, N, K, M, variant, exact=False)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, A = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert_tol(Y, Yref, A, "gemm M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("M", [4, 16])
+@pytest.mark.parametrize("N,K", [synth.GATE_UP, synth.DOWN])
+def test_gemm_binary_full_size_sampled(M, N, K):
+    codes, s, X = case(synth.seed_for(4, 50 + M + N % 7), N, K, M, BIN, exact=False)
+    Y = gpu_gemm(codes, s, X, BIN, N, K)
+    rows = _sampled_rows(N, 256, 100 + M)
+    Yref, A = oracle.gemm(codes[rows], s[rows], X, len(rows), K, BIN, threads=THREADS)
+    assert_tol(Y[:, rows], Yref, A, "binary gemm M=%d %dx%d" % (M, N, K))
+
+
+def test_gemm_zero_rows_and_special_scales():
+    """All-zero trit rows give |y| <= 1e-5 (the bound with A = 0); zero,
+    subnormal and large scales pass through the FP32 group scaling."""
+    N, K, M = 96, 1024, 8
+    t, s, X = synth.problem(9900, N, K, M, TERN, False)
+    t[:32] = 0
+    s[40, :] = 0
+    s[41, :] = np.float16(6e-8)
+    s[42, :] = np.float16(60000.0)
+    codes = tq.tq_pack(t, TERN)
+    Y = gpu_gemm(codes, s, X, TERN, N, K)
+    Yref, A = oracle.gemm(codes, s, X, N, K, TERN, threads=THREADS)
+    assert_tol(Y, Yref, A, "special")
+    assert np.abs(Y[:, :32]).max() <= 1e-5
+    assert np.all(Y[:, 40] == 0)
+
+
+def test_gemm_deterministic():
+    """The K-split partial sums are added in a fixed order: repeated calls
+    give identical bits."""
+    N, K, M = 2048, 5120, 16
+    codes, s, X = case(9950, N, K, M, TERN, exact=False)
+    cd, sd, Xd = up(codes), up(s), up(X)
+    Y0 = tq.tq_gemm(cd, sd, Xd, variant=TERN)
+    for _ in range(3):
+        Y1 = tq.tq_gemm(cd, sd, Xd, variant=TERN)
+        assert torch.equal(Y0, Y1)
