@@ -5,14 +5,19 @@ A step is one token's pass over one MLP block of packed ternary weights:
 gate 5120->17408, up 5120->17408 and down 17408->5120.  gate and up read the
 same activation, so they are stored as one 34816 x 5120 matrix (rows of gate,
 then rows of up) and run as one GEMV launch; down is a second launch.  Both go
-through the C ABI.  Weights rotate over >= 1 GiB of distinct device buffers so that no
-step reads from the 256 MB last-level cache what the previous one left there.
-Inputs are resident in HBM before the timed region starts.
+through the C ABI.  Weights rotate over >= 1 GiB of distinct device buffers so
+that no step reads from the 256 MB last-level cache what the previous one left
+there.  Inputs are resident in HBM before the timed region starts.
 
 Prints ONE JSON line: packed-weight GB/s (value), % of the 8 TB/s HBM peak,
-equivalent tokens/s of the 6.60 GB 64-layer stack, the roofline object of the
-dominant kernel (timed live with HIP events on its stream) and the oracle's
-CPU baseline on a bounded sample of the same workload.
+the roofline object of the dominant kernel (its launches timed one by one with
+HIP events on its stream), the oracle's CPU baseline on a bounded sample of the
+same workload, and context figures measured in the same run: the 64-layer
+stack sweep (equivalent tokens/s, eager and graph-replayed), the small-batch
+GEMM widths, the 1-bit variant and the LM head.
+
+--only-step runs just the timed step (for counter collection); --copy-calibration
+runs a plain 1 GiB device copy whose known byte count scales the HBM counters.
 """
 import argparse
 import hashlib
@@ -25,13 +30,14 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_HBM_GBS = 8000.0               # MI355X HBM3E, vendor figure
-STACK_BYTES = 6_595_543_040         # packed bytes of the 64-layer 24.83B-weight stack
-TERN_BYTES_PER_WEIGHT = 0.265625    # 2-bit slot + fp16 scale per 128
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, vendor figure
+PEAK_F16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA, vendor figure
+STACK_BYTES = 6_595_543_040  # packed bytes of the 64-layer 24.83B-weight stack
+COPY_BYTES = 1 << 30         # bytes read (and written) by the calibration copy
 
 
-def packed_bytes(N, K):
-    return N * K // 4 + 2 * N * K // 128
+def packed_bytes(N, K, variant=0):
+    return N * K // (8 if variant else 4) + 2 * N * K // 128
 
 
 def parse():
@@ -43,6 +49,12 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target duration of the oracle's CPU-baseline sample")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the stack sweep, GEMM, binary and LM-head figures")
+    p.add_argument("--only-step", action="store_true",
+                   help="run only the timed step (counter runs); implies --no-cpu --no-extras")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run only a 1 GiB device-to-device copy, 5 times")
     return p.parse_args()
 
 
@@ -98,12 +110,234 @@ def cpu_baseline(mats, seconds):
             "sample": "fp64 oracle GEMV, batch 1: %s, %.1f s" % (what, dt)}
 
 
+class Dev:
+    """Device-side synthetic weights for the timing-only figures (the parity
+    tests check the same kernels on the same shapes against the oracle).
+    Ternary code bytes are drawn uniformly from the 81 bytes whose four slots
+    are valid codes, i.e. iid uniform trits; binary bytes are uniform; scales
+    are float16(exp(N(-4, 0.5))); activations float16(N(0, 1))."""
+
+    def __init__(self, torch, tq, dev, seed):
+        import numpy as np
+        self.torch, self.dev = torch, dev
+        self.gen = torch.Generator(device=dev)
+        self.gen.manual_seed(seed)
+        t = np.zeros((81, 128), dtype=np.int8)  # row i: the i-th 4-trit tuple, then zeros
+        t[:, :4] = [[a, b, c, d] for a in (-1, 0, 1) for b in (-1, 0, 1)
+                    for c in (-1, 0, 1) for d in (-1, 0, 1)]
+        self.lut = torch.from_numpy(np.ascontiguousarray(tq.tq_pack(t, tq.TQ_TERNARY)[:, 0])).to(dev)
+
+    def codes(self, N, K, variant):
+        torch = self.torch
+        nbytes = N * K // (8 if variant else 4)
+        out = torch.empty(N, nbytes // N, dtype=torch.uint8, device=self.dev)
+        flat = out.view(-1)
+        chunk = 1 << 26
+        for i in range(0, nbytes, chunk):
+            n = min(chunk, nbytes - i)
+            if variant:
+                flat[i:i + n] = torch.randint(0, 256, (n,), device=self.dev, generator=self.gen,
+                                              dtype=torch.int32).to(torch.uint8)
+            else:
+                flat[i:i + n] = self.lut[torch.randint(0, 81, (n,), device=self.dev,
+                                                       generator=self.gen)]
+        return out
+
+    def scales(self, N, K):
+        torch = self.torch
+        g = torch.randn(N, K // 128, device=self.dev, generator=self.gen)
+        return torch.exp(g * 0.5 - 4.0).to(torch.float16)
+
+    def act(self, M, K):
+        return self.torch.randn(M, K, device=self.dev, generator=self.gen).to(self.torch.float16)
+
+
+def per_launch_ms(torch, stream, launch, n, warm=10):
+    """Average duration of `launch(i)` over n calls, each bracketed by its own
+    pair of HIP events on `stream` (so host gaps between calls are excluded)."""
+    for i in range(warm):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    for i in range(n):
+        ev[i][0].record(stream)
+        launch(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in ev) / n
+
+
+def back_to_back_ms(torch, stream, launch, n, warm=10):
+    """Average time per call of n back-to-back calls between two events."""
+    for i in range(warm):
+        launch(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for i in range(n):
+        launch(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def stack_sweep(torch, tq, gen, stream):
+    """Configs' whole-stack decode sweep: 64 layers, ~24.83B packed ternary
+    weights (6.60 GB), each read once per token.  Input-shared projections are
+    fused (gate;up, q;k;v, lin_qkv;lin_z): 4 GEMV launches per layer."""
+    from binary_g128_bit_amd import synth
+    launches = []   # (codes, scales, x, y)
+    total = 0
+    for mats in synth.stack_layers():
+        d = {name: (N, K) for name, N, K in mats}
+        if "q" in d:
+            groups = [["q", "k", "v"], ["o"], ["gate", "up"], ["down"]]
+        else:
+            groups = [["lin_qkv", "lin_z"], ["lin_out"], ["gate", "up"], ["down"]]
+        for g in groups:
+            N = sum(d[n][0] for n in g)
+            K = d[g[0]][1]
+            c, s = gen.codes(N, K, 0), gen.scales(N, K)
+            x = gen.act(1, K)[0]
+            y = torch.empty(N, dtype=torch.float32, device=gen.dev)
+            launches.append((c, s, x, y))
+            total += packed_bytes(N, K)
+
+    def token():
+        for c, s, x, y in launches:
+            tq.tq_gemv(c, s, x, y)
+
+    for _ in range(3):
+        token()
+    torch.cuda.synchronize()
+    T = 20
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(T):
+        token()
+    b.record(stream)
+    torch.cuda.synchronize()
+    eager_ms = a.elapsed_time(b) / T
+    ref = launches[-1][3].clone()
+
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        token()          # warm the side stream before capture
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        token()
+    for _ in range(3):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_ok = bool(torch.equal(launches[-1][3], ref))
+    a.record(stream)
+    for _ in range(T):
+        graph.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    graph_ms = a.elapsed_time(b) / T
+    graph_ok = graph_ok and bool(torch.equal(launches[-1][3], ref))
+    kernel_ms = sum(per_launch_ms(torch, stream, lambda i, L=L: tq.tq_gemv(*L), 5, warm=2)
+                    for L in launches)
+    del graph
+    return {
+        "workload": "64-layer batch-1 ternary decode sweep, 24.83B weights, each read once "
+                    "per token; 256 GEMV launches per token (input-shared projections fused)",
+        "bytes_per_token": total,
+        "launches_per_token": len(launches),
+        "ms_per_token_eager": round(eager_ms, 4),
+        "ms_per_token_graph": round(graph_ms, 4),
+        "ms_per_token_kernels_only": round(kernel_ms, 4),
+        "tok_s_eager": round(1e3 / eager_ms, 1),
+        "tok_s_graph": round(1e3 / graph_ms, 1),
+        "gbs_graph": round(total / graph_ms / 1e6, 1),
+        "pct_of_hbm_peak_graph": round(100 * total / graph_ms / 1e6 / PEAK_HBM_GBS, 2),
+        "graph_replay_matches_eager": graph_ok,
+    }
+
+
+def gemm_widths(torch, tq, gen, stream, bufs, slots):
+    """Small-batch GEMM (speculative verify / prefill widths) on gate
+    (17408 x 5120, the first half of the fused buffers) and down, rotating."""
+    from binary_g128_bit_amd import synth
+    out = {}
+    for name, m, (N, K) in (("gate_17408x5120", 0, synth.GATE_UP), ("down_5120x17408", 1, synth.DOWN)):
+        pool = [(c[:N], s[:N]) for c, s in (bufs[r][m] for r in range(slots))]
+        X = gen.act(512, K)
+        Y = torch.empty(512, N, dtype=torch.float32, device=gen.dev)
+        for M in synth.GEMM_WIDTHS:
+            Xm, Ym = X[:M], Y[:M]
+            ms = per_launch_ms(torch, stream,
+                               lambda i: tq.tq_gemm(pool[i % len(pool)][0], pool[i % len(pool)][1],
+                                                    Xm, Ym), 50)
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            gbs = packed_bytes(N, K) / (ms * 1e-3) / 1e9
+            out["%s_M%d" % (name, M)] = {
+                "us": round(ms * 1e3, 2), "weight_gbs": round(gbs, 1), "tflops": round(tf, 1),
+                "frac_hbm": round(gbs / PEAK_HBM_GBS, 4),
+                "frac_f16_mfma": round(tf / PEAK_F16_TFLOPS, 4)}
+    return out
+
+
+def binary_and_lm_head(torch, tq, gen, stream):
+    from binary_g128_bit_amd import synth
+    out = {}
+    # 1-bit variant on the MLP shapes: [gate;up] fused and down, rotating >= 1 GiB
+    for name, (N, K) in (("bin_gate_up_34816x5120", (2 * synth.GATE_UP[0], synth.GATE_UP[1])),
+                         ("bin_down_5120x17408", synth.DOWN)):
+        nb = packed_bytes(N, K, 1)
+        copies = max(2, math.ceil((1 << 30) / nb))
+        pool = [(gen.codes(N, K, 1), gen.scales(N, K)) for _ in range(copies)]
+        x = gen.act(1, K)[0]
+        y = torch.empty(N, dtype=torch.float32, device=gen.dev)
+        ms = per_launch_ms(torch, stream, lambda i: tq.tq_gemv(pool[i % copies][0], pool[i % copies][1],
+                                                               x, y, variant=tq.TQ_BINARY), 100)
+        out[name] = {"us": round(ms * 1e3, 2), "gbs": round(nb / ms / 1e6, 1),
+                     "frac_hbm": round(nb / ms / 1e6 / PEAK_HBM_GBS, 4)}
+        del pool
+    # LM head 5120 -> 248320, batch 1 (GEMV) and 8 (GEMM); 3 copies > last-level cache
+    N, K = synth.LM_HEAD
+    nb = packed_bytes(N, K)
+    pool = [(gen.codes(N, K, 0), gen.scales(N, K)) for _ in range(3)]
+    X = gen.act(8, K)
+    Y = torch.empty(8, N, dtype=torch.float32, device=gen.dev)
+    ms1 = per_launch_ms(torch, stream, lambda i: tq.tq_gemv(pool[i % 3][0], pool[i % 3][1], X[0], Y[0]), 30)
+    ms8 = per_launch_ms(torch, stream, lambda i: tq.tq_gemm(pool[i % 3][0], pool[i % 3][1], X, Y), 30)
+    out["lm_head_248320x5120_M1"] = {"us": round(ms1 * 1e3, 2), "gbs": round(nb / ms1 / 1e6, 1),
+                                     "frac_hbm": round(nb / ms1 / 1e6 / PEAK_HBM_GBS, 4)}
+    out["lm_head_248320x5120_M8"] = {"us": round(ms8 * 1e3, 2), "gbs": round(nb / ms8 / 1e6, 1),
+                                     "frac_hbm": round(nb / ms8 / 1e6 / PEAK_HBM_GBS, 4)}
+    return out
+
+
+def copy_calibration():
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": 5}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(got --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    if args.only_step:
+        args.no_cpu = args.no_extras = True
 
     import numpy as np
     import torch
@@ -154,30 +388,24 @@ def main():
     ms_per_step = e0.elapsed_time(e1) / args.steps
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # ---- dominant kernel: the fused 34816x5120 GEMV, timed alone on its stream
-    def kernel_avg_ms(m, launches, views=None):
-        pool = [bufs[r][m] for r in range(slots)] if views is None else views
-        for i in range(20):
-            c, s = pool[i % len(pool)]
-            tq.tq_gemv(c, s, xs[m], ys[m][:s.shape[0]])
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for i in range(launches):
-            c, s = pool[i % len(pool)]
-            tq.tq_gemv(c, s, xs[m], ys[m][:s.shape[0]])
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / launches
-
+    # ---- dominant kernel: the fused 34816x5120 GEMV, each launch timed alone
     launches = max(200, args.steps)
-    gu_ms = kernel_avg_ms(0, launches)
-    down_ms = kernel_avg_ms(1, launches)
+
+    def gemv_launch(m, pool):
+        return lambda i: tq.tq_gemv(pool[i % len(pool)][0], pool[i % len(pool)][1], xs[m],
+                                    ys[m][:pool[0][1].shape[0]])
+
+    gu_pool = [bufs[r][0] for r in range(slots)]
+    gu_ms = per_launch_ms(torch, stream, gemv_launch(0, gu_pool), launches)
+    down_ms = per_launch_ms(torch, stream, gemv_launch(1, [bufs[r][1] for r in range(slots)]), launches)
     # context: gate alone (17408 x 5120, the unfused per-matrix launch)
-    half = [(c[: c.shape[0] // 2], s[: s.shape[0] // 2]) for c, s in (bufs[r][0] for r in range(slots))]
-    gate_ms = kernel_avg_ms(0, launches, half)
+    half = [(c[: c.shape[0] // 2], s[: s.shape[0] // 2]) for c, s in gu_pool]
+    gate_ms = per_launch_ms(torch, stream, gemv_launch(0, half), launches)
+    gu_b2b_ms = back_to_back_ms(torch, stream, gemv_launch(0, gu_pool), launches)
     gu_bytes = packed_bytes(Ng + Nu, Kg)
-    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    # average launch duration: back-to-back launches between two events on the
+    # kernel's stream (per-launch event pairs add the events' own cost)
+    achieved = gu_bytes / (gu_b2b_ms * 1e-3) / 1e9
     src = os.path.join(ROOT, "binary_g128_bit_amd", "csrc", "tq_gemv.hip")
     traffic = read_traffic("gemv_tern_34816x5120", source_hash(src))
 
@@ -204,23 +432,35 @@ def main():
         },
         "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "equiv_tok_s": round(gbs * 1e9 / STACK_BYTES, 1),
-        "per_launch_us": {"gate_up_34816x5120": round(gu_ms * 1e3, 3),
-                          "down_5120x17408": round(down_ms * 1e3, 3),
-                          "gate_17408x5120_unfused": round(gate_ms * 1e3, 3)},
+        "per_launch_us": {"gate_up_34816x5120": round(gu_b2b_ms * 1e3, 3),
+                          "gate_up_34816x5120_event_pairs": round(gu_ms * 1e3, 3),
+                          "down_5120x17408_event_pairs": round(down_ms * 1e3, 3),
+                          "gate_17408x5120_unfused_event_pairs": round(gate_ms * 1e3, 3)},
         "per_launch_gbs": {"gate_up_34816x5120": round(achieved, 1),
-                           "down_5120x17408": round(packed_bytes(Nd, Kd) / down_ms / 1e6, 1),
-                           "gate_17408x5120_unfused": round(packed_bytes(Ng, Kg) / gate_ms / 1e6, 1)},
+                           "down_5120x17408_event_pairs": round(packed_bytes(Nd, Kd) / down_ms / 1e6, 1),
+                           "gate_17408x5120_unfused_event_pairs": round(packed_bytes(Ng, Kg) / gate_ms / 1e6, 1)},
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_kernel<0,8,5,1> on [gate;up] 34816x5120 ternary",
+            "kernel": "gemv_kernel, ternary, on [gate;up] 34816x5120",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
             "traffic": traffic,
+            "algorithmic_bytes_per_launch": gu_bytes,
         },
         "cpu_baseline": None if args.no_cpu else cpu_baseline(host, args.cpu_seconds),
     }
+    if not args.no_extras:
+        gen = Dev(torch, tq, dev, 12345)
+        line["gemm"] = gemm_widths(torch, tq, gen, stream, bufs, slots)
+        line["binary_and_lm_head"] = binary_and_lm_head(torch, tq, gen, stream)
+        del bufs
+        torch.cuda.empty_cache()
+        line["stack_sweep"] = stack_sweep(torch, tq, gen, stream)
+        line["stack_sweep"]["equiv_tok_s_note"] = (
+            "tok_s_graph is the whole stack's GEMVs per second; equiv_tok_s above "
+            "scales the MLP step's GB/s to the stack's bytes")
     print(json.dumps(line), flush=True)
 
 

@@ -271,3 +271,37 @@ def test_gemm_deterministic():
     for _ in range(3):
         Y1 = tq.tq_gemm(cd, sd, Xd, variant=TERN)
         assert torch.equal(Y0, Y1)
+
+
+def test_graph_replay_matches_eager():
+    """GEMV and GEMM launches captured in a HIP graph: every replay, with eager
+    work and synchronisation between replays, gives the eager result's bits."""
+    N, K = 4096, 5120
+    codes, s, X = case(9960, N, K, 16, TERN, exact=False)
+    cd, sd, Xd = up(codes), up(s), up(X)
+    y = torch.empty(N, dtype=torch.float32, device="cuda")
+    Y = torch.empty(16, N, dtype=torch.float32, device="cuda")
+    tq.tq_gemv(cd, sd, Xd[0], y)
+    tq.tq_gemm(cd, sd, Xd, Y)
+    torch.cuda.synchronize()
+    y_ref, Y_ref = y.clone(), Y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        tq.tq_gemv(cd, sd, Xd[0], y)
+        tq.tq_gemm(cd, sd, Xd, Y)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tq.tq_gemv(cd, sd, Xd[0], y)
+        tq.tq_gemm(cd, sd, Xd, Y)
+    for r in range(4):
+        y.fill_(float("nan"))
+        Y.fill_(float("nan"))
+        tq.tq_gemv(cd, sd, Xd[1], torch.empty_like(y))   # unrelated eager work
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), "GEMV replay %d" % r
+        assert torch.equal(Y, Y_ref), "GEMM replay %d" % r
