@@ -262,7 +262,8 @@ def stack_sweep(torch, tq, gen, stream):
 
 def gemm_widths(torch, tq, gen, stream, bufs, slots):
     """Small-batch GEMM (speculative verify / prefill widths) on gate
-    (17408 x 5120, the first half of the fused buffers) and down, rotating."""
+    (17408 x 5120, the first half of the fused buffers) and down, rotating;
+    back-to-back launches between two events."""
     from binary_g128_bit_amd import synth
     out = {}
     for name, m, (N, K) in (("gate_17408x5120", 0, synth.GATE_UP), ("down_5120x17408", 1, synth.DOWN)):
@@ -271,8 +272,8 @@ def gemm_widths(torch, tq, gen, stream, bufs, slots):
         Y = torch.empty(512, N, dtype=torch.float32, device=gen.dev)
         for M in synth.GEMM_WIDTHS:
             Xm, Ym = X[:M], Y[:M]
-            ms = per_launch_ms(torch, stream,
-                               lambda i: tq.tq_gemm(pool[i % len(pool)][0], pool[i % len(pool)][1],
+            ms = back_to_back_ms(torch, stream,
+                                 lambda i: tq.tq_gemm(pool[i % len(pool)][0], pool[i % len(pool)][1],
                                                     Xm, Ym), 50)
             tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
             gbs = packed_bytes(N, K) / (ms * 1e-3) / 1e9
@@ -294,8 +295,8 @@ def binary_and_lm_head(torch, tq, gen, stream):
         pool = [(gen.codes(N, K, 1), gen.scales(N, K)) for _ in range(copies)]
         x = gen.act(1, K)[0]
         y = torch.empty(N, dtype=torch.float32, device=gen.dev)
-        ms = per_launch_ms(torch, stream, lambda i: tq.tq_gemv(pool[i % copies][0], pool[i % copies][1],
-                                                               x, y, variant=tq.TQ_BINARY), 100)
+        ms = back_to_back_ms(torch, stream, lambda i: tq.tq_gemv(pool[i % copies][0], pool[i % copies][1],
+                                                                 x, y, variant=tq.TQ_BINARY), 100)
         out[name] = {"us": round(ms * 1e3, 2), "gbs": round(nb / ms / 1e6, 1),
                      "frac_hbm": round(nb / ms / 1e6 / PEAK_HBM_GBS, 4)}
         del pool
@@ -305,8 +306,8 @@ def binary_and_lm_head(torch, tq, gen, stream):
     pool = [(gen.codes(N, K, 0), gen.scales(N, K)) for _ in range(3)]
     X = gen.act(8, K)
     Y = torch.empty(8, N, dtype=torch.float32, device=gen.dev)
-    ms1 = per_launch_ms(torch, stream, lambda i: tq.tq_gemv(pool[i % 3][0], pool[i % 3][1], X[0], Y[0]), 30)
-    ms8 = per_launch_ms(torch, stream, lambda i: tq.tq_gemm(pool[i % 3][0], pool[i % 3][1], X, Y), 30)
+    ms1 = back_to_back_ms(torch, stream, lambda i: tq.tq_gemv(pool[i % 3][0], pool[i % 3][1], X[0], Y[0]), 30)
+    ms8 = back_to_back_ms(torch, stream, lambda i: tq.tq_gemm(pool[i % 3][0], pool[i % 3][1], X, Y), 30)
     out["lm_head_248320x5120_M1"] = {"us": round(ms1 * 1e3, 2), "gbs": round(nb / ms1 / 1e6, 1),
                                      "frac_hbm": round(nb / ms1 / 1e6 / PEAK_HBM_GBS, 4)}
     out["lm_head_248320x5120_M8"] = {"us": round(ms8 * 1e3, 2), "gbs": round(nb / ms8 / 1e6, 1),
@@ -397,10 +398,10 @@ def main():
 
     gu_pool = [bufs[r][0] for r in range(slots)]
     gu_ms = per_launch_ms(torch, stream, gemv_launch(0, gu_pool), launches)
-    down_ms = per_launch_ms(torch, stream, gemv_launch(1, [bufs[r][1] for r in range(slots)]), launches)
+    down_ms = back_to_back_ms(torch, stream, gemv_launch(1, [bufs[r][1] for r in range(slots)]), launches)
     # context: gate alone (17408 x 5120, the unfused per-matrix launch)
     half = [(c[: c.shape[0] // 2], s[: s.shape[0] // 2]) for c, s in gu_pool]
-    gate_ms = per_launch_ms(torch, stream, gemv_launch(0, half), launches)
+    gate_ms = back_to_back_ms(torch, stream, gemv_launch(0, half), launches)
     gu_b2b_ms = back_to_back_ms(torch, stream, gemv_launch(0, gu_pool), launches)
     gu_bytes = packed_bytes(Ng + Nu, Kg)
     # average launch duration: back-to-back launches between two events on the
@@ -434,11 +435,11 @@ def main():
         "equiv_tok_s": round(gbs * 1e9 / STACK_BYTES, 1),
         "per_launch_us": {"gate_up_34816x5120": round(gu_b2b_ms * 1e3, 3),
                           "gate_up_34816x5120_event_pairs": round(gu_ms * 1e3, 3),
-                          "down_5120x17408_event_pairs": round(down_ms * 1e3, 3),
-                          "gate_17408x5120_unfused_event_pairs": round(gate_ms * 1e3, 3)},
+                          "down_5120x17408": round(down_ms * 1e3, 3),
+                          "gate_17408x5120_unfused": round(gate_ms * 1e3, 3)},
         "per_launch_gbs": {"gate_up_34816x5120": round(achieved, 1),
-                           "down_5120x17408_event_pairs": round(packed_bytes(Nd, Kd) / down_ms / 1e6, 1),
-                           "gate_17408x5120_unfused_event_pairs": round(packed_bytes(Ng, Kg) / gate_ms / 1e6, 1)},
+                           "down_5120x17408": round(packed_bytes(Nd, Kd) / down_ms / 1e6, 1),
+                           "gate_17408x5120_unfused": round(packed_bytes(Ng, Kg) / gate_ms / 1e6, 1)},
         "roofline": {
             "bound": "hbm",
             "kernel": "gemv_kernel, ternary, on [gate;up] 34816x5120",

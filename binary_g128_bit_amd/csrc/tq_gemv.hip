@@ -274,6 +274,17 @@ __device__ __forceinline__ void chunk_dot(const u32x4 (&c)[RPL], const uint32_t 
                                 acc[r]);
 }
 
+// chunk_dot with the chunk's pairs and constant held in registers (ternary,
+// one row): xr[0..32) are the pairs of the chunk's four units, xr[32] the
+// constant.
+__device__ __forceinline__ void chunk_dot_reg(const u32x4 &c, const uint32_t (&xr)[33], uint32_t sbits,
+                                              float &acc, const Masks &km) {
+    float aE = 0.0f, aM = __builtin_bit_cast(float, xr[32]);
+    tern_acc32(c[0], c[1], xr, xr + 8, aE, aM, km);
+    tern_acc32(c[2], c[3], xr + 16, xr + 24, aE, aM, km);
+    acc = __builtin_fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)sbits), aE + aM, acc);
+}
+
 // One row block = RPL * 64/LPR consecutive rows handled by one wave: LPR lanes
 // per row, lane (seg, j) takes rows seg, seg + 64/LPR, ... of the block and in
 // each the 16-byte chunks j, j+LPR, ..., so consecutive lanes read consecutive
@@ -404,6 +415,92 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
     }
 }
 
+// Ternary GEMV, one row per lane, with the lane's activations in registers.
+// Lane j of a row segment only ever reads chunk columns j, j + LPR, ..., so
+// after the workgroup has staged x into LDS once (permuted, with the chunk
+// constants), each lane copies its NU chunk slots into VGPRs and the block
+// loop reads no LDS at all.
+template <int LPR, int NU, int WAVES, bool RAGGED>
+__global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__restrict__ codes,
+                                                               const uint16_t *__restrict__ scales,
+                                                               const uint16_t *__restrict__ x,
+                                                               float *__restrict__ y, int N, int K) {
+    extern __shared__ uint32_t xs[];
+    using XU = XUnit<TQ_TERNARY>;
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int RS = 64 / LPR;  // rows per block (one per lane segment)
+    constexpr int CAP = LPR * NU;
+    constexpr int XMAX = (CAP * 4 + THREADS - 1) / THREADS;
+    const int G = K >> 7, CPR = 2 * G;
+    const int nunits = CPR * 4;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int seg = lane / LPR, j = lane % LPR;
+    const int nblocks = (N + RS - 1) / RS;
+    const int b_begin = (int)(((long long)blockIdx.x * nblocks) / gridDim.x);
+    const int b_end = (int)(((long long)(blockIdx.x + 1) * nblocks) / gridDim.x);
+    const Masks km;
+
+    XU xu[XMAX];
+#pragma unroll
+    for (int k = 0; k < XMAX; ++k)
+        xu[k].load(x, min(min((int)threadIdx.x + k * THREADS, CAP * 4 - 1), nunits - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 ca[NU][1], cb[NU][1];
+    uint32_t sa[NU][1], sb[NU][1];
+    int b = b_begin + wave;
+    int row[1] = {min(min(b, b_end - 1) * RS + seg, N - 1)};
+    load_block<TQ_TERNARY, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, ca, sa);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < XMAX; ++k) {
+        const int u = min((int)threadIdx.x + k * THREADS, CAP * 4 - 1);
+        xu[k].store(xs, u, u < nunits);
+    }
+    __syncthreads();
+    uint32_t xr[NU][33];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        const uint32_t *slot = xs + (j + i * LPR) * XU::CHUNK_DW;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const u32x4 v = reinterpret_cast<const u32x4 *>(slot)[q];
+            xr[i][4 * q] = v[0];
+            xr[i][4 * q + 1] = v[1];
+            xr[i][4 * q + 2] = v[2];
+            xr[i][4 * q + 3] = v[3];
+        }
+        xr[i][32] = slot[32];
+    }
+
+    auto block = [&](const u32x4 (&c)[NU][1], const uint32_t (&sv)[NU][1], int bb)
+                     __attribute__((always_inline)) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            chunk_dot_reg(c[i][0], xr[i], sv[i][0], acc, km);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const float out = seg_sum<LPR>(acc) * XU::kRowScale;
+        const int rr = bb * RS + seg;
+        if (j == 0 && rr < N) y[rr] = out;
+    };
+    for (; b < b_end; b += 2 * WAVES) {
+        const int b2 = b + WAVES;
+        if (b2 < b_end) {
+            row[0] = b2 * RS + seg < N ? b2 * RS + seg : N - 1;
+            load_block<TQ_TERNARY, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, cb, sb);
+        }
+        block(ca, sa, b);
+        if (b2 >= b_end) break;
+        const int b3 = b2 + WAVES;
+        if (b3 < b_end) {
+            row[0] = b3 * RS + seg < N ? b3 * RS + seg : N - 1;
+            load_block<TQ_TERNARY, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, ca, sa);
+        }
+        block(cb, sb, b2);
+    }
+}
+
 struct Config {
     int lpr, nu;
 };
@@ -427,13 +524,14 @@ Config pick(int cpr) {
     return best;
 }
 
-// Rows per lane and waves per workgroup for a shape: two rows per lane halve
-// the LDS reads per weight; the wave count keeps two register sets of codes
-// within the VGPRs a lane may use (512 / waves-per-SIMD).
+// Rows per lane and waves per workgroup.  One row per lane and eight waves
+// (two per SIMD) give each wave several blocks to pipeline; fewer, larger
+// blocks per wave (two rows per lane, twelve waves) leave the first blocks'
+// latency exposed and measured slower on every shape.
 template <int NU>
 struct Tiling {
-    static constexpr int RPL = NU <= 6 ? 2 : 1;
-    static constexpr int WAVES = NU <= 6 ? 12 : (NU <= 8 ? 16 : 8);
+    static constexpr int RPL = 1;
+    static constexpr int WAVES = 8;
 };
 
 template <int VARIANT, int LPR, int NU>
@@ -493,9 +591,71 @@ hipError_t dispatch(const Config &c, const uint8_t *codes, const uint16_t *scale
 
 }  // namespace
 
+namespace {
+
+// Register-resident activations: (LPR, NU) with NU <= kXregMaxNU, the least
+// capacity LPR * NU that covers CPR chunks, ties to fewer chunks per lane;
+// {0, 0} when no shape fits.
+constexpr int kXregMaxNU = 5;
+constexpr int kXregWaves = 8;
+
+Config pick_xreg(int cpr) {
+    Config best{0, 0};
+    for (int lpr : {8, 16, 32, 64})
+        for (int nu = 1; nu <= kXregMaxNU; ++nu) {
+            const int cap = lpr * nu;
+            if (cap < cpr) continue;
+            if (!best.lpr || cap < best.lpr * best.nu || (cap == best.lpr * best.nu && nu < best.nu))
+                best = Config{lpr, nu};
+        }
+    return best;
+}
+
+template <int LPR, int NU>
+hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
+                       int N, int K, hipStream_t stream) {
+    constexpr int RS = 64 / LPR;
+    const int nblocks = (N + RS - 1) / RS;
+    const int grid = max(1, min(device_cus(), (nblocks + kXregWaves - 1) / kXregWaves));
+    constexpr size_t lds = lds_bytes<TQ_TERNARY, LPR, NU>();
+    if ((K / 128) * 2 == LPR * NU)
+        hipLaunchKernelGGL((gemv_xreg_kernel<LPR, NU, kXregWaves, false>), dim3(grid),
+                           dim3(64 * kXregWaves), lds, stream, codes, scales, x, y, N, K);
+    else
+        hipLaunchKernelGGL((gemv_xreg_kernel<LPR, NU, kXregWaves, true>), dim3(grid),
+                           dim3(64 * kXregWaves), lds, stream, codes, scales, x, y, N, K);
+    return hipGetLastError();
+}
+
+hipError_t dispatch_xreg(const Config &c, const uint8_t *codes, const uint16_t *scales,
+                         const uint16_t *x, float *y, int N, int K, hipStream_t s) {
+#define TQ_XCASE(L)                                                                  \
+    if (c.lpr == L) switch (c.nu) {                                                  \
+        case 1: return launch_xreg<L, 1>(codes, scales, x, y, N, K, s);              \
+        case 2: return launch_xreg<L, 2>(codes, scales, x, y, N, K, s);              \
+        case 3: return launch_xreg<L, 3>(codes, scales, x, y, N, K, s);              \
+        case 4: return launch_xreg<L, 4>(codes, scales, x, y, N, K, s);              \
+        case 5: return launch_xreg<L, 5>(codes, scales, x, y, N, K, s);              \
+    }
+    TQ_XCASE(8) TQ_XCASE(16) TQ_XCASE(32) TQ_XCASE(64)
+#undef TQ_XCASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
 int32_t gemv_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
                      int64_t N, int64_t K, int32_t variant, hipStream_t stream) {
     const int cpr = (int)(K / 128) * (variant == TQ_TERNARY ? 2 : 1);
+    if (variant == TQ_TERNARY) {
+        const Config xc = pick_xreg(cpr);
+        if (xc.lpr) {
+            const hipError_t e = dispatch_xreg(xc, codes, scales, x, y, (int)N, (int)K, stream);
+            if (e != hipSuccess)
+                return fail(TQ_ERR_HIP, "GEMV launch failed: %s", hipGetErrorString(e));
+            return TQ_OK;
+        }
+    }
     const Config c = pick(cpr);
     if (!c.lpr)
         return fail(TQ_ERR_SHAPE, "K=%lld is above the GEMV limit", (long long)K);
