@@ -40,9 +40,14 @@
 // with 16-byte loads, eight lanes per 128-byte row segment (4 ternary or 8
 // binary groups), written to the wave's LDS tile and read back in the MFMA
 // layout: loading that layout directly reads 32 bytes per row per instruction,
-// which streams from HBM at well under half the rate.  Activations (small,
-// L2-resident) are loaded straight into registers one group ahead.
+// which streams from HBM at well under half the rate.  Two kernels share this
+// structure: gemm_kernel loads each group's activations (small, L2-resident)
+// straight into registers one group ahead and holds up to 64 activation rows
+// per wave; gemm_stage_kernel (M <= 4) issues all loads of a stage in one
+// batch and stages the activations in LDS (see its comment).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "tq_internal.h"
 
@@ -338,6 +343,232 @@ __global__ __launch_bounds__(64 * KW) void gemm_kernel(const uint8_t *__restrict
     }
 }
 
+// Stage-pipelined variant for up to 16 activation rows.  A stage is SG groups
+// of K: the codes of the wave's 16*NT weight rows (128- or 64-byte row
+// segments), the activations of MR rows over the same groups and their
+// scales.  Loads are issued in a fixed order, one batch per stage: the next
+// stage's activations, then the codes and scales PC stages ahead (a ring of
+// PC register sets).  Loads complete in order, so waiting for a stage's
+// activations only forces code batches issued at least two stages earlier,
+// and every wave keeps about PC stages of codes in flight.  At the start of
+// a stage the wave writes its codes (transposed) and activations (permuted
+// into MFMA A-operand order) into its own LDS area and computes the stage
+// from there.  MR = 4 stages four activation rows (M <= 4): lanes of rows
+// 4..15 read row 3, whose duplicate outputs are never stored.
+template <int VARIANT, int MR>
+struct StageFmt {
+    using F = Fmt<VARIANT>;
+    // 128-byte code rows per stage where the activation tile stays small
+    static constexpr int SG = (VARIANT == TQ_BINARY && MR <= 4) ? 8 : 4;
+    static constexpr int ROW_BYTES = SG * F::kGroupBytes;      // 128 or 64
+    static constexpr int LPRW = ROW_BYTES / 16;                // lanes per code row
+    static constexpr int XITEMS = MR * SG * 4;                 // 32-activation items per stage
+    static constexpr int XPL = (XITEMS + 63) / 64;             // items per lane
+    static constexpr int XBYTES = SG * 16 * MR * 16;           // LDS activation tile
+};
+
+template <int VARIANT, int NT, int MR, int KW>
+constexpr size_t stage_lds_bytes() {
+    using SF = StageFmt<VARIANT, MR>;
+    constexpr size_t per_wave = (size_t)16 * NT * kPitch + SF::XBYTES;
+    constexpr size_t red = (size_t)KW * NT * 256 * sizeof(float);
+    return KW * per_wave > red ? KW * per_wave : red;
+}
+
+template <int VARIANT, int NT, int MR, int KW, int PC>
+__global__ __launch_bounds__(64 * KW) void gemm_stage_kernel(const uint8_t *__restrict__ codes,
+                                                             const uint16_t *__restrict__ scales,
+                                                             const uint16_t *__restrict__ X,
+                                                             float *__restrict__ Y, int M, int N,
+                                                             int K) {
+    using F = Fmt<VARIANT>;
+    using SF = StageFmt<VARIANT, MR>;
+    constexpr int SG = SF::SG, GB = F::kGroupBytes, SPL = SG / 4;
+    constexpr int ROWS = 16 * NT, RPI = 64 / SF::LPRW, LOADS = ROWS / RPI;
+    constexpr int PER_WAVE = ROWS * kPitch + SF::XBYTES;
+    __shared__ __attribute__((aligned(16))) uint8_t smem[stage_lds_bytes<VARIANT, NT, MR, KW>()];
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l16 = lane & 15, q = lane >> 4;
+    const int G = K >> 7;
+    const size_t RB = (size_t)G * GB;
+    const int n0 = blockIdx.x * ROWS, m0 = blockIdx.y * 16;
+    const int g_begin = (int)((int64_t)wave * G / KW), g_end = (int)((int64_t)(wave + 1) * G / KW);
+    uint8_t *lds_c = smem + wave * PER_WAVE;
+    u32x4 *lds_x = reinterpret_cast<u32x4 *>(lds_c + ROWS * kPitch);
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+    if (g_begin < g_end) {
+        const Decoder<VARIANT> dec;
+        const half8 cb[4] = {as_half8(F::corr(0), F::corr(1), F::corr(2), F::corr(3)),
+                             as_half8(F::corr(4), F::corr(5), F::corr(6), F::corr(7)),
+                             as_half8(F::corr(8), F::corr(9), F::corr(10), F::corr(11)),
+                             as_half8(F::corr(12), F::corr(13), F::corr(14), F::corr(15))};
+        const uint8_t *cp[LOADS];
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i)
+            cp[i] = codes + (size_t)min(n0 + RPI * i + lane / SF::LPRW, N - 1) * RB;
+        const int col = 16 * (lane % SF::LPRW);
+        const uint16_t *sp[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sp[t] = scales + (size_t)min(n0 + 16 * t + l16, N - 1) * G;
+        // activation items of this lane: item = lane + 64 k -> (row, group, quarter)
+        const uint16_t *xrow[SF::XPL];
+        int xg[SF::XPL], xq[SF::XPL], xm[SF::XPL];
+#pragma unroll
+        for (int k = 0; k < SF::XPL; ++k) {
+            const int it = min(lane + 64 * k, SF::XITEMS - 1);
+            xq[k] = it & 3;
+            xg[k] = (it >> 2) % SG;
+            xm[k] = it / (4 * SG);
+            xrow[k] = X + (size_t)min(m0 + xm[k], M - 1) * K + 32 * xq[k];
+        }
+        const int last = g_begin + (g_end - 1 - g_begin) / SG * SG;
+        // lane (row l16, quarter q) reads activation row min(l16, MR - 1)
+        const int xr_m = min(l16, MR - 1);
+
+        u32x4 cr[PC][LOADS];
+        float sc[PC][NT][SPL];
+        u32x4 xv[SF::XPL][4];
+        // codes and scales of the stage starting at group gs into ring set p
+        auto load_codes = [&](int p, int gs) __attribute__((always_inline)) {
+            gs = min(gs, last);
+            const int c = min(col, min(SG, g_end - gs) * GB - 16);
+#pragma unroll
+            for (int i = 0; i < LOADS; ++i)
+                cr[p][i] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4 *>(cp[i] + (size_t)gs * GB + c));
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+                for (int k = 0; k < SPL; ++k)
+                    sc[p][t][k] =
+                        (float)__builtin_bit_cast(_Float16, sp[t][min(gs + q + 4 * k, g_end - 1)]);
+        };
+        auto load_x = [&](int gs) __attribute__((always_inline)) {
+            gs = min(gs, last);
+#pragma unroll
+            for (int k = 0; k < SF::XPL; ++k) {
+                const uint16_t *src = xrow[k] + (size_t)min(gs + xg[k], g_end - 1) * 128;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) xv[k][v] = *reinterpret_cast<const u32x4 *>(src + 8 * v);
+            }
+        };
+        // a full stage is computed without branches so that the independent
+        // MFMA chains of its groups and tiles can be interleaved
+        auto compute = [&](auto full, const float (&scur)[NT][SPL], int gs) __attribute__((always_inline)) {
+            const int ng = min(SG, g_end - gs);
+#pragma unroll
+            for (int gl = 0; gl < SG; ++gl) {
+                if (decltype(full)::value || gl < ng) {
+                    u32x4 xa4[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) xa4[j] = lds_x[((gl * 4 + j) * 4 + q) * MR + xr_m];
+                    f32x4 cor = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        cor = mfma(as_half8(xa4[j][0], xa4[j][1], xa4[j][2], xa4[j][3]), cb[j], cor);
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const uint8_t *row = lds_c + (16 * t + l16) * kPitch + gl * GB;
+                        uint32_t d[2];
+                        if (VARIANT == TQ_TERNARY) {
+                            const u32x2 v = *reinterpret_cast<const u32x2 *>(row + 8 * q);
+                            d[0] = v.x;
+                            d[1] = v.y;
+                        } else {
+                            d[0] = *reinterpret_cast<const uint32_t *>(row + 4 * q);
+                            d[1] = 0;
+                        }
+                        uint32_t w[16];
+                        dec(d, w);
+                        const float s = __shfl(scur[t][gl / 4], l16 + 16 * (gl % 4));
+                        f32x4 D = cor;
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            D = mfma(as_half8(xa4[j][0], xa4[j][1], xa4[j][2], xa4[j][3]),
+                                     as_half8(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]), D);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(s, D[i], acc[t][i]);
+                    }
+                }
+            }
+        };
+
+        // prologue: codes of stage 0, activations of stage 0, codes of stages 1..PC-1
+        load_codes(0, g_begin);
+        load_x(g_begin);
+#pragma unroll
+        for (int p = 1; p < PC; ++p) load_codes(p, g_begin + p * SG);
+        for (int gs = g_begin;;) {
+#pragma unroll
+            for (int p = 0; p < PC; ++p) {
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i)
+                    *reinterpret_cast<u32x4 *>(lds_c + (RPI * i + lane / SF::LPRW) * kPitch + col) =
+                        cr[p][i];
+#pragma unroll
+                for (int k = 0; k < SF::XPL; ++k) {
+                    if (SF::XITEMS % 64 != 0 && lane + 64 * k >= SF::XITEMS) continue;
+                    uint32_t xa[16];
+                    permute_x<VARIANT>(xv[k], xa);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        lds_x[((xg[k] * 4 + j) * 4 + xq[k]) * MR + xm[k]] =
+                            (u32x4){xa[4 * j], xa[4 * j + 1], xa[4 * j + 2], xa[4 * j + 3]};
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                // this stage's scales leave ring set p before it is refilled
+                float scur[NT][SPL];
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int k = 0; k < SPL; ++k) scur[t][k] = sc[p][t][k];
+                load_x(gs + SG);
+                load_codes(p, gs + PC * SG);
+                if (gs + SG <= g_end)
+                    compute(std::true_type{}, scur, gs);
+                else
+                    compute(std::false_type{}, scur, gs);
+                if (gs >= last) goto done;
+                gs += SG;
+            }
+        }
+    done:;
+    }
+
+    __syncthreads();
+    float *red = reinterpret_cast<float *>(smem);
+    constexpr int E = NT * 256;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) red[wave * E + (t * 4 + i) * 64 + lane] = acc[t][i];
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 64 * KW) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < KW; ++w) s += red[w * E + e];
+        const int le = e & 63, i = (e >> 6) & 3, t = e >> 8;
+        const int m = m0 + 4 * (le >> 4) + i;
+        const int n = n0 + 16 * t + (le & 15);
+        if (m < M && n < N) Y[(size_t)m * N + n] = s * 16384.0f;
+    }
+}
+
+template <int VARIANT, int NT, int MR, int KW, int PC>
+hipError_t launch_stage(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
+                        int M, int N, int K, hipStream_t stream) {
+    const dim3 grid((N + 16 * NT - 1) / (16 * NT), (M + 15) / 16);
+    hipLaunchKernelGGL((gemm_stage_kernel<VARIANT, NT, MR, KW, PC>), grid, dim3(64 * KW), 0, stream,
+                       codes, scales, X, Y, M, N, K);
+    return hipGetLastError();
+}
+
 template <int VARIANT, int NT, int MT, int KW>
 hipError_t launch(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y, int M,
                   int N, int K, hipStream_t stream) {
@@ -347,12 +578,22 @@ hipError_t launch(const uint8_t *codes, const uint16_t *scales, const uint16_t *
     return hipGetLastError();
 }
 
+// Configurations measured on the MLP shapes (17408 x 5120 and 5120 x 17408):
+// M <= 4 takes the stage-pipelined kernel with four staged activation rows;
+// wider batches take the per-group kernel, with taller weight tiles and a
+// two-way K split when N leaves enough workgroups (N >= 8192), else shorter
+// tiles and a four-way split.
 template <int VARIANT>
 hipError_t dispatch(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
                     int M, int N, int K, hipStream_t s) {
-    if (M <= 16) return launch<VARIANT, 4, 1, 4>(codes, scales, X, Y, M, N, K, s);
+    const bool tall = N >= 8192;
+    if (M <= 4) return launch_stage<VARIANT, 2, 4, 4, 1>(codes, scales, X, Y, M, N, K, s);
+    if (M <= 16)
+        return tall ? launch<VARIANT, 4, 1, 2>(codes, scales, X, Y, M, N, K, s)
+                    : launch<VARIANT, 2, 1, 4>(codes, scales, X, Y, M, N, K, s);
     if (M <= 32) return launch<VARIANT, 4, 2, 4>(codes, scales, X, Y, M, N, K, s);
-    return launch<VARIANT, 4, 4, 4>(codes, scales, X, Y, M, N, K, s);
+    return tall ? launch<VARIANT, 4, 4, 2>(codes, scales, X, Y, M, N, K, s)
+                : launch<VARIANT, 4, 2, 4>(codes, scales, X, Y, M, N, K, s);
 }
 
 }  // namespace
