@@ -220,7 +220,9 @@ def test_lm_head_sampled(M):
 
 @pytest.mark.parametrize("variant", [TERN, BIN])
 @pytest.mark.parametrize("M,N,K", [(3, 1, 128), (17, 70, 128), (31, 129, 256), (33, 64, 640),
-                                   (100, 200, 2176), (5, 1000, 29952), (2, 77, 65536)])
+                                   (100, 200, 2176), (5, 1000, 29952), (2, 77, 65536),
+                                   (128, 128, 128), (130, 70, 384), (257, 300, 1024),
+                                   (200, 129, 5120)])
 def test_gemm_ragged(M, N, K, variant):
     """Ragged activation and weight tiles, K of one group (most waves of a
     workgroup idle) and the largest K."""
