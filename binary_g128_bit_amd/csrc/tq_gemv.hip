@@ -8,25 +8,25 @@
 //
 // Decode.  v_dot2_f32_f16 is accurate to a few ulp of its largest operand
 // when fed normal FP16 values, so every code is turned into a normal FP16
-// whose value is linear in the code, without a per-weight normalising op:
-//   E: a 2-bit code moved to bits [10,12) of a half (the exponent LSBs, the
-//      rest zero) is the FP16 c * 2^-14, exactly (0 for c = 0);
-//   M: a code moved to bits [8,10) under an exponent field of 1 is the FP16
-//      2^-14 * (1 + c/4): an offset only four times the code's unit.
-// One shifted copy of a code dword serves one E pair and one M pair (slot p
-// in the low half, slot p + 8 in the high half); a 64-bit shift moves two
-// code dwords at once (the bits it carries across the dword boundary land
-// where no mask looks).  The activations of E slots are staged pre-scaled by
-// 1/4, so both kinds of products come out in units of 2^-16 and accumulate
-// together; per 16-byte chunk the offsets of the M slots and sum x (t = c - 1)
-// are removed by seeding the accumulator with -(sum x + 4 S_M) * 2^-16, a
-// constant computed while x is staged (S_M sums x over the M slots), and the
-// row total is scaled by 2^16 once.  Rounding stays proportional to the terms
-// summed: the largest offset is 4x the code unit, so a row of zero trits
-// leaves only a residue of order 2^-22 * sum |s * x|.  The 1-bit variant uses
-// the same E slot (bit 10) and two M slots (bits 9 and 8, activations
-// pre-scaled by 1/4 and 1/2), seeds with -(sum x + 4 S_9 + 8 S_8) * 2^-17 and
-// scales by 2^17, which forms 2 * sum b*x - sum x = sum t*x.
+// whose value is linear in the code, without a per-weight normalising op.
+// Ternary uses three slot kinds, all in units of 2^-14:
+//   E:   a 2-bit code moved to bits [10,12) of a half (the exponent LSBs, the
+//        rest zero) is the FP16 c * 2^-14, exactly (0 for c = 0);
+//   M4:  a code at bits [8,10) under exponent field 3 is 2^-12 + c * 2^-14;
+//   M16: a code at bits [6,8) under exponent field 5 is 2^-10 + c * 2^-14.
+// One copy of a code dword serves an E, an M4 and an M16 pair (slot p in the
+// low half, p + 8 in the high half): d gives slots 5, 4, 3, d << 6 gives
+// 2, 1, 0 and d >> 4 gives 7, 6, so two shifts and one mask op per pair
+// decode 16 weights.  Per 16-byte chunk the slot offsets (4 and 16 units) and
+// sum x (t = c - 1) are removed by seeding the chunk's accumulator with
+// -(sum x + 4 S_M4 + 16 S_M16) * 2^-14, a constant computed while x is staged
+// (S_M4 and S_M16 sum x over those slots), and the row total is scaled by
+// 2^14 once.  Rounding stays proportional to the terms summed (the largest
+// offset is 16 code units), so a row of zero trits leaves only a small
+// residue of order 2^-20 * sum |s * x|.  The 1-bit variant uses an E slot at
+// bit 10 and two M slots (bits 9 and 8, activations pre-scaled by 1/4 and
+// 1/2), seeds with -(sum x + 4 S_9 + 8 S_8) * 2^-17 and scales by 2^17, which
+// forms 2 * sum b*x - sum x = sum t*x.
 //
 // Work split.  A wave owns 64/LPR row slots of LPR lanes each; lane j of a
 // slot takes groups j, j+LPR, j+2*LPR, ... of its RPL rows.  Each lane first
@@ -55,9 +55,11 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // Masks used with v_and_or_b32 stay in VGPRs: gfx9 VOP3 encodings take no
 // literal and read one SGPR at most, which then holds the exponent constant.
 struct Masks {
-    uint32_t m8, m9, b8;
-    __device__ __forceinline__ Masks() : m8(0x03000300u), m9(0x02000200u), b8(0x01000100u) {
+    uint32_t m8, m6, m9, b8;
+    __device__ __forceinline__ Masks()
+        : m8(0x03000300u), m6(0x00C000C0u), m9(0x02000200u), b8(0x01000100u) {
         asm volatile("" : "+v"(m8));
+        asm volatile("" : "+v"(m6));
         asm volatile("" : "+v"(m9));
         asm volatile("" : "+v"(b8));
     }
@@ -68,26 +70,23 @@ constexpr uint32_t kExp1 = 0x04000400u;  // exponent field 1 in both halves
 typedef uint64_t u64;
 
 // 32 ternary codes (dwords d0, d1) against pairs xp[p] = (x[p], x[p+8]) of
-// each dword's 16 weights (E pairs pre-scaled by 1/4).  aE takes slots
-// 1, 3, 5, 7 (E), aM slots 0, 2, 4, 6 (M), both in units of 2^-16.
+// each dword's 16 weights, accumulated into a in units of 2^-14.
 __device__ __forceinline__ void tern_acc32(uint32_t d0, uint32_t d1, const uint32_t *xp0,
-                                           const uint32_t *xp1, float &aE, float &aM,
-                                           const Masks &k) {
-    const u64 dd = ((u64)d1 << 32) | d0;
-    const u64 l4 = dd << 4, l8 = dd << 8, r4 = dd >> 4;
-    const uint32_t c0[4] = {d0, (uint32_t)l4, (uint32_t)l8, (uint32_t)r4};
-    const uint32_t c1[4] = {d1, (uint32_t)(l4 >> 32), (uint32_t)(l8 >> 32), (uint32_t)(r4 >> 32)};
-    // copy q brings E slot pe[q] and M slot pm[q] to bits [10,12) / [8,10)
-    constexpr int pe[4] = {5, 3, 1, 7}, pm[4] = {4, 2, 0, 6};
+                                           const uint32_t *xp1, float &a, const Masks &k) {
+    const uint32_t dd[2] = {d0, d1};
+    const uint32_t *xps[2] = {xp0, xp1};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        aE = dot2(c0[q] & 0x0C000C00u, xp0[pe[q]], aE);
-        aM = dot2((c0[q] & k.m8) | kExp1, xp0[pm[q]], aM);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        aE = dot2(c1[q] & 0x0C000C00u, xp1[pe[q]], aE);
-        aM = dot2((c1[q] & k.m8) | kExp1, xp1[pm[q]], aM);
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t *xp = xps[h];
+        const uint32_t c0 = dd[h], c6 = dd[h] << 6, r4 = dd[h] >> 4;
+        a = dot2(c0 & 0x0C000C00u, xp[5], a);              // E   slot 5
+        a = dot2((c0 & k.m8) | 0x0C000C00u, xp[4], a);     // M4  slot 4
+        a = dot2((c0 & k.m6) | 0x14001400u, xp[3], a);     // M16 slot 3
+        a = dot2(c6 & 0x0C000C00u, xp[2], a);              // E   slot 2
+        a = dot2((c6 & k.m8) | 0x0C000C00u, xp[1], a);     // M4  slot 1
+        a = dot2((c6 & k.m6) | 0x14001400u, xp[0], a);     // M16 slot 0
+        a = dot2(r4 & 0x0C000C00u, xp[7], a);              // E   slot 7
+        a = dot2((r4 & k.m8) | 0x0C000C00u, xp[6], a);     // M4  slot 6
     }
 }
 
@@ -164,23 +163,24 @@ struct XUnit {
     // FP16 pair (w, w) weighting pair p in the chunk constant
     static __device__ __forceinline__ uint32_t zweight(int p) {
         if constexpr (VARIANT == TQ_TERNARY) {
-            return (p & 1) ? 0x3C003C00u : 0x45004500u;  // 1 : 5
+            // E slots 2, 5, 7; M4 slots 1, 4, 6; M16 slots 0, 3
+            return (p == 0 || p == 3) ? 0x4C404C40u : (p == 1 || p == 4 || p == 6) ? 0x45004500u
+                                                                                    : 0x3C003C00u;  // 17 : 5 : 1
         } else {
             // E slots 1, 4, 7, 10, 13; bit-9 slots 0, 3, 6, 9, 12, 15; bit-8 slots 2, 5, 8, 11, 14
             return (p % 3 == 1) ? 0x3C003C00u : (p % 3 == 0) ? 0x45004500u : 0x48804880u;  // 1 : 5 : 9
         }
     }
 
-    // accumulator units: 2^-16 (ternary) or 2^-17 (binary, which also folds the 2 of 2b - 1)
-    static constexpr float kSeedScale = VARIANT == TQ_TERNARY ? 1.52587890625e-05f : 7.62939453125e-06f;
-    static constexpr float kRowScale = VARIANT == TQ_TERNARY ? 65536.0f : 131072.0f;
+    // accumulator units: 2^-14 (ternary) or 2^-17 (binary, which also folds the 2 of 2b - 1)
+    static constexpr float kSeedScale = VARIANT == TQ_TERNARY ? 6.103515625e-05f : 7.62939453125e-06f;
+    static constexpr float kRowScale = VARIANT == TQ_TERNARY ? 16384.0f : 131072.0f;
 
-    // pair p as staged: E slots times 1/4, binary bit-9 slots times 1/2
+    // pair p as staged: ternary as is; binary E slots times 1/4, bit-9 slots times 1/2
     static __device__ __forceinline__ uint32_t prescale(int p, uint32_t v) {
         bool e, h;
         if constexpr (VARIANT == TQ_TERNARY) {
-            e = p & 1;
-            h = false;
+            return v;
         } else {
             e = p % 3 == 1;
             h = p % 3 == 0;
@@ -209,11 +209,12 @@ struct XUnit {
             xp[2 * i + 1] = real ? (l >> 16) | (h & 0xFFFF0000u) : 0u;
         }
         // seed: -(sum over the pairs of w_p * (x[p] + x[p+UNIT/2])) * 2^-F with
-        // w = 1 for E slots, 1 + 4 (ternary M, binary bit 9), 1 + 8 (binary bit 8)
+        // w = 1 for E slots, 1 + 4 (ternary M4, binary bit 9), 1 + 16 (ternary
+        // M16), 1 + 8 (binary bit 8)
         float z = 0.0f;
 #pragma unroll
         for (int i = 0; i < UNIT / 2; ++i) z = dot2(xp[i], zweight(i), z);
-        // E slots (and binary bit-9 slots) are stored pre-scaled to unit 2^-16
+        // binary E and bit-9 slots are stored pre-scaled to the unit 2^-17
 #pragma unroll
         for (int i = 0; i < UNIT / 2; ++i) xp[i] = prescale(i, xp[i]);
         uint32_t *slot = xs + (u >> 2) * CHUNK_DW;
@@ -251,7 +252,7 @@ __device__ __forceinline__ void chunk_dot(const u32x4 (&c)[RPL], const uint32_t 
             const uint32_t xp0[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
             const uint32_t xp1[8] = {q2[0], q2[1], q2[2], q2[3], q3[0], q3[1], q3[2], q3[3]};
 #pragma unroll
-            for (int r = 0; r < RPL; ++r) tern_acc32(c[r][d], c[r][d + 1], xp0, xp1, aE[r], aM[r], km);
+            for (int r = 0; r < RPL; ++r) tern_acc32(c[r][d], c[r][d + 1], xp0, xp1, aM[r], km);
         } else {
             uint32_t xp0[16], xp1[16];
 #pragma unroll
@@ -279,10 +280,10 @@ __device__ __forceinline__ void chunk_dot(const u32x4 (&c)[RPL], const uint32_t 
 // constant.
 __device__ __forceinline__ void chunk_dot_reg(const u32x4 &c, const uint32_t (&xr)[33], uint32_t sbits,
                                               float &acc, const Masks &km) {
-    float aE = 0.0f, aM = __builtin_bit_cast(float, xr[32]);
-    tern_acc32(c[0], c[1], xr, xr + 8, aE, aM, km);
-    tern_acc32(c[2], c[3], xr + 16, xr + 24, aE, aM, km);
-    acc = __builtin_fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)sbits), aE + aM, acc);
+    float a = __builtin_bit_cast(float, xr[32]);
+    tern_acc32(c[0], c[1], xr, xr + 8, a, km);
+    tern_acc32(c[2], c[3], xr + 16, xr + 24, a, km);
+    acc = __builtin_fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)sbits), a, acc);
 }
 
 // One row block = RPL * 64/LPR consecutive rows handled by one wave: LPR lanes
