@@ -23,10 +23,12 @@
 // (S_M4 and S_M16 sum x over those slots), and the row total is scaled by
 // 2^14 once.  Rounding stays proportional to the terms summed (the largest
 // offset is 16 code units), so a row of zero trits leaves only a small
-// residue of order 2^-20 * sum |s * x|.  The 1-bit variant uses an E slot at
-// bit 10 and two M slots (bits 9 and 8, activations pre-scaled by 1/4 and
-// 1/2), seeds with -(sum x + 4 S_9 + 8 S_8) * 2^-17 and scales by 2^17, which
-// forms 2 * sum b*x - sum x = sum t*x.
+// residue of order 2^-20 * sum |s * x|.  The 1-bit variant reads bit b at
+// position 11 as b * 2^-13 and at position q <= 10 under exponent field
+// 12 - q as 2^(-3-q) + b * 2^-13 (offsets 1 .. 16 units of 2^-13); copies d,
+// d << 6 and d >> 4 cover a dword's 16 pairs through bits 11..6, and the seed
+// -(sum over pairs of (2 offset + 1) x) * 2^-14 leaves 2^-14 (2 sum b*x -
+// sum x) = 2^-14 sum t*x.
 //
 // Work split.  A wave owns 64/LPR row slots of LPR lanes each; lane j of a
 // slot takes groups j, j+LPR, j+2*LPR, ... of its RPL rows.  Each lane first
@@ -55,13 +57,17 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // Masks used with v_and_or_b32 stay in VGPRs: gfx9 VOP3 encodings take no
 // literal and read one SGPR at most, which then holds the exponent constant.
 struct Masks {
-    uint32_t m8, m6, m9, b8;
+    uint32_t m8, m6, b10, b9, b8, b7, b6;
     __device__ __forceinline__ Masks()
-        : m8(0x03000300u), m6(0x00C000C0u), m9(0x02000200u), b8(0x01000100u) {
+        : m8(0x03000300u), m6(0x00C000C0u), b10(0x04000400u), b9(0x02000200u), b8(0x01000100u),
+          b7(0x00800080u), b6(0x00400040u) {
         asm volatile("" : "+v"(m8));
         asm volatile("" : "+v"(m6));
-        asm volatile("" : "+v"(m9));
+        asm volatile("" : "+v"(b10));
+        asm volatile("" : "+v"(b9));
         asm volatile("" : "+v"(b8));
+        asm volatile("" : "+v"(b7));
+        asm volatile("" : "+v"(b6));
     }
 };
 
@@ -91,39 +97,29 @@ __device__ __forceinline__ void tern_acc32(uint32_t d0, uint32_t d1, const uint3
 }
 
 // 64 binary bits (dwords d0, d1) against pairs xp[p] = (x[p], x[p+16]) of
-// each dword's 32 weights.  aE: bit at 10, b * 2^-14 (x pre-scaled by 1/4);
-// a9: bit at 9, 2^-14 (1 + b/2) (x by 1/2); a8: bit at 8, 2^-14 (1 + b/4).
-// Copies d << s for s in {0, 3, 6, 9, -3, -6} bring bits 10-s, 9-s, 8-s there.
-__device__ __forceinline__ void bin_acc64(uint32_t d0, uint32_t d1, const uint32_t *xp0,
-                                          const uint32_t *xp1, float &aE, float &aM,
+// each dword's 32 weights, accumulated into a: bit b at position 11 is
+// b * 2^-13 and at position q <= 10 under exponent field 12 - q it is
+// 2^(-3-q) + b * 2^-13.  Copy d reads bits 11..6 (slots 11..6), d << 6 reads
+// bits 5..0 and d >> 4 bits 15..12, each through slots 11.. downwards.
+__device__ __forceinline__ void bin_slots(uint32_t c, const uint32_t *xp, int p0, int n, float &a,
                                           const Masks &k) {
-    const u64 dd = ((u64)d1 << 32) | d0;
-    const u64 sh[5] = {dd << 3, dd << 6, dd << 9, dd >> 3, dd >> 6};
+    a = dot2(c & 0x08000800u, xp[p0], a);                          // bit 11
+    a = dot2((c & k.b10) | 0x08000800u, xp[p0 - 1], a);            // bit 10, offset 1
+    a = dot2((c & k.b9) | 0x0C000C00u, xp[p0 - 2], a);             // bit 9,  offset 2
+    a = dot2((c & k.b8) | 0x10001000u, xp[p0 - 3], a);             // bit 8,  offset 4
+    if (n > 4) a = dot2((c & k.b7) | 0x14001400u, xp[p0 - 4], a);  // bit 7,  offset 8
+    if (n > 5) a = dot2((c & k.b6) | 0x18001800u, xp[p0 - 5], a);  // bit 6,  offset 16
+}
+
+__device__ __forceinline__ void bin_acc64(uint32_t d0, uint32_t d1, const uint32_t *xp0,
+                                          const uint32_t *xp1, float &a, const Masks &k) {
+    const uint32_t dd[2] = {d0, d1};
     const uint32_t *xps[2] = {xp0, xp1};
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const uint32_t *xp = xps[h];
-        const uint32_t c0 = h ? d1 : d0;
-        uint32_t c[5];
-#pragma unroll
-        for (int i = 0; i < 5; ++i) c[i] = h ? (uint32_t)(sh[i] >> 32) : (uint32_t)sh[i];
-        const uint32_t c3 = c[0], c6 = c[1], c9 = c[2], r3 = c[3], r6 = c[4];
-        aE = dot2(c0 & 0x04000400u, xp[10], aE);
-        aM = dot2((c0 & k.m9) | kExp1, xp[9], aM);
-        aE = dot2((c0 & k.b8) | kExp1, xp[8], aE);
-        aM = dot2(c3 & 0x04000400u, xp[7], aM);
-        aE = dot2((c3 & k.m9) | kExp1, xp[6], aE);
-        aM = dot2((c3 & k.b8) | kExp1, xp[5], aM);
-        aE = dot2(c6 & 0x04000400u, xp[4], aE);
-        aM = dot2((c6 & k.m9) | kExp1, xp[3], aM);
-        aE = dot2((c6 & k.b8) | kExp1, xp[2], aE);
-        aM = dot2(c9 & 0x04000400u, xp[1], aM);
-        aE = dot2((c9 & k.m9) | kExp1, xp[0], aE);
-        aM = dot2(r3 & 0x04000400u, xp[13], aM);
-        aE = dot2((r3 & k.m9) | kExp1, xp[12], aE);
-        aM = dot2((r3 & k.b8) | kExp1, xp[11], aM);
-        aE = dot2((r6 & k.m9) | kExp1, xp[15], aE);
-        aM = dot2((r6 & k.b8) | kExp1, xp[14], aM);
+        bin_slots(dd[h], xps[h], 11, 6, a, k);
+        bin_slots(dd[h] << 6, xps[h], 5, 6, a, k);
+        bin_slots(dd[h] >> 4, xps[h], 15, 4, a, k);
     }
 }
 
@@ -167,28 +163,20 @@ struct XUnit {
             return (p == 0 || p == 3) ? 0x4C404C40u : (p == 1 || p == 4 || p == 6) ? 0x45004500u
                                                                                     : 0x3C003C00u;  // 17 : 5 : 1
         } else {
-            // E slots 1, 4, 7, 10, 13; bit-9 slots 0, 3, 6, 9, 12, 15; bit-8 slots 2, 5, 8, 11, 14
-            return (p % 3 == 1) ? 0x3C003C00u : (p % 3 == 0) ? 0x45004500u : 0x48804880u;  // 1 : 5 : 9
+            // pair p is read by the slot at bit 11 - (p + 4) % 6 for p <= 11 (copies d
+            // and d << 6) or 11 - (15 - p) for p >= 12 (copy d >> 4); weight 2 off + 1
+            constexpr uint32_t w[16] = {0x50205020u, 0x4C404C40u, 0x48804880u, 0x45004500u,
+                                        0x42004200u, 0x3C003C00u, 0x50205020u, 0x4C404C40u,
+                                        0x48804880u, 0x45004500u, 0x42004200u, 0x3C003C00u,
+                                        0x48804880u, 0x45004500u, 0x42004200u, 0x3C003C00u};
+            return w[p];  // 33 17 9 5 3 1 | 33 17 9 5 3 1 | 9 5 3 1
         }
     }
 
-    // accumulator units: 2^-14 (ternary) or 2^-17 (binary, which also folds the 2 of 2b - 1)
-    static constexpr float kSeedScale = VARIANT == TQ_TERNARY ? 6.103515625e-05f : 7.62939453125e-06f;
-    static constexpr float kRowScale = VARIANT == TQ_TERNARY ? 16384.0f : 131072.0f;
-
-    // pair p as staged: ternary as is; binary E slots times 1/4, bit-9 slots times 1/2
-    static __device__ __forceinline__ uint32_t prescale(int p, uint32_t v) {
-        bool e, h;
-        if constexpr (VARIANT == TQ_TERNARY) {
-            return v;
-        } else {
-            e = p % 3 == 1;
-            h = p % 3 == 0;
-        }
-        if (!e && !h) return v;
-        const half2_t f = e ? half2_t{(_Float16)0.25f, (_Float16)0.25f} : half2_t{(_Float16)0.5f, (_Float16)0.5f};
-        return __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v) * f);
-    }
+    // accumulator unit 2^-14 for both variants (binary codes carry b in units of
+    // 2^-13, which folds the 2 of t = 2b - 1)
+    static constexpr float kSeedScale = 6.103515625e-05f;
+    static constexpr float kRowScale = 16384.0f;
 
     __device__ __forceinline__ void load(const uint16_t *__restrict__ x, int u) {
         const u32x4 *src = reinterpret_cast<const u32x4 *>(x + (size_t)u * UNIT);
@@ -208,15 +196,11 @@ struct XUnit {
             xp[2 * i] = real ? (l & 0xFFFFu) | (h << 16) : 0u;
             xp[2 * i + 1] = real ? (l >> 16) | (h & 0xFFFF0000u) : 0u;
         }
-        // seed: -(sum over the pairs of w_p * (x[p] + x[p+UNIT/2])) * 2^-F with
-        // w = 1 for E slots, 1 + 4 (ternary M4, binary bit 9), 1 + 16 (ternary
-        // M16), 1 + 8 (binary bit 8)
+        // seed: -(sum over the pairs of w_p * (x[p] + x[p+UNIT/2])) * 2^-14 with
+        // w = 1 + offset (ternary: 1, 5, 17) or 2 offset + 1 (binary: 1 .. 33)
         float z = 0.0f;
 #pragma unroll
         for (int i = 0; i < UNIT / 2; ++i) z = dot2(xp[i], zweight(i), z);
-        // binary E and bit-9 slots are stored pre-scaled to the unit 2^-17
-#pragma unroll
-        for (int i = 0; i < UNIT / 2; ++i) xp[i] = prescale(i, xp[i]);
         uint32_t *slot = xs + (u >> 2) * CHUNK_DW;
         uint32_t *dst = slot + (u & 3) * (UNIT / 2);
 #pragma unroll
@@ -266,7 +250,7 @@ __device__ __forceinline__ void chunk_dot(const u32x4 (&c)[RPL], const uint32_t 
                 }
             }
 #pragma unroll
-            for (int r = 0; r < RPL; ++r) bin_acc64(c[r][d], c[r][d + 1], xp0, xp1, aE[r], aM[r], km);
+            for (int r = 0; r < RPL; ++r) bin_acc64(c[r][d], c[r][d + 1], xp0, xp1, aM[r], km);
         }
     }
 #pragma unroll
