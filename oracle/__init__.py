@@ -9,5 +9,5 @@ only builds that file and marshals numpy arrays through ctypes.
 """
 from .oracle import (  # noqa: F401
     TERNARY, BINARY, OracleError, build, load, half_to_double, codes_bytes,
-    scales_count, pack, unpack, gemm, gemv, default_threads,
+    scales_count, pack, unpack, gemm, gemv, embed, default_threads,
 )

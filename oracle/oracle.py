@@ -66,6 +66,8 @@ def load(lib_path=_LIB):
     lib.oracle_unpack.restype = ci
     lib.oracle_gemm.argtypes = [vp, vp, vp, i64, i64, i64, i32, ci, vp, vp, ci]
     lib.oracle_gemm.restype = ci
+    lib.oracle_embed.argtypes = [vp, vp, vp, i64, i64, i64, i32, ci, vp]
+    lib.oracle_embed.restype = ci
     _lib_cache[lib_path] = lib
     return lib
 
@@ -148,3 +150,18 @@ def gemv(codes, scales, x, N, K, variant=TERNARY, group=128, threads=1, lib=None
     Y, A = gemm(codes, scales, np.asarray(x).reshape(1, -1), N, K, variant, group,
                 threads, lib)
     return Y[0], A[0]
+
+
+def embed(codes, scales, ids, N, K, variant=TERNARY, group=128, lib=None):
+    """out[n_ids][K] float64: row ids[i] of W = s * t (ids in [0, N))."""
+    lib = lib or load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scales)
+    s = s.view(np.uint16) if s.dtype == np.float16 else s.astype(np.uint16)
+    ids = np.ascontiguousarray(ids, dtype=np.int32).reshape(-1)
+    out = np.empty((ids.size, K), dtype=np.float64)
+    rc = lib.oracle_embed(_ptr(codes), _ptr(s), _ptr(ids), ids.size, N, K, group, variant, _ptr(out))
+    if rc:
+        raise OracleError(rc)
+    return out
+

@@ -211,3 +211,41 @@ int oracle_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
     free(x);
     return status;
 }
+
+/* Embedding rows: out[i][k] = s[id_i][k / group] * t[id_i][k] in fp64, for
+ * i < n, from the oracle's own unpack.  Every weight matrix of the model is
+ * ternary, the token embedding included (aitrends.kr,
+ * "Ternary-Bonsai-27B-mlx-2bit", section on what sets the build apart;
+ * thakicloud.github.io, "Bonsai 27B: ternary and 1-bit quantization", "What
+ * the technology is"), so a token's input vector is its row w = s_g * t.
+ * Ids must lie in [0, N); anything else returns OR_ERR_SHAPE. */
+int oracle_embed(const uint8_t *codes, const uint16_t *scales, const int32_t *ids, int64_t n,
+                 int64_t N, int64_t K, int32_t group, int variant, double *out)
+{
+    if (!codes || !scales || !ids || !out) return OR_ERR_NULL;
+    int rc = check_args(N, K, group, variant);
+    if (rc) return rc;
+    if (n < 0) return OR_ERR_SHAPE;
+    int64_t G = K / group;
+    int64_t row_bytes = oracle_codes_bytes(1, K, variant);
+    int8_t *t = (int8_t *)malloc((size_t)K);
+    if (!t) return OR_ERR_NOMEM;
+    for (int64_t i = 0; i < n; i++) {
+        int64_t id = ids[i];
+        if (id < 0 || id >= N) {
+            free(t);
+            return OR_ERR_SHAPE;
+        }
+        int64_t badi = 0;
+        rc = oracle_unpack(codes + id * row_bytes, 1, K, group, variant, t, &badi);
+        if (rc) {
+            free(t);
+            return rc;
+        }
+        for (int64_t k = 0; k < K; k++)
+            out[i * K + k] = oracle_half_to_double(scales[id * G + k / group]) * (double)t[k];
+    }
+    free(t);
+    return OR_OK;
+}
+

@@ -248,6 +248,31 @@ def check_errors(lib):
         assert e.code == 6 and e.index == 128 + 7 * 4 + 2, e.index
 
 
+# ---------------------------------------------------------- embedding rows
+def check_embed(lib):
+    """Row id of W = s * t, built from the input trits with numpy."""
+    g = synth.rng(23)
+    for variant in (oracle.TERNARY, oracle.BINARY):
+        N, K = 9, 512
+        t = synth.trits(g, N, K, variant)
+        s = synth.scales(g, N, K)
+        s[2, 1] = -s[2, 1]
+        s[4, 3] = np.float16(2.0 ** -20)
+        codes = oracle.pack(t, variant, lib=lib)
+        ids = np.array([0, 8, 2, 2, 4, 5, 1], np.int32)
+        got = oracle.embed(codes, s, ids, N, K, variant, lib=lib)
+        assert np.array_equal(got, _dense(t, s)[ids]), variant
+        empty = oracle.embed(codes, s, np.zeros(0, np.int32), N, K, variant, lib=lib)
+        assert empty.shape == (0, K)
+        for bad in (-1, N):
+            try:
+                oracle.embed(codes, s, np.array([0, bad], np.int32), N, K, variant, lib=lib)
+                raise AssertionError("id %d accepted" % bad)
+            except oracle.OracleError as e:
+                assert e.code == 2, e.code
+
+
 ALL_CHECKS = [check_half_decode, check_byte_counts, check_roundtrip_bytes,
               check_golden_layout, check_worked_gemv, check_bruteforce_numpy,
-              check_exact_integer, check_special_cases, check_bound, check_errors]
+              check_exact_integer, check_special_cases, check_bound, check_errors,
+              check_embed]

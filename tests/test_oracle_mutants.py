@@ -31,6 +31,10 @@ MUTANTS = [
     ("scale_abs_missing", [("bound += fabs(s) * apart;", "bound += s * apart;")]),
     ("row_stride", [("codes + n * row_bytes", "codes + n * (row_bytes / 2)")]),
     ("accept_code3", [("if (c == 3) {", "if (c == 4) {")]),
+    ("embed_row_stride", [("codes + id * row_bytes", "codes + id * (row_bytes / 2)")]),
+    ("embed_scale_row", [("scales[id * G + k / group]", "scales[k / group]")]),
+    ("embed_scale_group", [("scales[id * G + k / group]", "scales[id * G]")]),
+    ("embed_out_row", [("out[i * K + k]", "out[k]")]),
 ]
 
 
