@@ -182,6 +182,32 @@ def back_to_back_ms(torch, stream, launch, n, warm=10):
     return a.elapsed_time(b) / n
 
 
+def graph_ms(torch, launch, n, replays=5):
+    """Average time per call of n calls captured in one HIP graph and replayed
+    (no host cost per call: for launches shorter than a Python call)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(3):
+            launch(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            launch(i)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) / (n * replays)
+
+
 def stack_sweep(torch, tq, gen, stream):
     """Configs' whole-stack decode sweep: 64 layers, ~24.83B packed ternary
     weights (6.60 GB), each read once per token.  Input-shared projections are
@@ -312,6 +338,18 @@ def binary_and_lm_head(torch, tq, gen, stream):
                                      "frac_hbm": round(nb / ms1 / 1e6 / PEAK_HBM_GBS, 4)}
     out["lm_head_248320x5120_M8"] = {"us": round(ms8 * 1e3, 2), "gbs": round(nb / ms8 / 1e6, 1),
                                      "frac_hbm": round(nb / ms8 / 1e6 / PEAK_HBM_GBS, 4)}
+    # token-embedding rows from the same 248320 x 5120 ternary table: ids
+    # uniform over the vocabulary; bytes = code row + scale row read, FP16 row
+    # written, per id; timed as graph replays (a one-id gather is shorter than
+    # the Python call that launches it)
+    row_bytes = K // 4 + 2 * (K // 128) + 2 * K
+    for n_ids in (1, 512, 8192):
+        ids = torch.randint(0, N, (n_ids,), device=gen.dev, generator=gen.gen, dtype=torch.int32)
+        rows = torch.empty(n_ids, K, dtype=torch.float16, device=gen.dev)
+        ms = graph_ms(torch, lambda i: tq.tq_embed(pool[i % 3][0], pool[i % 3][1], ids, rows), 60)
+        out["embed_248320x5120_ids%d" % n_ids] = {
+            "us": round(ms * 1e3, 2), "gbs": round(n_ids * row_bytes / ms / 1e6, 1),
+            "frac_hbm": round(n_ids * row_bytes / ms / 1e6 / PEAK_HBM_GBS, 4)}
     return out
 
 
@@ -403,6 +441,11 @@ def main():
     half = [(c[: c.shape[0] // 2], s[: s.shape[0] // 2]) for c, s in gu_pool]
     gate_ms = back_to_back_ms(torch, stream, gemv_launch(0, half), launches)
     gu_b2b_ms = back_to_back_ms(torch, stream, gemv_launch(0, gu_pool), launches)
+    # the same launches replayed from a HIP graph (no Python cost per launch)
+    graph_us = {"gate_up_34816x5120": graph_ms(torch, gemv_launch(0, gu_pool), 4 * slots) * 1e3,
+                "down_5120x17408": graph_ms(torch, gemv_launch(1, [bufs[r][1] for r in range(slots)]),
+                                            4 * slots) * 1e3,
+                "gate_17408x5120_unfused": graph_ms(torch, gemv_launch(0, half), 4 * slots) * 1e3}
     gu_bytes = packed_bytes(Ng + Nu, Kg)
     # average launch duration: back-to-back launches between two events on the
     # kernel's stream (per-launch event pairs add the events' own cost)
@@ -437,6 +480,7 @@ def main():
                           "gate_up_34816x5120_event_pairs": round(gu_ms * 1e3, 3),
                           "down_5120x17408": round(down_ms * 1e3, 3),
                           "gate_17408x5120_unfused": round(gate_ms * 1e3, 3)},
+        "per_launch_us_graph": {k: round(v, 3) for k, v in graph_us.items()},
         "per_launch_gbs": {"gate_up_34816x5120": round(achieved, 1),
                            "down_5120x17408": round(packed_bytes(Nd, Kd) / down_ms / 1e6, 1),
                            "gate_17408x5120_unfused": round(packed_bytes(Ng, Kg) / gate_ms / 1e6, 1)},

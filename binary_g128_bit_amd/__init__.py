@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 
 # every symbol include/tq.h declares
 EXPORTS = ("tq_codes_bytes", "tq_scales_count", "tq_pack", "tq_unpack", "tq_gemv", "tq_gemm",
-           "tq_last_error", "tq_last_error_index", "tq_version")
+           "tq_embed", "tq_last_error", "tq_last_error_index", "tq_version")
 
 
 class TQError(RuntimeError):
@@ -64,6 +64,8 @@ def lib():
     L.tq_gemv.restype = i32
     L.tq_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
     L.tq_gemm.restype = i32
+    L.tq_embed.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
+    L.tq_embed.restype = i32
     L.tq_last_error.argtypes = []
     L.tq_last_error.restype = ctypes.c_char_p
     L.tq_last_error_index.argtypes = []
@@ -171,3 +173,23 @@ def tq_gemm(codes, scales, X, Y=None, variant=TQ_TERNARY, group=GROUP, stream=No
                          _dev(X, "X", half), _dev(Y, "Y", (torch.float32,)), M, N, K, group,
                          variant, _stream(stream)))
     return Y
+
+
+def tq_embed(codes, scales, ids, out=None, variant=TQ_TERNARY, group=GROUP, stream=None):
+    """FP16 rows out[n_ids][K] = s[ids] * t[ids] on the current stream.
+    codes uint8 table, scales float16 [N][K/128], ids int32 [n_ids]."""
+    import torch
+    N, G = scales.shape
+    K = G * GROUP
+    _shape_checks(codes, scales, K, variant)
+    n_ids = ids.numel()
+    if out is None:
+        out = torch.empty((n_ids, K), dtype=torch.float16, device=ids.device)
+    if out.numel() != n_ids * K:
+        raise ValueError("out holds %d values, %d needed" % (out.numel(), n_ids * K))
+    half = (torch.float16, torch.int16)
+    _check(lib().tq_embed(_dev(codes, "codes", (torch.uint8,)), _dev(scales, "scales", half),
+                          _dev(ids, "ids", (torch.int32,)), _dev(out, "out", half), n_ids, N, K,
+                          group, variant, _stream(stream)))
+    return out
+

@@ -12,6 +12,9 @@ int32_t gemv_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_
                      int64_t N, int64_t K, int32_t variant, hipStream_t stream);
 int32_t gemm_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
                      int64_t M, int64_t N, int64_t K, int32_t variant, hipStream_t stream);
+int32_t embed_enqueue(const uint8_t *codes, const uint16_t *scales, const int32_t *ids,
+                      uint16_t *out, int64_t n_ids, int64_t N, int64_t K, int32_t variant,
+                      hipStream_t stream);
 
 namespace {
 int32_t check_device_args(const void *codes, const void *scales, const void *x, const void *y,
@@ -46,6 +49,23 @@ int32_t tq_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
                                 static_cast<hipStream_t>(stream));
     return tq::gemm_enqueue(codes, scales, X, Y, M, N, K, variant,
                             static_cast<hipStream_t>(stream));
+}
+
+int32_t tq_embed(const uint8_t *codes, const uint16_t *scales, const int32_t *ids, uint16_t *out,
+                 int64_t n_ids, int64_t N, int64_t K, int32_t group, int32_t variant,
+                 void *stream) {
+    tq::clear_error();
+    if (int32_t rc = tq::check_shape(1, N, K, group, variant)) return rc;
+    if (n_ids < 0 || n_ids > tq::kMaxN)
+        return tq::fail(TQ_ERR_SHAPE, "n_ids=%lld outside [0, 2^31)", (long long)n_ids);
+    if (n_ids == 0) return TQ_OK;
+    if (!codes || !scales || !ids || !out) return tq::fail(TQ_ERR_NULL, "NULL pointer argument");
+    if (!tq::aligned(codes, 4)) return tq::fail(TQ_ERR_ALIGN, "codes must be 4-byte aligned");
+    if (!tq::aligned(scales, 2)) return tq::fail(TQ_ERR_ALIGN, "scales must be 2-byte aligned");
+    if (!tq::aligned(ids, 4)) return tq::fail(TQ_ERR_ALIGN, "ids must be 4-byte aligned");
+    if (!tq::aligned(out, 16)) return tq::fail(TQ_ERR_ALIGN, "output must be 16-byte aligned");
+    return tq::embed_enqueue(codes, scales, ids, out, n_ids, N, K, variant,
+                             static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -110,6 +110,22 @@ int32_t tq_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
                 float *Y, int64_t M, int64_t N, int64_t K, int32_t group,
                 int32_t variant, void *stream);
 
+/* Device.  Embedding rows: out[i][k] = s[ids[i]][k/128] * t[ids[i]][k] as
+ * IEEE FP16 for i < n_ids, k < K.  Every weight matrix of the model is ternary,
+ * the token embedding included (aitrends.kr, "Ternary-Bonsai-27B-mlx-2bit",
+ * section on what sets the build apart), and w = s_g * t (thakicloud.github.io,
+ * "Bonsai 27B: ternary and 1-bit quantization", "How the compression works");
+ * with t in {-1, 0, +1} each output is exact (a signed zero keeps the sign
+ * of s * 0).  codes / scales: the packed table, as tq_gemv (N rows, K per
+ * row); codes need 4-byte alignment only.  ids: int32 [n_ids] device,
+ * 4-byte aligned.  out: uint16 (FP16 bits) [n_ids][K] device, 16-byte
+ * aligned, caller-owned.  An id outside [0, N) yields a row of +0 (nothing is
+ * read for it).  n_ids == 0 returns TQ_OK without touching any pointer;
+ * n_ids < 0 or >= 2^31 returns TQ_ERR_SHAPE.  Other errors as tq_gemv. */
+int32_t tq_embed(const uint8_t *codes, const uint16_t *scales, const int32_t *ids,
+                 uint16_t *out, int64_t n_ids, int64_t N, int64_t K, int32_t group,
+                 int32_t variant, void *stream);
+
 /* Text of the calling thread's last error ("" if none). */
 const char *tq_last_error(void);
 

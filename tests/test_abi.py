@@ -69,6 +69,39 @@ def test_device_entry_points_validate_on_host(args, status):
         assert rc == status
 
 
+@pytest.mark.parametrize("args,status", [
+    # (codes, scales, ids, out, n_ids, N, K, group, variant)
+    ((0, FAKE, FAKE, FAKE, 4, 8, 128, 128, 0), 1),
+    ((FAKE, FAKE, 0, FAKE, 4, 8, 128, 128, 0), 1),
+    ((FAKE, FAKE, FAKE, 0, 4, 8, 128, 128, 1), 1),
+    ((FAKE, FAKE, FAKE, FAKE, -1, 8, 128, 128, 0), 2),
+    ((FAKE, FAKE, FAKE, FAKE, 1 << 31, 8, 128, 128, 0), 2),
+    ((FAKE, FAKE, FAKE, FAKE, 4, 0, 128, 128, 0), 2),
+    ((FAKE, FAKE, FAKE, FAKE, 4, 8, 200, 128, 0), 2),
+    ((FAKE, FAKE, FAKE, FAKE, 4, 8, 256, 64, 0), 3),
+    ((FAKE, FAKE, FAKE, FAKE, 4, 8, 256, 128, 3), 4),
+    ((FAKE + 2, FAKE, FAKE, FAKE, 4, 8, 256, 128, 0), 7),
+    ((FAKE, FAKE + 1, FAKE, FAKE, 4, 8, 256, 128, 0), 7),
+    ((FAKE, FAKE, FAKE + 2, FAKE, 4, 8, 256, 128, 0), 7),
+    ((FAKE, FAKE, FAKE, FAKE + 8, 4, 8, 256, 128, 0), 7),
+    # nothing to do: no pointer is looked at
+    ((0, 0, 0, 0, 0, 8, 256, 128, 0), 0),
+])
+def test_embed_validates_on_host(args, status):
+    L = tq.lib()
+    codes, scales, ids, out, n_ids, N, K, group, variant = args
+    p = ctypes.c_void_p
+    rc = L.tq_embed(p(codes), p(scales), p(ids), p(out), n_ids, N, K, group, variant, None)
+    assert rc == status, L.tq_last_error()
+    if status:
+        assert L.tq_last_error()
+    # codes need only 4-byte alignment: an offset of 4 passes that check and
+    # fails on the NULL output instead
+    if status == 0:
+        rc = L.tq_embed(p(FAKE + 4), p(FAKE), p(FAKE), p(0), 2, N, K, group, variant, None)
+        assert rc == 1, L.tq_last_error()
+
+
 def test_pack_errors():
     t = np.zeros((2, 128), np.int8)
     t[1, 5] = 2

@@ -45,7 +45,7 @@ def assert_tol(Y, Yref, A, what=""):
 
 def case(seed, N, K, M, variant, exact):
     t, s, X = synth.problem(seed, N, K, M, variant, exact)
-    codes = tq.tq_pack(t, variant)
+    codes = oracle.pack(t, variant)
     return codes, s, X
 
 
@@ -115,7 +115,7 @@ def test_gemv_special_values():
     X = synth.activations(g, 1, K)
     X[0, :64] = np.float16(2.0 ** -24) * np.arange(64)
     X[0, 200:300] = 0
-    codes = tq.tq_pack(t)
+    codes = oracle.pack(t)
     Y = gpu_gemm(codes, s, X, TERN, N, K)
     Yref, A = oracle.gemm(codes, s, X, N, K, TERN)
     assert_tol(Y, Yref, A, "special")
@@ -132,7 +132,7 @@ def test_gemv_sparse_rows(p_zero):
     t[g.random((N, K)) < p_zero] = 0
     s = synth.scales(g, N, K)
     X = synth.activations(g, 1, K)
-    codes = tq.tq_pack(t)
+    codes = oracle.pack(t)
     Y = gpu_gemm(codes, s, X, TERN, N, K)
     Yref, A = oracle.gemm(codes, s, X, N, K, TERN)
     assert_tol(Y, Yref, A, "sparse %.2f" % p_zero)
@@ -255,7 +255,7 @@ def test_gemm_zero_rows_and_special_scales():
     s[40, :] = 0
     s[41, :] = np.float16(6e-8)
     s[42, :] = np.float16(60000.0)
-    codes = tq.tq_pack(t, TERN)
+    codes = oracle.pack(t, TERN)
     Y = gpu_gemm(codes, s, X, TERN, N, K)
     Yref, A = oracle.gemm(codes, s, X, N, K, TERN, threads=THREADS)
     assert_tol(Y, Yref, A, "special")
