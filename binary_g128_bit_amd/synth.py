@@ -5,7 +5,8 @@ of the method's arithmetic (no packing, no decoding, no products), so both the
 oracle-side tests and the product-side tests and bench can share it.
 
 Distributions (27B-shaped decode weights; the weights themselves are not public):
-  * trits t: iid uniform over {-1, 0, +1} (ternary) or {-1, +1} (binary);
+  * trits t: iid uniform over {-1, 0, +1} (ternary, either storage) or
+    {-1, +1} (binary);
   * group scales: float16(exp(N(-4, 0.5))), one per 128 weights along K;
   * activations: float16(N(0, 1)) drawn in float32, round-to-nearest-even;
   * integer-exact sets: activations uniform integers in [-8, 8] and scales
@@ -19,6 +20,7 @@ import numpy as np
 
 TERNARY = 0
 BINARY = 1
+TERNARY5 = 2  # ternary trits stored five to a byte
 GROUP = 128
 
 # Workload shapes (out N, in K).  The 27B-like projection shapes: MLP gate/up
@@ -60,7 +62,7 @@ def seed_for(config_index, matrix_index):
 
 def trits(g, N, K, variant=TERNARY):
     """int8 [N][K] with values in the variant's set."""
-    if variant == TERNARY:
+    if variant in (TERNARY, TERNARY5):
         return (g.integers(0, 3, size=(N, K), dtype=np.int8) - 1).astype(np.int8)
     return (2 * g.integers(0, 2, size=(N, K), dtype=np.int8) - 1).astype(np.int8)
 

@@ -12,6 +12,7 @@ import numpy as np
 
 TERNARY = 0
 BINARY = 1
+TERNARY5 = 2  # five trits per byte, 26 bytes per group, rows padded to 16 bytes
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tq_oracle.c")
@@ -19,7 +20,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 _ERRORS = {1: "null pointer", 2: "bad shape", 3: "group must be 128",
            4: "unknown variant", 5: "value outside the variant's set",
-           6: "invalid code 3", 7: "out of memory"}
+           6: "invalid code (ternary code 3, or a five-trit byte out of range)",
+           7: "out of memory"}
 
 
 class OracleError(RuntimeError):
@@ -97,7 +99,8 @@ def scales_count(N, K, group=128, lib=None):
 
 
 def pack(t, variant=TERNARY, group=128, lib=None):
-    """t: int8 [N][K] -> uint8 codes [N][K/4] (ternary) or [N][K/8] (binary)."""
+    """t: int8 [N][K] -> uint8 codes [N][K/4] (ternary), [N][K/8] (binary) or
+    [N][row bytes] (five-trit bytes)."""
     lib = lib or load()
     t = np.ascontiguousarray(t, dtype=np.int8)
     N, K = t.shape
@@ -111,7 +114,8 @@ def pack(t, variant=TERNARY, group=128, lib=None):
 
 
 def unpack(codes, N, K, variant=TERNARY, group=128, lib=None):
-    """codes -> int8 t [N][K]; raises OracleError(code=6, index) on code 3."""
+    """codes -> int8 t [N][K]; raises OracleError(code=6, index) on an invalid
+    code (index of the first trit it holds)."""
     lib = lib or load()
     codes = np.ascontiguousarray(codes, dtype=np.uint8)
     t = np.empty((N, K), dtype=np.int8)

@@ -27,7 +27,15 @@
  *       [2(k mod 4), 2(k mod 4) + 2); rows are contiguous, row-major;
  *   R4  binary: bit b = (t + 1) / 2, 8 weights per byte, LSB-first;
  *   R5  scales are a separate FP16 array [N][K/128], row-major;
- *   R6  activations FP16 row-major X[M][K], output Y[M][N] (y = W x).
+ *   R6  activations FP16 row-major X[M][K], output Y[M][N] (y = W x);
+ *   R7  five-trit bytes (the native ternary packing the model card names as
+ *       the next step, aitrends.kr, "Ternary-Bonsai-27B-mlx-2bit", section
+ *       "Technical features"; 3^5 = 243 <= 256): a group's 128 trits fill
+ *       26 bytes, byte b holding trits 5b .. 5b+4 of the group as the base-3
+ *       number sum_i (t_{5b+i} + 1) * 3^i (least significant digit first,
+ *       like the 2-bit slots); byte 25 holds trits 125..127 and its digits
+ *       3 and 4 are 0.  A row's G groups are consecutive and the row is
+ *       padded with zero bytes to a multiple of 16 bytes.
  *
  * The product is the plain definition, evaluated in fp64:
  *   Y[m][n] = sum_g s[n][g] * ( sum_{j<128} t[n][128g+j] * X[m][128g+j] )
@@ -43,7 +51,14 @@
 
 enum { OR_OK = 0, OR_ERR_NULL = 1, OR_ERR_SHAPE = 2, OR_ERR_GROUP = 3,
        OR_ERR_VARIANT = 4, OR_ERR_VALUE = 5, OR_ERR_CODE = 6, OR_ERR_NOMEM = 7 };
-enum { OR_TERNARY = 0, OR_BINARY = 1 };
+enum { OR_TERNARY = 0, OR_BINARY = 1, OR_TERNARY5 = 2 };
+
+/* R7: bytes of one row of five-trit codes (26 per group, padded to 16). */
+static int64_t ternary5_row_bytes(int64_t K)
+{
+    int64_t raw = 26 * (K / 128);
+    return (raw + 15) / 16 * 16;
+}
 
 /* IEEE-754 binary16 bit pattern -> real value, from the format's definition:
  * sign bit, 5-bit exponent (bias 15), 10-bit fraction; exponent 0 is the
@@ -69,6 +84,7 @@ int64_t oracle_codes_bytes(int64_t N, int64_t K, int variant)
 {
     if (variant == OR_TERNARY) return N * K / 4;
     if (variant == OR_BINARY) return N * K / 8;
+    if (variant == OR_TERNARY5) return N * ternary5_row_bytes(K);
     return -1;
 }
 
@@ -82,7 +98,8 @@ static int check_args(int64_t N, int64_t K, int32_t group, int variant)
 {
     if (group != 128) return OR_ERR_GROUP;
     if (N < 1 || K < 128 || K % 128 != 0) return OR_ERR_SHAPE;
-    if (variant != OR_TERNARY && variant != OR_BINARY) return OR_ERR_VARIANT;
+    if (variant != OR_TERNARY && variant != OR_BINARY && variant != OR_TERNARY5)
+        return OR_ERR_VARIANT;
     return OR_OK;
 }
 
@@ -98,13 +115,27 @@ int oracle_pack(const int8_t *t, int64_t N, int64_t K, int32_t group,
     int64_t nbytes = oracle_codes_bytes(N, K, variant);
     for (int64_t i = 0; i < N * K; i++) {
         int v = t[i];
-        int ok = (variant == OR_TERNARY) ? (v >= -1 && v <= 1) : (v == -1 || v == 1);
+        int ok = (variant == OR_BINARY) ? (v == -1 || v == 1) : (v >= -1 && v <= 1);
         if (!ok) {
             if (bad) *bad = i;
             return OR_ERR_VALUE;
         }
     }
     memset(codes, 0, (size_t)nbytes);
+    if (variant == OR_TERNARY5) {
+        int64_t rb = ternary5_row_bytes(K);
+        for (int64_t n = 0; n < N; n++)
+            for (int64_t g = 0; g < K / 128; g++)
+                for (int b = 0; b < 26; b++) {                  /* R7 */
+                    int value = 0, power = 1;
+                    for (int i = 0; i < 5 && 5 * b + i < 128; i++) {
+                        value += (t[n * K + 128 * g + 5 * b + i] + 1) * power;
+                        power *= 3;
+                    }
+                    codes[n * rb + 26 * g + b] = (uint8_t)value;
+                }
+        return OR_OK;
+    }
     for (int64_t n = 0; n < N; n++) {
         for (int64_t k = 0; k < K; k++) {
             int v = t[n * K + k];
@@ -130,6 +161,31 @@ int oracle_unpack(const uint8_t *codes, int64_t N, int64_t K, int32_t group,
     if (!codes || !t) return OR_ERR_NULL;
     int rc = check_args(N, K, group, variant);
     if (rc) return rc;
+    if (variant == OR_TERNARY5) {
+        /* R7: a byte is valid when it is below 3^5 and, in byte 25 of a group,
+         * its digits 3 and 4 are 0; otherwise OR_ERR_CODE with the flat index
+         * of the byte's first trit.  Padding bytes are not read. */
+        int64_t rb = ternary5_row_bytes(K);
+        for (int64_t n = 0; n < N; n++)
+            for (int64_t g = 0; g < K / 128; g++)
+                for (int b = 0; b < 26; b++) {
+                    int value = codes[n * rb + 26 * g + b];
+                    for (int i = 0; i < 5; i++) {
+                        int c = value % 3;
+                        value /= 3;
+                        if (5 * b + i < 128)
+                            t[n * K + 128 * g + 5 * b + i] = (int8_t)(c - 1);
+                        else if (c != 0)
+                            value = -1;
+                        if (value < 0) break;
+                    }
+                    if (value != 0) {
+                        if (bad) *bad = n * K + 128 * g + 5 * b;
+                        return OR_ERR_CODE;
+                    }
+                }
+        return OR_OK;
+    }
     for (int64_t n = 0; n < N; n++) {
         for (int64_t k = 0; k < K; k++) {
             if (variant == OR_TERNARY) {

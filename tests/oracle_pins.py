@@ -68,6 +68,16 @@ def check_byte_counts(lib):
         bb = lib.oracle_codes_bytes(N, K, 1)
         assert 8 * (tb + 2 * sc) == 2.125 * N * K, (N, K, tb)
         assert 8 * (bb + 2 * sc) == 1.125 * N * K, (N, K, bb)
+    # five-trit bytes: ceil(128 / 5) = 26 bytes per group, rows padded to 16
+    # bytes; with the scale that is (26 * 8 + 16) / 128 = 1.75 bpw whenever a
+    # row's groups fill whole 16-byte units (G a multiple of 8)
+    for N, K in shapes:
+        G = K // 128
+        rb = -(-26 * G // 16) * 16
+        assert lib.oracle_codes_bytes(N, K, 2) == N * rb, (N, K)
+        if G % 8 == 0:
+            assert 8 * (N * rb + 2 * N * G) == 1.75 * N * K, (N, K)
+    assert math.ceil(128 / 5) == 26 and 3 ** 5 <= 256 < 3 ** 6
     # the pages' deploy size follows from 2.125 bpw on the FP16 model's weights:
     # 54 GB at 16 bpw -> 27.0e9 weights -> 7.17 GB with 2-bit slots
     n_weights = pf["fp16_model_gb"]["value"] * 1e9 * 8 / 16
@@ -104,8 +114,25 @@ def check_roundtrip_bytes(lib):
         t = oracle.unpack(row, 1, 128, oracle.BINARY, lib=lib)
         assert set(np.unique(t)) <= {-1, 1}
         assert np.array_equal(oracle.pack(t, oracle.BINARY, lib=lib), row), b
+    # five-trit bytes: every byte below 3^5 round-trips at positions 0..24 of
+    # a group; at position 25 only values below 3^3; all others are rejected
+    # with the index of the byte's first trit
+    for pos, limit in ((0, 243), (7, 243), (24, 243), (25, 27)):
+        valid = 0
+        for b in range(256):
+            row = np.zeros((1, 16 * 4), dtype=np.uint8)  # K = 256: 2 groups, 64 bytes
+            row[0, 26 + pos] = b
+            try:
+                t = oracle.unpack(row, 1, 256, oracle.TERNARY5, lib=lib)
+            except oracle.OracleError as e:
+                assert e.code == 6 and e.index == 128 + 5 * pos, (pos, b, e.index)
+                assert b >= limit, (pos, b)
+                continue
+            valid += 1
+            assert np.array_equal(oracle.pack(t, oracle.TERNARY5, lib=lib), row), (pos, b)
+        assert valid == limit, (pos, valid)
     g = synth.rng(7)
-    for variant in (oracle.TERNARY, oracle.BINARY):
+    for variant in (oracle.TERNARY, oracle.BINARY, oracle.TERNARY5):
         for N, K in ((1, 128), (5, 384), (16, 1024)):
             t = synth.trits(g, N, K, variant)
             c = oracle.pack(t, variant, lib=lib)
@@ -126,6 +153,26 @@ def check_golden_layout(lib):
         assert np.array_equal(oracle.unpack(codes.reshape(1, -1), 1, K, variant, lib=lib), t)
 
 
+def check_golden_ternary5(lib):
+    ex = _golden("layout_examples.json")["ternary5_row"]
+    K = ex["K"]
+    t = np.ones((1, K), dtype=np.int8)
+    for k in range(128):
+        b, i = divmod(k, 5)
+        t[0, k] = (b + i) % 3 - 1
+    codes = oracle.pack(t, oracle.TERNARY5, lib=lib)[0]
+    assert [int(h, 16) for h in ex["bytes_hex"]] == list(codes), list(codes)
+    assert np.array_equal(oracle.unpack(codes.reshape(1, -1), 1, K, oracle.TERNARY5, lib=lib), t)
+    for bad in ex["invalid"]:
+        c = codes.copy()
+        c[bad["byte_index"]] = bad["value"]
+        try:
+            oracle.unpack(c.reshape(1, -1), 1, K, oracle.TERNARY5, lib=lib)
+            raise AssertionError("accepted %r" % bad)
+        except oracle.OracleError as e:
+            assert e.code == 6 and e.index == bad["error_index"], (bad, e.index)
+
+
 def check_worked_gemv(lib):
     ex = _golden("layout_examples.json")["worked_gemv"]
     N, K = ex["N"], ex["K"]
@@ -143,7 +190,7 @@ def check_worked_gemv(lib):
 # ------------------------------------------------------------ the product
 def check_bruteforce_numpy(lib):
     g = synth.rng(11)
-    for variant in (oracle.TERNARY, oracle.BINARY):
+    for variant in (oracle.TERNARY, oracle.BINARY, oracle.TERNARY5):
         for N, K, M in ((1, 128, 1), (3, 256, 2), (8, 384, 4), (5, 128, 3)):
             t = synth.trits(g, N, K, variant)
             s = synth.scales(g, N, K)
@@ -161,7 +208,7 @@ def check_bruteforce_numpy(lib):
 
 def check_exact_integer(lib):
     g = synth.rng(13)
-    for variant in (oracle.TERNARY, oracle.BINARY):
+    for variant in (oracle.TERNARY, oracle.BINARY, oracle.TERNARY5):
         N, K, M = 4, 384, 3
         t = synth.trits(g, N, K, variant)
         s = np.ones((N, K // 128), dtype=np.float16)
@@ -235,7 +282,7 @@ def check_errors(lib):
         except oracle.OracleError as e:
             assert e.code == 5 and e.index == idx, (e.code, e.index)
     for N, K, group, variant, code in ((2, 100, 128, 0, 2), (2, 192, 128, 0, 2), (0, 128, 128, 0, 2),
-                                       (2, 128, 64, 0, 3), (2, 128, 128, 2, 4)):
+                                       (2, 128, 64, 0, 3), (2, 128, 128, 3, 4)):
         rc = lib.oracle_pack(t.ctypes.data, N, K, group, variant,
                              np.zeros(64, np.uint8).ctypes.data, None)
         assert rc == code, (N, K, group, variant, rc)
@@ -252,7 +299,7 @@ def check_errors(lib):
 def check_embed(lib):
     """Row id of W = s * t, built from the input trits with numpy."""
     g = synth.rng(23)
-    for variant in (oracle.TERNARY, oracle.BINARY):
+    for variant in (oracle.TERNARY, oracle.BINARY, oracle.TERNARY5):
         N, K = 9, 512
         t = synth.trits(g, N, K, variant)
         s = synth.scales(g, N, K)
@@ -275,4 +322,4 @@ def check_embed(lib):
 ALL_CHECKS = [check_half_decode, check_byte_counts, check_roundtrip_bytes,
               check_golden_layout, check_worked_gemv, check_bruteforce_numpy,
               check_exact_integer, check_special_cases, check_bound, check_errors,
-              check_embed]
+              check_embed, check_golden_ternary5]

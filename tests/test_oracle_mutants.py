@@ -35,6 +35,17 @@ MUTANTS = [
     ("embed_scale_row", [("scales[id * G + k / group]", "scales[k / group]")]),
     ("embed_scale_group", [("scales[id * G + k / group]", "scales[id * G]")]),
     ("embed_out_row", [("out[i * K + k]", "out[k]")]),
+    ("t5_msb_digit_first", [("int value = 0, power = 1;", "int value = 0, power = 81;"),
+                            ("power *= 3;", "power /= 3;")]),
+    ("t5_group_stride", [("codes[n * rb + 26 * g + b] = (uint8_t)value;",
+                          "codes[n * rb + 25 * g + b] = (uint8_t)value;")]),
+    ("t5_no_row_padding", [("return (raw + 15) / 16 * 16;", "return raw;")]),
+    ("t5_tail_digits_unchecked", [("else if (c != 0)", "else if (c > 2)")]),
+    ("t5_range_unchecked", [("if (value != 0) {", "if (value > 1) {")]),
+    ("t5_code_map", [("t[n * K + 128 * g + 5 * b + i] = (int8_t)(c - 1);",
+                      "t[n * K + 128 * g + 5 * b + i] = (int8_t)(1 - c);"),
+                     ("value += (t[n * K + 128 * g + 5 * b + i] + 1) * power;",
+                      "value += (1 - t[n * K + 128 * g + 5 * b + i]) * power;")]),
 ]
 
 
