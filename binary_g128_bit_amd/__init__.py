@@ -16,6 +16,7 @@ import numpy as np
 
 TQ_TERNARY = 0
 TQ_BINARY = 1
+TQ_TERNARY5 = 2  # five trits per byte (GEMV only)
 GROUP = 128
 
 _STATUS = {0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_GROUP",
@@ -96,13 +97,14 @@ def tq_scales_count(N, K, group=GROUP):
 
 # ------------------------------------------------------------------ host side
 def tq_pack(t, variant=TQ_TERNARY, group=GROUP):
-    """int8 t [N][K] (numpy) -> uint8 codes [N][K/4] (ternary) or [N][K/8]."""
+    """int8 t [N][K] (numpy) -> uint8 codes [N][row bytes]: K/4 (ternary),
+    K/8 (binary) or 26*K/128 rounded up to 16 (five-trit bytes)."""
     t = np.ascontiguousarray(t, dtype=np.int8)
     if t.ndim != 2:
         raise ValueError("t must be 2-D [N][K]")
     N, K = t.shape
-    per = 4 if variant == TQ_TERNARY else 8
-    out = np.empty((N, max(K // per, 1)), dtype=np.uint8)
+    nbytes = lib().tq_codes_bytes(N, K, variant) if N > 0 else 0
+    out = np.empty((N, max(nbytes // max(N, 1), 1)), dtype=np.uint8)
     _check(lib().tq_pack(t.ctypes.data, N, K, group, variant, out.ctypes.data))
     return out
 

@@ -12,6 +12,8 @@ int32_t gemv_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_
                      int64_t N, int64_t K, int32_t variant, hipStream_t stream);
 int32_t gemm_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
                      int64_t M, int64_t N, int64_t K, int32_t variant, hipStream_t stream);
+int32_t gemv5_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
+                      int64_t N, int64_t K, hipStream_t stream);
 int32_t embed_enqueue(const uint8_t *codes, const uint16_t *scales, const int32_t *ids,
                       uint16_t *out, int64_t n_ids, int64_t N, int64_t K, int32_t variant,
                       hipStream_t stream);
@@ -36,6 +38,8 @@ int32_t tq_gemv(const uint8_t *codes, const uint16_t *scales, const uint16_t *x,
                 int64_t N, int64_t K, int32_t group, int32_t variant, void *stream) {
     tq::clear_error();
     if (int32_t rc = tq::check_device_args(codes, scales, x, y, 1, N, K, group, variant)) return rc;
+    if (variant == TQ_TERNARY5)
+        return tq::gemv5_enqueue(codes, scales, x, y, N, K, static_cast<hipStream_t>(stream));
     return tq::gemv_enqueue(codes, scales, x, y, N, K, variant,
                             static_cast<hipStream_t>(stream));
 }
@@ -44,6 +48,12 @@ int32_t tq_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
                 int64_t M, int64_t N, int64_t K, int32_t group, int32_t variant, void *stream) {
     tq::clear_error();
     if (int32_t rc = tq::check_device_args(codes, scales, X, Y, M, N, K, group, variant)) return rc;
+    if (variant == TQ_TERNARY5) {
+        if (M != 1)
+            return tq::fail(TQ_ERR_VARIANT, "TQ_TERNARY5 has a GEMV only (M = 1), got M=%lld",
+                            (long long)M);
+        return tq::gemv5_enqueue(codes, scales, X, Y, N, K, static_cast<hipStream_t>(stream));
+    }
     if (M == 1)
         return tq::gemv_enqueue(codes, scales, X, Y, N, K, variant,
                                 static_cast<hipStream_t>(stream));
@@ -56,6 +66,8 @@ int32_t tq_embed(const uint8_t *codes, const uint16_t *scales, const int32_t *id
                  void *stream) {
     tq::clear_error();
     if (int32_t rc = tq::check_shape(1, N, K, group, variant)) return rc;
+    if (variant == TQ_TERNARY5)
+        return tq::fail(TQ_ERR_VARIANT, "tq_embed takes TQ_TERNARY or TQ_BINARY tables");
     if (n_ids < 0 || n_ids > tq::kMaxN)
         return tq::fail(TQ_ERR_SHAPE, "n_ids=%lld outside [0, 2^31)", (long long)n_ids);
     if (n_ids == 0) return TQ_OK;

@@ -1,0 +1,419 @@
+// Batch-1 decode GEMV over ternary weights stored five trits per byte, gfx950.
+//
+// y[n] = sum_g s[n][g] * sum_{j<128} t[n][128g+j] * x[128g+j] with w = s_g * t
+// (thakicloud.github.io, "Bonsai 27B: ternary and 1-bit quantization", "How
+// the compression works").  The storage is the native ternary packing that
+// the model card names as the step after 2-bit slots (aitrends.kr,
+// "Ternary-Bonsai-27B-mlx-2bit", "Technical features"): byte b of a group
+// holds trits 5b..5b+4 as the base-3 number sum_i (t_{5b+i} + 1) 3^i, 26
+// bytes per group (the last one holds three trits), rows padded to 16 bytes.
+// That is 1.75 bits per weight with the scale against 2.125 for 2-bit slots.
+//
+// Decode.  Base-3 digits do not fall out of shifts and masks, so each code
+// byte is looked up in a table in LDS whose 16-byte entry already holds the
+// byte's five trits as FP16 {-1, 0, +1}, laid out against the activation
+// pairs (x[2i], x[2i+1]) in natural order: a byte at an even position of its
+// group starts on a pair boundary (halves t0..t4, 0), one at an odd position
+// starts in the middle of a pair (halves 0, t0..t4).  So one lookup and three
+// v_dot2_f32_f16 take five weights, with no activation permutation and no
+// offset correction (the products t*x are exact).  The lookup address is
+// byte * 256 + copy * 16 (+ table offset), built with one v_perm_b32; every
+// lane of a 16-lane (or 8-lane) LDS phase reads its own copy of the table,
+// which keeps the random lookups free of bank conflicts.
+//
+// Work split.  A lane owns units of two groups (52 code bytes, 13 dwords,
+// dword aligned) of its rows; LPR lanes cover a row and 64/LPR rows make a
+// wave-block.  Workgroups are persistent (one per CU) and walk contiguous
+// ranges of blocks, with two register sets of codes in flight.  The partial
+// sum of each group is scaled once by its FP16 scale; row partials are summed
+// across the LPR lanes with DPP moves.
+#include <hip/hip_runtime.h>
+
+#include <type_traits>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+
+constexpr size_t kMaxLds5 = 163840;
+constexpr int kUnitDw = 13;      // code dwords per two-group unit
+constexpr int kXUnitDw = 132;    // LDS dwords per unit of x: 128 + 4 (bank spread)
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c,
+                                  false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                 0xF, 0xF, false));
+}
+
+template <int LPR>
+__device__ __forceinline__ float seg_sum(float v) {
+    if (LPR >= 2) v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+    if (LPR >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+    if (LPR >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+    if (LPR >= 16) v += dpp_f<0x140>(v); // row_mirror
+    if (LPR >= 32) v += __shfl_xor(v, 16);
+    if (LPR >= 64) v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Table geometry.  16 copies: entry (parity p, byte v, copy c) at
+// p * 65536 + v * 256 + c * 16 (128 KiB).  8 copies: v * 256 + p * 128 + c * 16
+// (64 KiB; two lanes of a 16-lane phase share a copy).
+template <int COPIES>
+struct Lut {
+    static constexpr int BYTES = 2 * 256 * COPIES * 16;
+    static __device__ __forceinline__ uint32_t base(int p, int lane) {
+        const uint32_t c = (uint32_t)(lane & (COPIES - 1)) * 16u;
+        return COPIES == 16 ? (uint32_t)p * 65536u + c : (uint32_t)p * 128u + c;
+    }
+    static __device__ __forceinline__ uint32_t addr(int p, int v, int c) {
+        return COPIES == 16 ? (uint32_t)(p * 65536 + v * 256 + c * 16)
+                            : (uint32_t)(v * 256 + p * 128 + c * 16);
+    }
+};
+
+// FP16 bits of the trit (c - 1) for a base-3 digit c.
+__device__ __forceinline__ uint32_t trit_half(uint32_t c) {
+    return c == 0 ? 0xBC00u : (c == 2 ? 0x3C00u : 0u);
+}
+
+// Entry for byte value v: even layout (t0 t1 | t2 t3 | t4 0 | 0 0), odd
+// layout (0 t0 | t1 t2 | t3 t4 | 0 0).  Bytes 243..255 hold no valid code
+// and map to zeros.
+__device__ __forceinline__ u32x4 lut_entry(int p, uint32_t v) {
+    if (v >= 243u) return u32x4{0u, 0u, 0u, 0u};
+    uint32_t h[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        h[i] = trit_half(v % 3u);
+        v /= 3u;
+    }
+    if (p == 0) return u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4], 0u};
+    return u32x4{h[0] << 16, h[1] | (h[2] << 16), h[3] | (h[4] << 16), 0u};
+}
+
+// Bytes [B0, B1) of one group (26 code bytes starting at byte 26*H of the
+// unit's dwords cd) against the group's activation pairs xg (LDS), for RPL
+// rows sharing x.  Only the pairs these bytes touch are read.
+template <int H, int B0, int B1, int RPL>
+__device__ __forceinline__ void bytes_dot(const uint32_t (&cd)[RPL][kUnitDw], const uint32_t *xg,
+                                          const char *lut, uint32_t le, uint32_t lo,
+                                          float (&a)[RPL]) {
+    constexpr int P0 = (5 * B0) / 2 / 4 * 4;                  // first pair, rounded down to 4
+    constexpr int P1 = ((5 * B1 + 1) / 2 + 3) / 4 * 4;         // one past the last, rounded up
+    constexpr int NP = (P1 < 64 ? P1 : 64) - P0;
+    uint32_t X[NP];
+#pragma unroll
+    for (int q = 0; q < NP / 4; ++q) {
+        const u32x4 v = reinterpret_cast<const u32x4 *>(xg + P0)[q];
+        X[4 * q] = v[0];
+        X[4 * q + 1] = v[1];
+        X[4 * q + 2] = v[2];
+        X[4 * q + 3] = v[3];
+    }
+#pragma unroll
+    for (int b = B0; b < B1; ++b) {
+        const int q = 26 * H + b;
+        // result bytes: [base.b0, code byte, base.b2, 0]
+        constexpr uint32_t kSelHi = 0x0C020000u;
+        const uint32_t sel = kSelHi | ((uint32_t)(4 + (q & 3)) << 8);
+        const int x0 = ((b & 1) ? (5 * b - 1) / 2 : 5 * b / 2) - P0;
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const uint32_t ad = __builtin_amdgcn_perm(cd[r][q >> 2], (b & 1) ? lo : le, sel);
+            const u32x4 e = *reinterpret_cast<const u32x4 *>(lut + ad);
+            a[r] = dot2(e[0], X[x0], a[r]);
+            a[r] = dot2(e[1], X[x0 + 1], a[r]);
+            if (b != 25) a[r] = dot2(e[2], X[x0 + 2], a[r]);
+        }
+    }
+}
+
+template <int H, int RPL>
+__device__ __forceinline__ void group_dot(const uint32_t (&cd)[RPL][kUnitDw], const uint32_t *xg,
+                                          const char *lut, uint32_t le, uint32_t lo,
+                                          float (&a)[RPL]) {
+    bytes_dot<H, 0, 13, RPL>(cd, xg, lut, le, lo, a);
+    __builtin_amdgcn_sched_barrier(0);
+    bytes_dot<H, 13, 26, RPL>(cd, xg, lut, le, lo, a);
+}
+
+__device__ __forceinline__ float half_f(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// Loads for one block: per row r and unit slot i, the unit's 13 code dwords
+// (group 0: bytes 0..27, group 1: bytes 28..51) and its two group scales.
+// RAGGED clamps the last unit slot (the only one that can lie past the row:
+// the host picks shapes with (NU - 1) * LPR <= units) to the last unit, and
+// when a unit has no second group (an odd group count) reads group 1's dwords
+// from the unit's start instead of past the row; those slots meet zero
+// activations and contribute nothing.
+template <int LPR, int NU, int RPL, bool RAGGED>
+__device__ __forceinline__ void load_block5(const uint8_t *__restrict__ codes,
+                                            const uint16_t *__restrict__ scales,
+                                            const int (&row)[RPL], int j, int U, int G, int rbytes,
+                                            uint32_t (&c)[NU][RPL][kUnitDw],
+                                            uint32_t (&s)[NU][RPL]) {
+    // the unit's two scales in one register (group 2u low, 2u + 1 high); an
+    // even group count keeps every pair 4-byte aligned
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const uint16_t *sp = scales + (size_t)row[r] * G;
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int u = (RAGGED && i == NU - 1) ? min(j + i * LPR, U - 1) : j + i * LPR;
+            if (RAGGED)
+                s[i][r] = (uint32_t)sp[2 * u] | ((uint32_t)sp[min(2 * u + 1, G - 1)] << 16);
+            else
+                s[i][r] = reinterpret_cast<const uint32_t *>(sp)[u];
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < RPL; ++r) {
+        const uint8_t *rp = codes + (size_t)row[r] * rbytes;
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int u = (RAGGED && i == NU - 1) ? min(j + i * LPR, U - 1) : j + i * LPR;
+            const uint8_t *up = rp + 52 * u;
+            const uint8_t *up1 = (!RAGGED || 2 * u + 1 < G) ? up + 28 : up;
+            const u32x4a v0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4a *>(up));
+            const u32x4a v1 = __builtin_nontemporal_load(reinterpret_cast<const u32x4a *>(up + 12));
+            const u32x4a v2 = __builtin_nontemporal_load(reinterpret_cast<const u32x4a *>(up1));
+            const u32x4a v3 = __builtin_nontemporal_load(reinterpret_cast<const u32x4a *>(up1 + 8));
+            // bytes 0..15 | 12..27 | 28..43 | 36..51
+            c[i][r][0] = v0[0];
+            c[i][r][1] = v0[1];
+            c[i][r][2] = v0[2];
+            c[i][r][3] = v1[0];
+            c[i][r][4] = v1[1];
+            c[i][r][5] = v1[2];
+            c[i][r][6] = v1[3];
+            c[i][r][7] = v2[0];
+            c[i][r][8] = v2[1];
+            c[i][r][9] = v2[2];
+            c[i][r][10] = v3[1];
+            c[i][r][11] = v3[2];
+            c[i][r][12] = v3[3];
+        }
+    }
+}
+
+template <int CAP>
+constexpr int copies_for() {
+    return (size_t)Lut<16>::BYTES + (size_t)CAP * kXUnitDw * 4 <= kMaxLds5 ? 16 : 8;
+}
+
+template <int LPR, int NU>
+constexpr size_t lds5_bytes() {
+    return (size_t)Lut<copies_for<LPR * NU>()>::BYTES + (size_t)LPR * NU * kXUnitDw * 4;
+}
+
+template <int LPR, int NU, int RPL, int WAVES, bool RAGGED>
+__global__ __launch_bounds__(64 * WAVES) void gemv5_kernel(const uint8_t *__restrict__ codes,
+                                                           const uint16_t *__restrict__ scales,
+                                                           const uint16_t *__restrict__ x,
+                                                           float *__restrict__ y, int N, int K) {
+    extern __shared__ u32x4 lds5[];
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int CAP = LPR * NU;
+    constexpr int COPIES = copies_for<CAP>();
+    using L = Lut<COPIES>;
+    constexpr int RS = 64 / LPR;
+    constexpr int RB = RS * RPL;
+    constexpr int XV = CAP * kXUnitDw / 4;             // 16-byte x slots in LDS
+    constexpr int XPER = (XV + THREADS - 1) / THREADS;
+    char *lut = reinterpret_cast<char *>(lds5);
+    uint32_t *xs = reinterpret_cast<uint32_t *>(lut + L::BYTES);
+    const int G = K >> 7, U = (G + 1) >> 1;
+    const int rbytes = (26 * G + 15) & ~15;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int seg = lane / LPR, j = lane % LPR;
+    const int nblocks = (N + RB - 1) / RB;
+    const int b_begin = (int)(((long long)blockIdx.x * nblocks) / gridDim.x);
+    const int b_end = (int)(((long long)(blockIdx.x + 1) * nblocks) / gridDim.x);
+
+    // 1. x into registers: LDS slot v of unit u holds x dwords 4(v%33).. of
+    // that unit (slots 32 of each unit are padding); zero past K
+    const int xdw = K >> 1;  // x dwords
+    u32x4 xv[XPER];
+#pragma unroll
+    for (int k = 0; k < XPER; ++k) {
+        const int v = threadIdx.x + k * THREADS;
+        const int u = v / (kXUnitDw / 4), w = v % (kXUnitDw / 4);
+        const int d = u * 128 + 4 * w;
+        xv[k] = (v < XV && w < 32 && d < xdw) ? reinterpret_cast<const u32x4 *>(x)[d >> 2]
+                                             : u32x4{0u, 0u, 0u, 0u};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. the first block's codes and scales
+    uint32_t ca[NU][RPL][kUnitDw], cb[NU][RPL][kUnitDw];
+    uint32_t sa[NU][RPL], sb[NU][RPL];
+    int row[RPL];
+    auto rows_of = [&](int bb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) row[r] = min(bb * RB + r * RS + seg, N - 1);
+    };
+    int b = b_begin + wave;
+    rows_of(min(b, b_end - 1));
+    load_block5<LPR, NU, RPL, RAGGED>(codes, scales, row, j, U, G, rbytes, ca, sa);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 3. the lookup tables, every copy
+    for (int e = threadIdx.x; e < 512; e += THREADS) {
+        const int p = e >> 8, v = e & 255;
+        const u32x4 ent = lut_entry(p, (uint32_t)v);
+#pragma unroll
+        for (int c = 0; c < COPIES; ++c)
+            *reinterpret_cast<u32x4 *>(lut + L::addr(p, v, c)) = ent;
+    }
+    // 4. x into LDS
+#pragma unroll
+    for (int k = 0; k < XPER; ++k) {
+        const int v = threadIdx.x + k * THREADS;
+        if (v < XV) reinterpret_cast<u32x4 *>(xs)[v] = xv[k];
+    }
+    __syncthreads();
+
+    const uint32_t le = L::base(0, lane), lo = L::base(1, lane);
+    auto block = [&](const uint32_t (&c)[NU][RPL][kUnitDw], const uint32_t (&sv)[NU][RPL],
+                     int bb) __attribute__((always_inline)) {
+        float acc[RPL];
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) acc[r] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const uint32_t *xu = xs + (j + i * LPR) * kXUnitDw;
+            float a0[RPL], a1[RPL];
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) a0[r] = a1[r] = 0.0f;
+            group_dot<0, RPL>(c[i], xu, lut, le, lo, a0);
+            group_dot<1, RPL>(c[i], xu + 64, lut, le, lo, a1);
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                acc[r] = __builtin_fmaf(half_f(sv[i][r] & 0xFFFFu), a0[r], acc[r]);
+                acc[r] = __builtin_fmaf(half_f(sv[i][r] >> 16), a1[r], acc[r]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const float out = seg_sum<LPR>(acc[r]);
+            const int rr = bb * RB + r * RS + seg;
+            if (j == 0 && rr < N) y[rr] = out;
+        }
+    };
+    for (; b < b_end; b += 2 * WAVES) {
+        const int b2 = b + WAVES;
+        if (b2 < b_end) {
+            rows_of(b2);
+            load_block5<LPR, NU, RPL, RAGGED>(codes, scales, row, j, U, G, rbytes, cb, sb);
+        }
+        block(ca, sa, b);
+        if (b2 >= b_end) break;
+        const int b3 = b2 + WAVES;
+        if (b3 < b_end) {
+            rows_of(b3);
+            load_block5<LPR, NU, RPL, RAGGED>(codes, scales, row, j, U, G, rbytes, ca, sa);
+        }
+        block(cb, sb, b2);
+    }
+}
+
+struct Config5 {
+    int lpr, nu;
+};
+
+// (lanes per row, units per lane), least capacity first.
+// The widest, 160 units (K = 40960), is the most whose activations fit next
+// to the 64 KiB table.
+constexpr Config5 kConfigs5[] = {{2, 1},  {4, 1},  {8, 1},  {4, 3},  {8, 2},  {4, 5},
+                                 {8, 3},  {16, 2}, {8, 5},  {16, 3}, {16, 4}, {16, 5}, {32, 3},
+                                 {32, 4}, {32, 5}};
+constexpr int64_t kMaxK5 = 160 * 256;
+
+Config5 pick5(int units) {
+    Config5 best{0, 0};
+    for (const Config5 &c : kConfigs5) {
+        const int cap = c.lpr * c.nu;
+        if (cap < units || (c.nu - 1) * c.lpr > units) continue;
+        if (!best.lpr || cap < best.lpr * best.nu || (cap == best.lpr * best.nu && c.nu < best.nu))
+            best = c;
+    }
+    return best;
+}
+
+constexpr int kWaves5 = 8;
+
+int device_cus5() {
+    static int cache[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cache[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cache[dev] = n;
+    }
+    return cache[dev];
+}
+
+template <int LPR, int NU>
+hipError_t launch5(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y, int N,
+                   int K, hipStream_t stream) {
+    constexpr int RPL = 1;
+    constexpr size_t lds = lds5_bytes<LPR, NU>();
+    static_assert(lds <= kMaxLds5, "LDS budget");
+    constexpr int rows_per_block = (64 / LPR) * RPL;
+    const int nblocks = (N + rows_per_block - 1) / rows_per_block;
+    const int grid = max(1, min(device_cus5(), (nblocks + kWaves5 - 1) / kWaves5));
+    const int G = K / 128;
+    // the exact shape also reads each unit's two scales as one dword
+    const bool exact = (G % 2 == 0) && (G / 2 == LPR * NU) &&
+                       (reinterpret_cast<uintptr_t>(scales) & 3) == 0;
+    if (exact)
+        hipLaunchKernelGGL((gemv5_kernel<LPR, NU, RPL, kWaves5, false>), dim3(grid),
+                           dim3(64 * kWaves5), lds, stream, codes, scales, x, y, N, K);
+    else
+        hipLaunchKernelGGL((gemv5_kernel<LPR, NU, RPL, kWaves5, true>), dim3(grid),
+                           dim3(64 * kWaves5), lds, stream, codes, scales, x, y, N, K);
+    return hipGetLastError();
+}
+
+hipError_t dispatch5(const Config5 &c, const uint8_t *codes, const uint16_t *scales,
+                     const uint16_t *x, float *y, int N, int K, hipStream_t s) {
+#define TQ5_CASE(L, U) \
+    if (c.lpr == L && c.nu == U) return launch5<L, U>(codes, scales, x, y, N, K, s);
+    TQ5_CASE(2, 1) TQ5_CASE(4, 1) TQ5_CASE(8, 1) TQ5_CASE(4, 3) TQ5_CASE(8, 2)
+    TQ5_CASE(4, 5) TQ5_CASE(8, 3) TQ5_CASE(16, 2) TQ5_CASE(8, 5) TQ5_CASE(16, 3) TQ5_CASE(16, 4)
+    TQ5_CASE(16, 5) TQ5_CASE(32, 3) TQ5_CASE(32, 4) TQ5_CASE(32, 5)
+#undef TQ5_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int32_t gemv5_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
+                      int64_t N, int64_t K, hipStream_t stream) {
+    const int units = (int)((K / 128 + 1) / 2);
+    const Config5 c = pick5(units);
+    if (!c.lpr || K > kMaxK5)
+        return fail(TQ_ERR_SHAPE, "K=%lld is above the five-trit GEMV limit %lld", (long long)K,
+                    (long long)kMaxK5);
+    const hipError_t e = dispatch5(c, codes, scales, x, y, (int)N, (int)K, stream);
+    if (e != hipSuccess) return fail(TQ_ERR_HIP, "GEMV launch failed: %s", hipGetErrorString(e));
+    return TQ_OK;
+}
+
+}  // namespace tq

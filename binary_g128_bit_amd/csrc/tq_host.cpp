@@ -5,6 +5,9 @@
 // slot (aitrends.kr, "Ternary-Bonsai-27B-mlx-2bit", section "Technical
 // features") and the 1-bit build's {-1, +1} set (thakicloud.github.io,
 // "Bonsai 27B: ternary and 1-bit quantization", "How the compression works").
+// The five-trit storage (TQ_TERNARY5) is the native ternary packing the
+// model card names as the next step: 26 bytes per 128-weight group, byte b
+// the base-3 number of trits 5b..5b+4 (least significant digit first).
 #include <cstdarg>
 #include <cstring>
 #include <string>
@@ -68,6 +71,48 @@ inline int bin_byte(const int8_t *o) {
     return int(v);
 }
 
+// Base-3 digits of every byte value: digits[v][i] for i < 5; ok[v] when v < 3^5.
+struct Base3Table {
+    int8_t trit[256][5];
+    bool below243[256];
+    Base3Table() {
+        for (int v = 0; v < 256; ++v) {
+            int r = v;
+            for (int i = 0; i < 5; ++i) {
+                trit[v][i] = int8_t(r % 3 - 1);
+                r /= 3;
+            }
+            below243[v] = r == 0;
+        }
+    }
+};
+const Base3Table &base3() {
+    static const Base3Table table;
+    return table;
+}
+
+// Five-trit bytes of one row: n trits per byte (5, or 3 for the last byte of
+// a group) folded most significant first, c = t + 1, then zero padding.  A
+// trit outside {-1,0,+1} returns TQ_ERR_VALUE with its index in the row.
+int32_t pack_row5(const int8_t *t, int64_t K, uint8_t *out, int64_t *bad_k) {
+    for (int64_t k = 0; k < K; ++k)
+        if (static_cast<unsigned>(int(t[k]) + 1) > 2u) {
+            *bad_k = k;
+            return TQ_ERR_VALUE;
+        }
+    const int64_t G = K / kGroup, rb = ternary5_row_bytes(K);
+    for (int64_t g = 0; g < G; ++g) {
+        const int8_t *tg = t + g * kGroup;
+        for (int b = 0; b < 26; ++b) {
+            int v = 0;
+            for (int i = (b < 25 ? 5 : 3) - 1; i >= 0; --i) v = 3 * v + int(tg[5 * b + i]) + 1;
+            out[g * 26 + b] = uint8_t(v);
+        }
+    }
+    for (int64_t i = G * 26; i < rb; ++i) out[i] = 0;
+    return TQ_OK;
+}
+
 int32_t check_host(const void *a, const void *b, int64_t N, int64_t K, int32_t group,
                    int32_t variant) {
     if (!a || !b) return fail(TQ_ERR_NULL, "NULL pointer argument");
@@ -83,6 +128,7 @@ size_t tq_codes_bytes(int64_t N, int64_t K, int32_t variant) {
     if (N < 1 || K < tq::kGroup || K % tq::kGroup) return 0;
     if (variant == TQ_TERNARY) return size_t(N) * size_t(K / 4);
     if (variant == TQ_BINARY) return size_t(N) * size_t(K / 8);
+    if (variant == TQ_TERNARY5) return size_t(N) * size_t(tq::ternary5_row_bytes(K));
     return 0;
 }
 
@@ -95,6 +141,18 @@ int32_t tq_pack(const int8_t *t, int64_t N, int64_t K, int32_t group, int32_t va
                 uint8_t *codes) {
     tq::clear_error();
     if (int32_t rc = tq::check_host(t, codes, N, K, group, variant)) return rc;
+    if (variant == TQ_TERNARY5) {
+        const int64_t rb = tq::ternary5_row_bytes(K);
+        for (int64_t n = 0; n < N; ++n) {
+            int64_t k = -1;
+            if (tq::pack_row5(t + n * K, K, codes + n * rb, &k) != TQ_OK) {
+                const int64_t idx = n * K + k;
+                return tq::fail_at(TQ_ERR_VALUE, idx, "t[%lld] = %d is outside {-1,0,+1}",
+                                   (long long)idx, int(t[idx]));
+            }
+        }
+        return TQ_OK;
+    }
     const int64_t per = variant == TQ_TERNARY ? 4 : 8;
     const int64_t nbytes = N * (K / per);
     for (int64_t i = 0; i < nbytes; ++i) {
@@ -115,6 +173,26 @@ int32_t tq_unpack(const uint8_t *codes, int64_t N, int64_t K, int32_t group, int
                   int8_t *t) {
     tq::clear_error();
     if (int32_t rc = tq::check_host(codes, t, N, K, group, variant)) return rc;
+    if (variant == TQ_TERNARY5) {
+        const tq::Base3Table &tb = tq::base3();
+        const int64_t G = K / tq::kGroup, rb = tq::ternary5_row_bytes(K);
+        for (int64_t n = 0; n < N; ++n)
+            for (int64_t g = 0; g < G; ++g)
+                for (int b = 0; b < 26; ++b) {
+                    const uint8_t v = codes[n * rb + g * 26 + b];
+                    // the last byte of a group holds three trits: digits 3, 4 must be 0
+                    const bool ok = b < 25 ? tb.below243[v] : v < 27;
+                    const int64_t idx = n * K + g * tq::kGroup + 5 * b;
+                    if (!ok)
+                        return tq::fail_at(TQ_ERR_CODE, idx,
+                                           "invalid five-trit byte %u at weight %lld (row %lld, k %lld)",
+                                           unsigned(v), (long long)idx, (long long)n,
+                                           (long long)(idx - n * K));
+                    const int nt = b < 25 ? 5 : 3;
+                    for (int i = 0; i < nt; ++i) t[idx + i] = tb.trit[v][i];
+                }
+        return TQ_OK;
+    }
     if (variant == TQ_TERNARY) {
         const int64_t nbytes = N * (K / 4);
         for (int64_t i = 0; i < nbytes; ++i) {

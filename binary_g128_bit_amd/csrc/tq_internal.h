@@ -35,11 +35,14 @@ inline int32_t check_shape(int64_t M, int64_t N, int64_t K, int32_t group, int32
                     (long long)kMaxK);
     if (group != kGroup)
         return fail(TQ_ERR_GROUP, "group=%d; only 128 is supported", group);
-    if (variant != TQ_TERNARY && variant != TQ_BINARY)
-        return fail(TQ_ERR_VARIANT, "variant=%d is neither TQ_TERNARY (0) nor TQ_BINARY (1)",
-                    variant);
+    if (variant != TQ_TERNARY && variant != TQ_BINARY && variant != TQ_TERNARY5)
+        return fail(TQ_ERR_VARIANT,
+                    "variant=%d is not TQ_TERNARY (0), TQ_BINARY (1) or TQ_TERNARY5 (2)", variant);
     return TQ_OK;
 }
+
+// Bytes of one row of five-trit codes: 26 per group, padded to 16.
+inline int64_t ternary5_row_bytes(int64_t K) { return (26 * (K / kGroup) + 15) / 16 * 16; }
 
 inline bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 

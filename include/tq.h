@@ -57,20 +57,33 @@ extern "C" {
 /* weight variants */
 #define TQ_TERNARY 0 /* t in {-1,0,+1}, 2-bit slots, 2.125 bits/weight stored */
 #define TQ_BINARY 1  /* t in {-1,+1},   1-bit slots, 1.125 bits/weight stored */
+/* t in {-1,0,+1} stored five trits to a byte: the native ternary packing
+ * the model card names as the step after 2-bit slots (aitrends.kr,
+ * "Ternary-Bonsai-27B-mlx-2bit", "Technical features"; 3^5 = 243 <= 256).
+ * Byte b (0..25) of a 128-weight group holds trits 5b..5b+4 of the group as
+ * sum_i (t_{5b+i} + 1) * 3^i, least significant digit first; byte 25 holds
+ * trits 125..127 and its digits 3 and 4 are 0.  A row is its K/128 groups
+ * of 26 bytes followed by zero bytes up to a multiple of 16, so rows stay
+ * 16-byte aligned: 1.75 bits/weight stored (with the scale) when K is a
+ * multiple of 1024.  Supported by tq_codes_bytes, tq_pack, tq_unpack,
+ * tq_gemv and tq_gemm with M == 1 (K <= 40960); other entry points return
+ * TQ_ERR_VARIANT. */
+#define TQ_TERNARY5 2
 
 /* status codes */
 #define TQ_OK 0
 #define TQ_ERR_NULL 1    /* a required pointer is NULL                          */
 #define TQ_ERR_SHAPE 2   /* M or N < 1, K < 128, K % 128 != 0, or too large     */
 #define TQ_ERR_GROUP 3   /* group != 128                                         */
-#define TQ_ERR_VARIANT 4 /* variant is neither TQ_TERNARY nor TQ_BINARY         */
+#define TQ_ERR_VARIANT 4 /* unknown variant, or one the entry point does not take */
 #define TQ_ERR_VALUE 5   /* tq_pack: a t outside the variant's set              */
-#define TQ_ERR_CODE 6    /* tq_unpack: a ternary code 3                          */
+#define TQ_ERR_CODE 6    /* tq_unpack: a ternary code 3 or a bad five-trit byte  */
 #define TQ_ERR_ALIGN 7   /* a device pointer is not aligned as required          */
 #define TQ_ERR_HIP 8     /* the HIP runtime rejected a launch                    */
 
-/* Size of the packed code array: N*K/4 bytes (ternary) or N*K/8 (binary).
- * Returns 0 for an invalid shape or variant. */
+/* Size of the packed code array: N*K/4 bytes (ternary), N*K/8 (binary) or
+ * N * roundup(26*K/128, 16) (five-trit bytes).  Returns 0 for an invalid
+ * shape or variant. */
 size_t tq_codes_bytes(int64_t N, int64_t K, int32_t variant);
 
 /* Number of FP16 scales: N*K/group.  Returns 0 for an invalid shape/group. */
@@ -86,7 +99,9 @@ int32_t tq_pack(const int8_t *t, int64_t N, int64_t K, int32_t group,
 
 /* Host -> host.  Inverse of tq_pack: writes t (int8 [N][K]).  A ternary
  * code 3 returns TQ_ERR_CODE; tq_last_error_index() gives the flat weight
- * index of the first such slot. */
+ * index of the first such slot.  TQ_TERNARY5: a byte >= 243, or a last byte
+ * of a group >= 27, returns TQ_ERR_CODE with the flat index of the byte's
+ * first trit; padding bytes are not read. */
 int32_t tq_unpack(const uint8_t *codes, int64_t N, int64_t K, int32_t group,
                   int32_t variant, int8_t *t);
 

@@ -51,8 +51,10 @@ FAKE = 0x7f0000000000  # 16-byte aligned address that is never dereferenced
     ((FAKE, FAKE, FAKE, FAKE, 1, 8, 0, 128, 0), 2),
     ((FAKE, FAKE, FAKE, FAKE, 1, 8, 131072, 128, 0), 2),
     ((FAKE, FAKE, FAKE, FAKE, 1, 8, 256, 64, 0), 3),
-    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 256, 128, 2), 4),
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 256, 128, 3), 4),
     ((FAKE + 8, FAKE, FAKE, FAKE, 1, 8, 256, 128, 0), 7),
+    ((FAKE + 8, FAKE, FAKE, FAKE, 1, 8, 256, 128, 2), 7),
+    ((FAKE, FAKE, FAKE, FAKE, 2, 8, 256, 128, 2), 4),       # five-trit bytes: GEMV only
     ((FAKE, FAKE, FAKE + 2, FAKE, 1, 8, 256, 128, 0), 7),
     ((FAKE, FAKE + 1, FAKE, FAKE, 1, 8, 256, 128, 0), 7),
     ((FAKE, FAKE, FAKE, FAKE + 2, 1, 8, 256, 128, 0), 7),
@@ -80,6 +82,7 @@ def test_device_entry_points_validate_on_host(args, status):
     ((FAKE, FAKE, FAKE, FAKE, 4, 8, 200, 128, 0), 2),
     ((FAKE, FAKE, FAKE, FAKE, 4, 8, 256, 64, 0), 3),
     ((FAKE, FAKE, FAKE, FAKE, 4, 8, 256, 128, 3), 4),
+    ((FAKE, FAKE, FAKE, FAKE, 4, 8, 256, 128, 2), 4),       # five-trit tables: not for rows
     ((FAKE + 2, FAKE, FAKE, FAKE, 4, 8, 256, 128, 0), 7),
     ((FAKE, FAKE + 1, FAKE, FAKE, 4, 8, 256, 128, 0), 7),
     ((FAKE, FAKE, FAKE + 2, FAKE, 4, 8, 256, 128, 0), 7),
@@ -119,6 +122,7 @@ def test_pack_errors():
     with pytest.raises(tq.TQError) as e:
         tq.tq_pack(np.zeros((2, 128), np.int8), 3)
     assert e.value.status == 4
+    assert tq.tq_codes_bytes(2, 128, 3) == 0
     L = tq.lib()
     assert L.tq_pack(None, 2, 128, 128, 0, None) == 1
     assert L.tq_pack(t.ctypes.data, 2, 128, 64, 0, t.ctypes.data) == 3

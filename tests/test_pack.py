@@ -7,7 +7,7 @@ import oracle
 from binary_g128_bit_amd import synth
 
 
-@pytest.mark.parametrize("variant", [tq.TQ_TERNARY, tq.TQ_BINARY])
+@pytest.mark.parametrize("variant", [tq.TQ_TERNARY, tq.TQ_BINARY, tq.TQ_TERNARY5])
 @pytest.mark.parametrize("N,K", [(1, 128), (3, 256), (17, 384), (64, 1024), (5, 5120),
                                  (2, 17408), (33, 640)])
 def test_pack_matches_oracle(variant, N, K):
@@ -45,3 +45,42 @@ def test_pack_large_rows_and_extremes():
     for fill in (-1, 1):
         t = np.full((N, K), fill, np.int8)
         assert np.array_equal(tq.tq_pack(t, tq.TQ_BINARY), oracle.pack(t, oracle.BINARY))
+
+
+def test_ternary5_all_bytes_unpack_like_oracle():
+    """Every byte value at every position class of a group (even, odd, the
+    three-trit last byte) and in the second group: same trits, or the same
+    error and index, as the oracle."""
+    K = 256
+    for pos in (0, 1, 24, 25, 26, 51):
+        for b in range(256):
+            row = np.zeros((1, 64), np.uint8)
+            row[0, pos] = b
+            try:
+                ref = oracle.unpack(row, 1, K, oracle.TERNARY5)
+            except oracle.OracleError as e:
+                with pytest.raises(tq.TQError) as me:
+                    tq.tq_unpack(row, 1, K, tq.TQ_TERNARY5)
+                assert me.value.status == 6 and me.value.index == e.index, (pos, b)
+                continue
+            assert np.array_equal(tq.tq_unpack(row, 1, K, tq.TQ_TERNARY5), ref), (pos, b)
+
+
+def test_ternary5_sizes_and_errors():
+    assert tq.tq_codes_bytes(1, 5120, tq.TQ_TERNARY5) == 1040
+    assert tq.tq_codes_bytes(3, 384, tq.TQ_TERNARY5) == 3 * 80
+    assert tq.tq_codes_bytes(248320, 5120, tq.TQ_TERNARY5) == 248320 * 1040
+    t = np.zeros((3, 384), np.int8)
+    t[2, 301] = -2
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_pack(t, tq.TQ_TERNARY5)
+    assert e.value.status == 5 and e.value.index == 2 * 384 + 301
+    with pytest.raises(oracle.OracleError) as eo:
+        oracle.pack(t, oracle.TERNARY5)
+    assert eo.value.index == e.value.index
+    # padding bytes are written as zeros and never read
+    c = tq.tq_pack(np.ones((2, 384), np.int8), tq.TQ_TERNARY5)
+    assert c.shape == (2, 80) and np.all(c[:, 78:] == 0)
+    c[:, 78:] = 0xFF
+    assert np.all(tq.tq_unpack(c, 2, 384, tq.TQ_TERNARY5) == 1)
+
