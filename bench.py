@@ -353,6 +353,44 @@ def binary_and_lm_head(torch, tq, gen, stream):
     return out
 
 
+def ternary5(torch, tq, gen, stream):
+    """Five-trit-per-byte storage on the MLP and head shapes, next to the 2-bit
+    figures: back-to-back launches over >= 1 GiB of rotating copies (graph
+    replays as well).  Codes: bytes uniform over the 243 valid values (the
+    three-trit last byte of a group over 27), i.e. iid uniform trits."""
+    from binary_g128_bit_amd import synth
+    out = {}
+    for name, (N, K) in (("gate_up_34816x5120", (2 * synth.GATE_UP[0], synth.GATE_UP[1])),
+                         ("down_5120x17408", synth.DOWN), ("lm_head_248320x5120", synth.LM_HEAD)):
+        nb = tq.tq_codes_bytes(N, K, tq.TQ_TERNARY5)
+        G = K // 128
+        alg = nb + 2 * N * G
+        copies = max(2, math.ceil((1 << 30) / alg))
+        pool = []
+        for _ in range(copies):
+            c = torch.zeros(N, nb // N, dtype=torch.uint8, device=gen.dev)
+            body = c[:, :26 * G].view(N, G, 26)
+            body[:, :, :25] = torch.randint(0, 243, (N, G, 25), device=gen.dev, generator=gen.gen,
+                                            dtype=torch.int32).to(torch.uint8)
+            body[:, :, 25] = torch.randint(0, 27, (N, G), device=gen.dev, generator=gen.gen,
+                                           dtype=torch.int32).to(torch.uint8)
+            pool.append((c, gen.scales(N, K)))
+        x = gen.act(1, K)[0]
+        y = torch.empty(N, dtype=torch.float32, device=gen.dev)
+
+        def launch(i):
+            return tq.tq_gemv(pool[i % copies][0], pool[i % copies][1], x, y, variant=tq.TQ_TERNARY5)
+
+        ms = back_to_back_ms(torch, stream, launch, 100 if N < 100000 else 30)
+        msg = graph_ms(torch, launch, 4 * copies)
+        out[name] = {"us": round(ms * 1e3, 2), "us_graph": round(msg * 1e3, 2),
+                     "gbs": round(alg / ms / 1e6, 1), "frac_hbm": round(alg / ms / 1e6 / PEAK_HBM_GBS, 4),
+                     "gweights_s": round(N * K / ms / 1e6, 1), "bytes": alg}
+        del pool
+        torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration():
     import torch
     dev = torch.device("cuda:0")
@@ -500,6 +538,7 @@ def main():
         gen = Dev(torch, tq, dev, 12345)
         line["gemm"] = gemm_widths(torch, tq, gen, stream, bufs, slots)
         line["binary_and_lm_head"] = binary_and_lm_head(torch, tq, gen, stream)
+        line["ternary5"] = ternary5(torch, tq, gen, stream)
         del bufs
         torch.cuda.empty_cache()
         line["stack_sweep"] = stack_sweep(torch, tq, gen, stream)

@@ -121,17 +121,28 @@ __device__ __forceinline__ void bytes_dot(const uint32_t (&cd)[RPL][kUnitDw], co
         X[4 * q + 2] = v[2];
         X[4 * q + 3] = v[3];
     }
+    // every lookup of the span is issued before the first use, so the LDS
+    // latency is paid once per span rather than once per byte
+    u32x4 E[RPL][B1 - B0];
 #pragma unroll
     for (int b = B0; b < B1; ++b) {
         const int q = 26 * H + b;
         // result bytes: [base.b0, code byte, base.b2, 0]
         constexpr uint32_t kSelHi = 0x0C020000u;
         const uint32_t sel = kSelHi | ((uint32_t)(4 + (q & 3)) << 8);
-        const int x0 = ((b & 1) ? (5 * b - 1) / 2 : 5 * b / 2) - P0;
 #pragma unroll
         for (int r = 0; r < RPL; ++r) {
             const uint32_t ad = __builtin_amdgcn_perm(cd[r][q >> 2], (b & 1) ? lo : le, sel);
-            const u32x4 e = *reinterpret_cast<const u32x4 *>(lut + ad);
+            E[r][b - B0] = *reinterpret_cast<const u32x4 *>(lut + ad);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int b = B0; b < B1; ++b) {
+        const int x0 = ((b & 1) ? (5 * b - 1) / 2 : 5 * b / 2) - P0;
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const u32x4 e = E[r][b - B0];
             a[r] = dot2(e[0], X[x0], a[r]);
             a[r] = dot2(e[1], X[x0 + 1], a[r]);
             if (b != 25) a[r] = dot2(e[2], X[x0 + 2], a[r]);
@@ -143,9 +154,13 @@ template <int H, int RPL>
 __device__ __forceinline__ void group_dot(const uint32_t (&cd)[RPL][kUnitDw], const uint32_t *xg,
                                           const char *lut, uint32_t le, uint32_t lo,
                                           float (&a)[RPL]) {
-    bytes_dot<H, 0, 13, RPL>(cd, xg, lut, le, lo, a);
+    bytes_dot<H, 0, 7, RPL>(cd, xg, lut, le, lo, a);
     __builtin_amdgcn_sched_barrier(0);
-    bytes_dot<H, 13, 26, RPL>(cd, xg, lut, le, lo, a);
+    bytes_dot<H, 7, 13, RPL>(cd, xg, lut, le, lo, a);
+    __builtin_amdgcn_sched_barrier(0);
+    bytes_dot<H, 13, 20, RPL>(cd, xg, lut, le, lo, a);
+    __builtin_amdgcn_sched_barrier(0);
+    bytes_dot<H, 20, 26, RPL>(cd, xg, lut, le, lo, a);
 }
 
 __device__ __forceinline__ float half_f(uint32_t bits) {
