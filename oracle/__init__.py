@@ -8,6 +8,6 @@ The arithmetic lives in ``tq_oracle.c`` (plain C, built with gcc).  This module
 only builds that file and marshals numpy arrays through ctypes.
 """
 from .oracle import (  # noqa: F401
-    TERNARY, BINARY, TERNARY5, OracleError, build, load, half_to_double, codes_bytes,
-    scales_count, pack, unpack, gemm, gemv, embed, default_threads,
+    TERNARY, BINARY, TERNARY5, AFFINE2, OracleError, build, load, half_to_double, codes_bytes,
+    scales_count, pack, unpack, gemm, gemv, embed, affine_gemm, default_threads,
 )

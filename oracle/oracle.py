@@ -13,6 +13,7 @@ import numpy as np
 TERNARY = 0
 BINARY = 1
 TERNARY5 = 2  # five trits per byte, 26 bytes per group, rows padded to 16 bytes
+AFFINE2 = 3   # unsigned 2-bit level q per weight, FP16 scale and bias per group
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "tq_oracle.c")
@@ -70,6 +71,8 @@ def load(lib_path=_LIB):
     lib.oracle_gemm.restype = ci
     lib.oracle_embed.argtypes = [vp, vp, vp, i64, i64, i64, i32, ci, vp]
     lib.oracle_embed.restype = ci
+    lib.oracle_affine_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp, ci]
+    lib.oracle_affine_gemm.restype = ci
     _lib_cache[lib_path] = lib
     return lib
 
@@ -168,4 +171,27 @@ def embed(codes, scales, ids, N, K, variant=TERNARY, group=128, lib=None):
     if rc:
         raise OracleError(rc)
     return out
+
+
+def _bits(a):
+    a = np.ascontiguousarray(a)
+    return a.view(np.uint16) if a.dtype == np.float16 else a.astype(np.uint16)
+
+
+def affine_gemm(codes, scales, biases, X, N, K, group=128, threads=1, lib=None):
+    """Y[M][N], A[M][N] float64 for the affine 2-bit weights w = s * q + b."""
+    lib = lib or load()
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    s, b = _bits(scales), _bits(biases)
+    X = _bits(X)
+    if X.ndim == 1:
+        X = X.reshape(1, -1)
+    M = X.shape[0]
+    Y = np.empty((M, N), dtype=np.float64)
+    A = np.empty((M, N), dtype=np.float64)
+    rc = lib.oracle_affine_gemm(_ptr(codes), _ptr(s), _ptr(b), _ptr(X), M, N, K, group,
+                                _ptr(Y), _ptr(A), int(threads))
+    if rc:
+        raise OracleError(rc)
+    return Y, A
 

@@ -35,7 +35,13 @@
  *       number sum_i (t_{5b+i} + 1) * 3^i (least significant digit first,
  *       like the 2-bit slots); byte 25 holds trits 125..127 and its digits
  *       3 and 4 are 0.  A row's G groups are consecutive and the row is
- *       padded with zero bytes to a multiple of 16 bytes.
+ *       padded with zero bytes to a multiple of 16 bytes;
+ *   R8  affine 2-bit storage (the MLX packaging keeps a scale and a bias per
+ *       group, aitrends.kr, "Ternary-Bonsai-27B-mlx-2bit", "Technical
+ *       features"): an unsigned level q in {0,1,2,3} per weight in the 2-bit
+ *       slots of R3, and per group an FP16 scale s_g and FP16 bias b_g with
+ *       w = s_g * q + b_g.  Ternary weights are the case q = t + 1,
+ *       b_g = -s_g.  pack / unpack take and return q itself.
  *
  * The product is the plain definition, evaluated in fp64:
  *   Y[m][n] = sum_g s[n][g] * ( sum_{j<128} t[n][128g+j] * X[m][128g+j] )
@@ -51,7 +57,7 @@
 
 enum { OR_OK = 0, OR_ERR_NULL = 1, OR_ERR_SHAPE = 2, OR_ERR_GROUP = 3,
        OR_ERR_VARIANT = 4, OR_ERR_VALUE = 5, OR_ERR_CODE = 6, OR_ERR_NOMEM = 7 };
-enum { OR_TERNARY = 0, OR_BINARY = 1, OR_TERNARY5 = 2 };
+enum { OR_TERNARY = 0, OR_BINARY = 1, OR_TERNARY5 = 2, OR_AFFINE2 = 3 };
 
 /* R7: bytes of one row of five-trit codes (26 per group, padded to 16). */
 static int64_t ternary5_row_bytes(int64_t K)
@@ -82,7 +88,7 @@ double oracle_half_to_double(uint16_t h)
  * 8 per byte (binary). */
 int64_t oracle_codes_bytes(int64_t N, int64_t K, int variant)
 {
-    if (variant == OR_TERNARY) return N * K / 4;
+    if (variant == OR_TERNARY || variant == OR_AFFINE2) return N * K / 4;
     if (variant == OR_BINARY) return N * K / 8;
     if (variant == OR_TERNARY5) return N * ternary5_row_bytes(K);
     return -1;
@@ -98,7 +104,8 @@ static int check_args(int64_t N, int64_t K, int32_t group, int variant)
 {
     if (group != 128) return OR_ERR_GROUP;
     if (N < 1 || K < 128 || K % 128 != 0) return OR_ERR_SHAPE;
-    if (variant != OR_TERNARY && variant != OR_BINARY && variant != OR_TERNARY5)
+    if (variant != OR_TERNARY && variant != OR_BINARY && variant != OR_TERNARY5 &&
+        variant != OR_AFFINE2)
         return OR_ERR_VARIANT;
     return OR_OK;
 }
@@ -115,7 +122,9 @@ int oracle_pack(const int8_t *t, int64_t N, int64_t K, int32_t group,
     int64_t nbytes = oracle_codes_bytes(N, K, variant);
     for (int64_t i = 0; i < N * K; i++) {
         int v = t[i];
-        int ok = (variant == OR_BINARY) ? (v == -1 || v == 1) : (v >= -1 && v <= 1);
+        int ok = (variant == OR_BINARY)    ? (v == -1 || v == 1)
+                 : (variant == OR_AFFINE2) ? (v >= 0 && v <= 3)
+                                           : (v >= -1 && v <= 1);
         if (!ok) {
             if (bad) *bad = i;
             return OR_ERR_VALUE;
@@ -139,7 +148,10 @@ int oracle_pack(const int8_t *t, int64_t N, int64_t K, int32_t group,
     for (int64_t n = 0; n < N; n++) {
         for (int64_t k = 0; k < K; k++) {
             int v = t[n * K + k];
-            if (variant == OR_TERNARY) {
+            if (variant == OR_AFFINE2) {
+                int64_t byte = n * (K / 4) + k / 4;             /* R8, R3 */
+                codes[byte] |= (uint8_t)(v << (2 * (k % 4)));
+            } else if (variant == OR_TERNARY) {
                 int c = v + 1;                                  /* R2 */
                 int64_t byte = n * (K / 4) + k / 4;             /* R3 */
                 codes[byte] |= (uint8_t)(c << (2 * (k % 4)));
@@ -188,7 +200,10 @@ int oracle_unpack(const uint8_t *codes, int64_t N, int64_t K, int32_t group,
     }
     for (int64_t n = 0; n < N; n++) {
         for (int64_t k = 0; k < K; k++) {
-            if (variant == OR_TERNARY) {
+            if (variant == OR_AFFINE2) {
+                uint8_t byte = codes[n * (K / 4) + k / 4];
+                t[n * K + k] = (int8_t)((byte >> (2 * (k % 4))) & 3);
+            } else if (variant == OR_TERNARY) {
                 uint8_t byte = codes[n * (K / 4) + k / 4];
                 int c = (byte >> (2 * (k % 4))) & 3;
                 if (c == 3) {
@@ -217,6 +232,7 @@ int oracle_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
     if (!codes || !scales || !X || !Y) return OR_ERR_NULL;
     int rc = check_args(N, K, group, variant);
     if (rc) return rc;
+    if (variant == OR_AFFINE2) return OR_ERR_VARIANT;   /* needs biases: oracle_affine_gemm */
     if (M < 1) return OR_ERR_SHAPE;
     int64_t G = K / group;
     int64_t row_bytes = oracle_codes_bytes(1, K, variant);
@@ -281,6 +297,7 @@ int oracle_embed(const uint8_t *codes, const uint16_t *scales, const int32_t *id
     if (!codes || !scales || !ids || !out) return OR_ERR_NULL;
     int rc = check_args(N, K, group, variant);
     if (rc) return rc;
+    if (variant == OR_AFFINE2) return OR_ERR_VARIANT;
     if (n < 0) return OR_ERR_SHAPE;
     int64_t G = K / group;
     int64_t row_bytes = oracle_codes_bytes(1, K, variant);
@@ -303,5 +320,55 @@ int oracle_embed(const uint8_t *codes, const uint16_t *scales, const int32_t *id
     }
     free(t);
     return OR_OK;
+}
+
+/* Affine 2-bit product (R8): Y[m][n] = sum_k (s[n][g] * q[n][k] + b[n][g]) *
+ * X[m][k], g = k / group, with the weight formed per element in fp64 as the
+ * definition states.  A[m][n] = sum_g (|s| * sum_j |q * x| + |b| * sum_j |x|)
+ * bounds the magnitude of the terms a kernel that applies the scale and the
+ * bias per group (s * sum q x + b * sum x) adds up. */
+int oracle_affine_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                       const uint16_t *X, int64_t M, int64_t N, int64_t K, int32_t group,
+                       double *Y, double *A, int threads)
+{
+    if (!codes || !scales || !biases || !X || !Y) return OR_ERR_NULL;
+    int rc = check_args(N, K, group, OR_AFFINE2);
+    if (rc) return rc;
+    if (M < 1) return OR_ERR_SHAPE;
+    int64_t G = K / group;
+    double *x = (double *)malloc((size_t)(M * K) * sizeof(double));
+    if (!x) return OR_ERR_NOMEM;
+    for (int64_t i = 0; i < M * K; i++) x[i] = oracle_half_to_double(X[i]);
+    int status = OR_OK;
+    if (threads < 1) threads = 1;
+#pragma omp parallel num_threads(threads)
+    {
+        int8_t *q = (int8_t *)malloc((size_t)K);
+        if (!q) {
+#pragma omp atomic write
+            status = OR_ERR_NOMEM;
+        }
+#pragma omp for schedule(static)
+        for (int64_t n = 0; n < N; n++) {
+            if (!q) continue;
+            int64_t badi = 0;
+            oracle_unpack(codes + n * (K / 4), 1, K, group, OR_AFFINE2, q, &badi);
+            for (int64_t m = 0; m < M; m++) {
+                double acc = 0.0, bound = 0.0;
+                for (int64_t k = 0; k < K; k++) {
+                    double sg = oracle_half_to_double(scales[n * G + k / group]);
+                    double bg = oracle_half_to_double(biases[n * G + k / group]);
+                    double w = sg * (double)q[k] + bg;
+                    acc += w * x[m * K + k];
+                    bound += fabs(sg) * fabs((double)q[k] * x[m * K + k]) + fabs(bg) * fabs(x[m * K + k]);
+                }
+                Y[m * N + n] = acc;
+                if (A) A[m * N + n] = bound;
+            }
+        }
+        free(q);
+    }
+    free(x);
+    return status;
 }
 

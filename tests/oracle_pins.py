@@ -282,7 +282,7 @@ def check_errors(lib):
         except oracle.OracleError as e:
             assert e.code == 5 and e.index == idx, (e.code, e.index)
     for N, K, group, variant, code in ((2, 100, 128, 0, 2), (2, 192, 128, 0, 2), (0, 128, 128, 0, 2),
-                                       (2, 128, 64, 0, 3), (2, 128, 128, 3, 4)):
+                                       (2, 128, 64, 0, 3), (2, 128, 128, 4, 4)):
         rc = lib.oracle_pack(t.ctypes.data, N, K, group, variant,
                              np.zeros(64, np.uint8).ctypes.data, None)
         assert rc == code, (N, K, group, variant, rc)
@@ -319,7 +319,82 @@ def check_embed(lib):
                 assert e.code == 2, e.code
 
 
+# ------------------------------------------------------------- affine 2-bit
+def _affine_dense(q, s, b):
+    """W[n][k] = s[n][k/128] * q[n][k] + b[n][k/128] from the inputs."""
+    s64 = np.repeat(np.asarray(s, np.float16).astype(np.float64), 128, axis=1)
+    b64 = np.repeat(np.asarray(b, np.float16).astype(np.float64), 128, axis=1)
+    return s64 * q.astype(np.float64) + b64
+
+
+def check_affine(lib):
+    ex = _golden("layout_examples.json")["affine2_row"]
+    q = np.full((1, ex["K"]), ex["q_rest"], np.int8)
+    q[0, :len(ex["q_prefix"])] = ex["q_prefix"]
+    codes = oracle.pack(q, oracle.AFFINE2, lib=lib)[0]
+    pre = [int(h, 16) for h in ex["bytes_prefix_hex"]]
+    assert list(codes[:len(pre)]) == pre, list(codes[:4])
+    assert all(int(v) == int(ex["byte_rest_hex"], 16) for v in codes[len(pre):])
+    # every byte is valid and round-trips
+    allb = np.arange(256, dtype=np.uint8).reshape(8, 32)
+    qa = oracle.unpack(allb, 8, 128, oracle.AFFINE2, lib=lib)
+    assert qa.min() == 0 and qa.max() == 3
+    assert np.array_equal(oracle.pack(qa, oracle.AFFINE2, lib=lib), allb)
+    # worked example
+    w = ex["worked"]
+    s = np.full((1, 1), w["scale"], np.float16)
+    b = np.full((1, 1), w["bias"], np.float16)
+    qq = np.zeros((1, 128), np.int8)
+    qq[0, :4] = [0, 1, 2, 3]
+    x = np.zeros(128, np.float16)
+    x[:4] = 1
+    Y, _ = oracle.affine_gemm(oracle.pack(qq, oracle.AFFINE2, lib=lib), s, b, x, 1, 128, lib=lib)
+    assert Y[0, 0] == w["y"], Y
+    g = synth.rng(29)
+    N, K, M = 6, 384, 3
+    qr = g.integers(0, 4, size=(N, K)).astype(np.int8)
+    s = synth.scales(g, N, K)
+    b = (-synth.scales(g, N, K).astype(np.float32) * 1.5).astype(np.float16)
+    s[0, 1] = -s[0, 1]
+    b[2, 0] = np.float16(2.0 ** -21)
+    X = synth.activations(g, M, K)
+    c = oracle.pack(qr, oracle.AFFINE2, lib=lib)
+    Y, A = oracle.affine_gemm(c, s, b, X, N, K, lib=lib)
+    W = _affine_dense(qr, s, b)
+    ref = X.astype(np.float64) @ W.T
+    assert np.all(np.abs(Y - ref) <= 1e-12 * A), np.abs(Y - ref).max()
+    refA = (np.abs(X.astype(np.float64)) @ (np.abs(np.repeat(s.astype(np.float64), 128, 1)) * qr).T
+            + np.abs(X.astype(np.float64)) @ np.abs(np.repeat(b.astype(np.float64), 128, 1)).T)
+    assert np.allclose(A, refA, rtol=1e-12, atol=0)
+    # one-hot x: y = s * q_k + b exactly
+    for k in (0, 5, 127, 128, 300, 383):
+        x = np.zeros(K, np.float16)
+        x[k] = 1
+        y, _ = oracle.affine_gemm(c, s, b, x, N, K, lib=lib)
+        exact = s[:, k // 128].astype(np.float64) * qr[:, k] + b[:, k // 128].astype(np.float64)
+        assert np.array_equal(y[0], exact), k
+    # q = 0: y = sum_g b_g * sum x_g
+    z = oracle.pack(np.zeros((N, K), np.int8), oracle.AFFINE2, lib=lib)
+    y, _ = oracle.affine_gemm(z, s, b, X[0], N, K, lib=lib)
+    xg = X[0].astype(np.float64).reshape(-1, 128).sum(axis=1)
+    assert np.allclose(y[0], b.astype(np.float64) @ xg, rtol=1e-13, atol=0)
+    # ternary weights are the case q = t + 1, b = -s: the ternary product
+    t = synth.trits(g, N, K)
+    Yt, At = oracle.gemm(oracle.pack(t, lib=lib), s, X, N, K, lib=lib)
+    Ya, _ = oracle.affine_gemm(oracle.pack((t + 1).astype(np.int8), oracle.AFFINE2, lib=lib), s,
+                               -s, X, N, K, lib=lib)
+    assert np.all(np.abs(Ya - Yt) <= 1e-12 * At + 1e-300)
+    # the bias-free entry points refuse the affine variant
+    for call in (lambda: oracle.gemm(c, s, X, N, K, oracle.AFFINE2, lib=lib),
+                 lambda: oracle.embed(c, s, np.zeros(1, np.int32), N, K, oracle.AFFINE2, lib=lib)):
+        try:
+            call()
+            raise AssertionError("affine accepted without biases")
+        except oracle.OracleError as e:
+            assert e.code == 4
+
+
 ALL_CHECKS = [check_half_decode, check_byte_counts, check_roundtrip_bytes,
               check_golden_layout, check_worked_gemv, check_bruteforce_numpy,
               check_exact_integer, check_special_cases, check_bound, check_errors,
-              check_embed, check_golden_ternary5]
+              check_embed, check_golden_ternary5, check_affine]

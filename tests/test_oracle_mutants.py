@@ -42,6 +42,12 @@ MUTANTS = [
     ("t5_no_row_padding", [("return (raw + 15) / 16 * 16;", "return raw;")]),
     ("t5_tail_digits_unchecked", [("else if (c != 0)", "else if (c > 2)")]),
     ("t5_range_unchecked", [("if (value != 0) {", "if (value > 1) {")]),
+    ("affine_bias_dropped", [("double w = sg * (double)q[k] + bg;", "double w = sg * (double)q[k];")]),
+    ("affine_bias_group", [("double bg = oracle_half_to_double(biases[n * G + k / group]);",
+                            "double bg = oracle_half_to_double(biases[n * G]);")]),
+    ("affine_level_mask", [("t[n * K + k] = (int8_t)((byte >> (2 * (k % 4))) & 3);",
+                            "t[n * K + k] = (int8_t)((byte >> (2 * (k % 4))) & 1);")]),
+    ("affine_bound_bias", [("+ fabs(bg) * fabs(x[m * K + k]);", ";")]),
     ("t5_code_map", [("t[n * K + 128 * g + 5 * b + i] = (int8_t)(c - 1);",
                       "t[n * K + 128 * g + 5 * b + i] = (int8_t)(1 - c);"),
                      ("value += (t[n * K + 128 * g + 5 * b + i] + 1) * power;",
