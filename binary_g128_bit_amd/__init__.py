@@ -17,6 +17,7 @@ import numpy as np
 TQ_TERNARY = 0
 TQ_BINARY = 1
 TQ_TERNARY5 = 2  # five trits per byte (GEMV only)
+TQ_AFFINE2 = 3   # levels q in {0..3}, scale and bias per group (tq_gemv_affine)
 GROUP = 128
 
 _STATUS = {0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_GROUP",
@@ -27,7 +28,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 
 # every symbol include/tq.h declares
 EXPORTS = ("tq_codes_bytes", "tq_scales_count", "tq_pack", "tq_unpack", "tq_gemv", "tq_gemm",
-           "tq_embed", "tq_last_error", "tq_last_error_index", "tq_version")
+           "tq_embed", "tq_gemv_affine", "tq_last_error", "tq_last_error_index", "tq_version")
 
 
 class TQError(RuntimeError):
@@ -67,6 +68,8 @@ def lib():
     L.tq_gemm.restype = i32
     L.tq_embed.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
     L.tq_embed.restype = i32
+    L.tq_gemv_affine.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp]
+    L.tq_gemv_affine.restype = i32
     L.tq_last_error.argtypes = []
     L.tq_last_error.restype = ctypes.c_char_p
     L.tq_last_error_index.argtypes = []
@@ -194,4 +197,21 @@ def tq_embed(codes, scales, ids, out=None, variant=TQ_TERNARY, group=GROUP, stre
                           _dev(ids, "ids", (torch.int32,)), _dev(out, "out", half), n_ids, N, K,
                           group, variant, _stream(stream)))
     return out
+
+
+def tq_gemv_affine(codes, scales, biases, x, y=None, group=GROUP, stream=None):
+    """y[N] = W x with w = s * q + b (affine 2-bit levels) on the current
+    stream.  codes uint8 [N][K/4], scales / biases float16 [N][K/128]."""
+    import torch
+    K = x.shape[-1]
+    N = _shape_checks(codes, scales, K, TQ_AFFINE2)
+    if tuple(biases.shape) != tuple(scales.shape):
+        raise ValueError("biases must have the shape of scales")
+    if y is None:
+        y = torch.empty(N, dtype=torch.float32, device=x.device)
+    half = (torch.float16, torch.int16)
+    _check(lib().tq_gemv_affine(_dev(codes, "codes", (torch.uint8,)), _dev(scales, "scales", half),
+                                _dev(biases, "biases", half), _dev(x, "x", half),
+                                _dev(y, "y", (torch.float32,)), N, K, group, _stream(stream)))
+    return y
 

@@ -14,6 +14,8 @@ int32_t gemm_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_
                      int64_t M, int64_t N, int64_t K, int32_t variant, hipStream_t stream);
 int32_t gemv5_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
                       int64_t N, int64_t K, hipStream_t stream);
+int32_t gemv_affine_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                            const uint16_t *x, float *y, int64_t N, int64_t K, hipStream_t stream);
 int32_t embed_enqueue(const uint8_t *codes, const uint16_t *scales, const int32_t *ids,
                       uint16_t *out, int64_t n_ids, int64_t N, int64_t K, int32_t variant,
                       hipStream_t stream);
@@ -38,6 +40,8 @@ int32_t tq_gemv(const uint8_t *codes, const uint16_t *scales, const uint16_t *x,
                 int64_t N, int64_t K, int32_t group, int32_t variant, void *stream) {
     tq::clear_error();
     if (int32_t rc = tq::check_device_args(codes, scales, x, y, 1, N, K, group, variant)) return rc;
+    if (variant == TQ_AFFINE2)
+        return tq::fail(TQ_ERR_VARIANT, "TQ_AFFINE2 weights need biases: use tq_gemv_affine");
     if (variant == TQ_TERNARY5)
         return tq::gemv5_enqueue(codes, scales, x, y, N, K, static_cast<hipStream_t>(stream));
     return tq::gemv_enqueue(codes, scales, x, y, N, K, variant,
@@ -48,6 +52,8 @@ int32_t tq_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
                 int64_t M, int64_t N, int64_t K, int32_t group, int32_t variant, void *stream) {
     tq::clear_error();
     if (int32_t rc = tq::check_device_args(codes, scales, X, Y, M, N, K, group, variant)) return rc;
+    if (variant == TQ_AFFINE2)
+        return tq::fail(TQ_ERR_VARIANT, "TQ_AFFINE2 weights need biases: use tq_gemv_affine");
     if (variant == TQ_TERNARY5) {
         if (M != 1)
             return tq::fail(TQ_ERR_VARIANT, "TQ_TERNARY5 has a GEMV only (M = 1), got M=%lld",
@@ -66,7 +72,7 @@ int32_t tq_embed(const uint8_t *codes, const uint16_t *scales, const int32_t *id
                  void *stream) {
     tq::clear_error();
     if (int32_t rc = tq::check_shape(1, N, K, group, variant)) return rc;
-    if (variant == TQ_TERNARY5)
+    if (variant == TQ_TERNARY5 || variant == TQ_AFFINE2)
         return tq::fail(TQ_ERR_VARIANT, "tq_embed takes TQ_TERNARY or TQ_BINARY tables");
     if (n_ids < 0 || n_ids > tq::kMaxN)
         return tq::fail(TQ_ERR_SHAPE, "n_ids=%lld outside [0, 2^31)", (long long)n_ids);
@@ -78,6 +84,18 @@ int32_t tq_embed(const uint8_t *codes, const uint16_t *scales, const int32_t *id
     if (!tq::aligned(out, 16)) return tq::fail(TQ_ERR_ALIGN, "output must be 16-byte aligned");
     return tq::embed_enqueue(codes, scales, ids, out, n_ids, N, K, variant,
                              static_cast<hipStream_t>(stream));
+}
+
+int32_t tq_gemv_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                       const uint16_t *x, float *y, int64_t N, int64_t K, int32_t group,
+                       void *stream) {
+    tq::clear_error();
+    if (!biases) return tq::fail(TQ_ERR_NULL, "NULL pointer argument");
+    if (int32_t rc = tq::check_device_args(codes, scales, x, y, 1, N, K, group, TQ_AFFINE2))
+        return rc;
+    if (!tq::aligned(biases, 2)) return tq::fail(TQ_ERR_ALIGN, "biases must be 2-byte aligned");
+    return tq::gemv_affine_enqueue(codes, scales, biases, x, y, N, K,
+                                   static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

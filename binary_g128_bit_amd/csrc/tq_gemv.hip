@@ -57,11 +57,12 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 // Masks used with v_and_or_b32 stay in VGPRs: gfx9 VOP3 encodings take no
 // literal and read one SGPR at most, which then holds the exponent constant.
 struct Masks {
-    uint32_t m8, m6, b10, b9, b8, b7, b6;
+    uint32_t m8, m6, m4, b10, b9, b8, b7, b6;
     __device__ __forceinline__ Masks()
-        : m8(0x03000300u), m6(0x00C000C0u), b10(0x04000400u), b9(0x02000200u), b8(0x01000100u),
-          b7(0x00800080u), b6(0x00400040u) {
+        : m8(0x03000300u), m6(0x00C000C0u), m4(0x00300030u), b10(0x04000400u), b9(0x02000200u),
+          b8(0x01000100u), b7(0x00800080u), b6(0x00400040u) {
         asm volatile("" : "+v"(m8));
+        asm volatile("" : "+v"(m4));
         asm volatile("" : "+v"(m6));
         asm volatile("" : "+v"(b10));
         asm volatile("" : "+v"(b9));
@@ -93,6 +94,31 @@ __device__ __forceinline__ void tern_acc32(uint32_t d0, uint32_t d1, const uint3
         a = dot2((c6 & k.m6) | 0x14001400u, xp[0], a);     // M16 slot 0
         a = dot2(r4 & 0x0C000C00u, xp[7], a);              // E   slot 7
         a = dot2((r4 & k.m8) | 0x0C000C00u, xp[6], a);     // M4  slot 6
+    }
+}
+
+// 32 affine levels q in {0..3} (dwords d0, d1) against pairs xp[p] =
+// (x[p], x[p+8]), accumulated into a in units of 2^-14.  Level 3 rules out the
+// E slot (exponent field 3 is 4 units, not 3), so three mantissa slots serve
+// a copy: M4 at bits [8,10) (exponent 3, 2^-12 + q 2^-14), M16 at [6,8)
+// (exponent 5, 2^-10 + q 2^-14) and M64 at [4,6) (exponent 7, 2^-8 + q 2^-14).
+// Copies d (slots 4, 3, 2), d << 6 (1, 0) and d >> 6 (7, 6, 5).
+__device__ __forceinline__ void aff_acc32(uint32_t d0, uint32_t d1, const uint32_t *xp0,
+                                          const uint32_t *xp1, float &a, const Masks &k) {
+    const uint32_t dd[2] = {d0, d1};
+    const uint32_t *xps[2] = {xp0, xp1};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t *xp = xps[h];
+        const uint32_t c0 = dd[h], c6 = dd[h] << 6, r6 = dd[h] >> 6;
+        a = dot2((c0 & k.m8) | 0x0C000C00u, xp[4], a);     // M4  slot 4
+        a = dot2((c0 & k.m6) | 0x14001400u, xp[3], a);     // M16 slot 3
+        a = dot2((c0 & k.m4) | 0x1C001C00u, xp[2], a);     // M64 slot 2
+        a = dot2((c6 & k.m8) | 0x0C000C00u, xp[1], a);     // M4  slot 1
+        a = dot2((c6 & k.m6) | 0x14001400u, xp[0], a);     // M16 slot 0
+        a = dot2((r6 & k.m8) | 0x0C000C00u, xp[7], a);     // M4  slot 7
+        a = dot2((r6 & k.m6) | 0x14001400u, xp[6], a);     // M16 slot 6
+        a = dot2((r6 & k.m4) | 0x1C001C00u, xp[5], a);     // M64 slot 5
     }
 }
 
@@ -150,7 +176,7 @@ __device__ __forceinline__ float seg_sum(float v) {
 // ragged row shape) hold zeros, which makes their contribution exactly 0.
 template <int VARIANT>
 struct XUnit {
-    static constexpr int UNIT = VARIANT == TQ_TERNARY ? 16 : 32;
+    static constexpr int UNIT = VARIANT == TQ_BINARY ? 32 : 16;
     static constexpr int PAIRS = 4 * UNIT / 2;        // pair dwords per chunk
     static constexpr int CHUNK_DW = PAIRS + 4;        // 36 or 68: 16-byte aligned, bank-spread
     static constexpr int V4 = UNIT / 8;               // 16-byte loads per unit
@@ -158,7 +184,12 @@ struct XUnit {
 
     // FP16 pair (w, w) weighting pair p in the chunk constant
     static __device__ __forceinline__ uint32_t zweight(int p) {
-        if constexpr (VARIANT == TQ_TERNARY) {
+        if constexpr (VARIANT == TQ_AFFINE2) {
+            // the slot offsets alone (no t = c - 1 shift): M16 slots 0, 3, 6;
+            // M4 slots 1, 4, 7; M64 slots 2, 5
+            return (p == 0 || p == 3 || p == 6) ? 0x4C004C00u : (p == 2 || p == 5) ? 0x54005400u
+                                                                                   : 0x44004400u;  // 16 : 64 : 4
+        } else if constexpr (VARIANT == TQ_TERNARY) {
             // E slots 2, 5, 7; M4 slots 1, 4, 6; M16 slots 0, 3
             return (p == 0 || p == 3) ? 0x4C404C40u : (p == 1 || p == 4 || p == 6) ? 0x45004500u
                                                                                     : 0x3C003C00u;  // 17 : 5 : 1
@@ -208,6 +239,14 @@ struct XUnit {
             reinterpret_cast<u32x4 *>(dst)[i] = u32x4{xp[4 * i], xp[4 * i + 1], xp[4 * i + 2], xp[4 * i + 3]};
         z = seg_sum<4>(z) * -kSeedScale;
         if ((u & 3) == 0) slot[PAIRS] = __builtin_bit_cast(uint32_t, z);
+        if constexpr (VARIANT == TQ_AFFINE2) {
+            // the chunk's plain sum of x, in the accumulator unit, for the bias
+            float zs = 0.0f;
+#pragma unroll
+            for (int i = 0; i < UNIT / 2; ++i) zs = dot2(xp[i], 0x3C003C00u, zs);
+            zs = seg_sum<4>(zs) * kSeedScale;
+            if ((u & 3) == 0) slot[PAIRS + 1] = __builtin_bit_cast(uint32_t, zs);
+        }
     }
 };
 
@@ -259,15 +298,36 @@ __device__ __forceinline__ void chunk_dot(const u32x4 (&c)[RPL], const uint32_t 
                                 acc[r]);
 }
 
-// chunk_dot with the chunk's pairs and constant held in registers (ternary,
-// one row): xr[0..32) are the pairs of the chunk's four units, xr[32] the
-// constant.
-__device__ __forceinline__ void chunk_dot_reg(const u32x4 &c, const uint32_t (&xr)[33], uint32_t sbits,
-                                              float &acc, const Masks &km) {
+// Registers a lane keeps per chunk column: 32 pair dwords and the seed, plus
+// the chunk's sum of x for affine levels.
+template <int VARIANT>
+struct XReg {
+    static constexpr int N = VARIANT == TQ_AFFINE2 ? 34 : 33;
+};
+
+__device__ __forceinline__ float half_bits(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
+// chunk_dot with the chunk's pairs and constants held in registers (one
+// row): xr[0..32) are the pairs of the chunk's four units, xr[32] the seed.
+// Affine levels add the group's bias times xr[33], the chunk's sum of x in
+// the accumulator unit (w = s q + b: s * sum q x + b * sum x).
+template <int VARIANT>
+__device__ __forceinline__ void chunk_dot_reg(const u32x4 &c, const uint32_t (&xr)[XReg<VARIANT>::N],
+                                              uint32_t sbits, uint32_t bbits, float &acc,
+                                              const Masks &km) {
     float a = __builtin_bit_cast(float, xr[32]);
-    tern_acc32(c[0], c[1], xr, xr + 8, a, km);
-    tern_acc32(c[2], c[3], xr + 16, xr + 24, a, km);
-    acc = __builtin_fmaf((float)__builtin_bit_cast(_Float16, (uint16_t)sbits), a, acc);
+    if constexpr (VARIANT == TQ_AFFINE2) {
+        aff_acc32(c[0], c[1], xr, xr + 8, a, km);
+        aff_acc32(c[2], c[3], xr + 16, xr + 24, a, km);
+        acc = __builtin_fmaf(half_bits(sbits), a, acc);
+        acc = __builtin_fmaf(half_bits(bbits), __builtin_bit_cast(float, xr[33]), acc);
+    } else {
+        tern_acc32(c[0], c[1], xr, xr + 8, a, km);
+        tern_acc32(c[2], c[3], xr + 16, xr + 24, a, km);
+        acc = __builtin_fmaf(half_bits(sbits), a, acc);
+    }
 }
 
 // One row block = RPL * 64/LPR consecutive rows handled by one wave: LPR lanes
@@ -282,7 +342,7 @@ __device__ __forceinline__ void load_block(const uint8_t *__restrict__ codes,
                                            const uint16_t *__restrict__ scales, const int (&row)[RPL],
                                            int j, int CPR, int G, u32x4 (&c)[NU][RPL],
                                            uint32_t (&s)[NU][RPL]) {
-    constexpr int CPG = VARIANT == TQ_TERNARY ? 2 : 1;  // 16-byte chunks per group
+    constexpr int CPG = VARIANT == TQ_BINARY ? 1 : 2;  // 16-byte chunks per group
 #pragma unroll
     for (int r = 0; r < RPL; ++r) {
         const uint16_t *sp = scales + (size_t)row[r] * G;
@@ -332,7 +392,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
     constexpr int RB = RS * RPL;                        // rows per block
     constexpr int CAP = LPR * NU;                       // chunk slots per row
     constexpr int XMAX = (CAP * 4 + THREADS - 1) / THREADS;
-    const int G = K >> 7, CPR = G * (VARIANT == TQ_TERNARY ? 2 : 1);
+    const int G = K >> 7, CPR = G * (VARIANT == TQ_BINARY ? 1 : 2);
     const int nunits = CPR * 4;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int seg = lane / LPR, j = lane % LPR;
@@ -400,18 +460,32 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
     }
 }
 
-// Ternary GEMV, one row per lane, with the lane's activations in registers.
-// Lane j of a row segment only ever reads chunk columns j, j + LPR, ..., so
-// after the workgroup has staged x into LDS once (permuted, with the chunk
-// constants), each lane copies its NU chunk slots into VGPRs and the block
-// loop reads no LDS at all.
-template <int LPR, int NU, int WAVES, bool RAGGED>
+// Group biases of a block (affine levels), indexed like the scales in
+// load_block (two chunks per group).
+template <int LPR, int NU, bool RAGGED>
+__device__ __forceinline__ void load_bias(const uint16_t *__restrict__ biases, int row, int j, int CPR,
+                                          int G, uint32_t (&bv)[NU][1]) {
+    const uint16_t *bp = biases + (size_t)row * G;
+#pragma unroll
+    for (int i = 0; i < NU; ++i)
+        bv[i][0] = RAGGED ? bp[min(j + i * LPR, CPR - 1) / 2] : bp[j / 2 + i * (LPR / 2)];
+}
+
+// Ternary (and affine 2-bit) GEMV, one row per lane, with the lane's
+// activations in registers.  Lane j of a row segment only ever reads chunk
+// columns j, j + LPR, ..., so after the workgroup has staged x into LDS once
+// (permuted, with the chunk constants), each lane copies its NU chunk slots
+// into VGPRs and the block loop reads no LDS at all.
+template <int VARIANT, int LPR, int NU, int WAVES, bool RAGGED>
 __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__restrict__ codes,
                                                                const uint16_t *__restrict__ scales,
+                                                               const uint16_t *__restrict__ biases,
                                                                const uint16_t *__restrict__ x,
                                                                float *__restrict__ y, int N, int K) {
     extern __shared__ uint32_t xs[];
-    using XU = XUnit<TQ_TERNARY>;
+    using XU = XUnit<VARIANT>;
+    constexpr bool AFF = VARIANT == TQ_AFFINE2;
+    constexpr int XN = XReg<VARIANT>::N;
     constexpr int THREADS = 64 * WAVES;
     constexpr int RS = 64 / LPR;  // rows per block (one per lane segment)
     constexpr int CAP = LPR * NU;
@@ -432,9 +506,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
     __builtin_amdgcn_sched_barrier(0);
     u32x4 ca[NU][1], cb[NU][1];
     uint32_t sa[NU][1], sb[NU][1];
+    uint32_t ba[NU][1] = {}, bb_[NU][1] = {};
     int b = b_begin + wave;
     int row[1] = {min(min(b, b_end - 1) * RS + seg, N - 1)};
-    load_block<TQ_TERNARY, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, ca, sa);
+    if constexpr (AFF) load_bias<LPR, NU, RAGGED>(biases, row[0], j, CPR, G, ba);
+    load_block<VARIANT, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, ca, sa);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int k = 0; k < XMAX; ++k) {
@@ -442,7 +518,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         xu[k].store(xs, u, u < nunits);
     }
     __syncthreads();
-    uint32_t xr[NU][33];
+    uint32_t xr[NU][XN];
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
         const uint32_t *slot = xs + (j + i * LPR) * XU::CHUNK_DW;
@@ -455,14 +531,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
             xr[i][4 * q + 3] = v[3];
         }
         xr[i][32] = slot[32];
+        if constexpr (AFF) xr[i][33] = slot[33];
     }
 
-    auto block = [&](const u32x4 (&c)[NU][1], const uint32_t (&sv)[NU][1], int bb)
-                     __attribute__((always_inline)) {
+    auto block = [&](const u32x4 (&c)[NU][1], const uint32_t (&sv)[NU][1],
+                     const uint32_t (&bv)[NU][1], int bb) __attribute__((always_inline)) {
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
-            chunk_dot_reg(c[i][0], xr[i], sv[i][0], acc, km);
+            chunk_dot_reg<VARIANT>(c[i][0], xr[i], sv[i][0], bv[i][0], acc, km);
             __builtin_amdgcn_sched_barrier(0);
         }
         const float out = seg_sum<LPR>(acc) * XU::kRowScale;
@@ -473,16 +550,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         const int b2 = b + WAVES;
         if (b2 < b_end) {
             row[0] = b2 * RS + seg < N ? b2 * RS + seg : N - 1;
-            load_block<TQ_TERNARY, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, cb, sb);
+            if constexpr (AFF) load_bias<LPR, NU, RAGGED>(biases, row[0], j, CPR, G, bb_);
+            load_block<VARIANT, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, cb, sb);
         }
-        block(ca, sa, b);
+        block(ca, sa, ba, b);
         if (b2 >= b_end) break;
         const int b3 = b2 + WAVES;
         if (b3 < b_end) {
             row[0] = b3 * RS + seg < N ? b3 * RS + seg : N - 1;
-            load_block<TQ_TERNARY, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, ca, sa);
+            if constexpr (AFF) load_bias<LPR, NU, RAGGED>(biases, row[0], j, CPR, G, ba);
+            load_block<VARIANT, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, ca, sa);
         }
-        block(cb, sb, b2);
+        block(cb, sb, bb_, b2);
     }
 }
 
@@ -596,31 +675,33 @@ Config pick_xreg(int cpr) {
     return best;
 }
 
-template <int LPR, int NU>
-hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
-                       int N, int K, hipStream_t stream) {
+template <int VARIANT, int LPR, int NU>
+hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                       const uint16_t *x, float *y, int N, int K, hipStream_t stream) {
     constexpr int RS = 64 / LPR;
     const int nblocks = (N + RS - 1) / RS;
     const int grid = max(1, min(device_cus(), (nblocks + kXregWaves - 1) / kXregWaves));
-    constexpr size_t lds = lds_bytes<TQ_TERNARY, LPR, NU>();
+    constexpr size_t lds = lds_bytes<VARIANT, LPR, NU>();
     if ((K / 128) * 2 == LPR * NU)
-        hipLaunchKernelGGL((gemv_xreg_kernel<LPR, NU, kXregWaves, false>), dim3(grid),
-                           dim3(64 * kXregWaves), lds, stream, codes, scales, x, y, N, K);
+        hipLaunchKernelGGL((gemv_xreg_kernel<VARIANT, LPR, NU, kXregWaves, false>), dim3(grid),
+                           dim3(64 * kXregWaves), lds, stream, codes, scales, biases, x, y, N, K);
     else
-        hipLaunchKernelGGL((gemv_xreg_kernel<LPR, NU, kXregWaves, true>), dim3(grid),
-                           dim3(64 * kXregWaves), lds, stream, codes, scales, x, y, N, K);
+        hipLaunchKernelGGL((gemv_xreg_kernel<VARIANT, LPR, NU, kXregWaves, true>), dim3(grid),
+                           dim3(64 * kXregWaves), lds, stream, codes, scales, biases, x, y, N, K);
     return hipGetLastError();
 }
 
+template <int VARIANT>
 hipError_t dispatch_xreg(const Config &c, const uint8_t *codes, const uint16_t *scales,
-                         const uint16_t *x, float *y, int N, int K, hipStream_t s) {
-#define TQ_XCASE(L)                                                                  \
-    if (c.lpr == L) switch (c.nu) {                                                  \
-        case 1: return launch_xreg<L, 1>(codes, scales, x, y, N, K, s);              \
-        case 2: return launch_xreg<L, 2>(codes, scales, x, y, N, K, s);              \
-        case 3: return launch_xreg<L, 3>(codes, scales, x, y, N, K, s);              \
-        case 4: return launch_xreg<L, 4>(codes, scales, x, y, N, K, s);              \
-        case 5: return launch_xreg<L, 5>(codes, scales, x, y, N, K, s);              \
+                         const uint16_t *biases, const uint16_t *x, float *y, int N, int K,
+                         hipStream_t s) {
+#define TQ_XCASE(L)                                                                            \
+    if (c.lpr == L) switch (c.nu) {                                                            \
+        case 1: return launch_xreg<VARIANT, L, 1>(codes, scales, biases, x, y, N, K, s);       \
+        case 2: return launch_xreg<VARIANT, L, 2>(codes, scales, biases, x, y, N, K, s);       \
+        case 3: return launch_xreg<VARIANT, L, 3>(codes, scales, biases, x, y, N, K, s);       \
+        case 4: return launch_xreg<VARIANT, L, 4>(codes, scales, biases, x, y, N, K, s);       \
+        case 5: return launch_xreg<VARIANT, L, 5>(codes, scales, biases, x, y, N, K, s);       \
     }
     TQ_XCASE(8) TQ_XCASE(16) TQ_XCASE(32) TQ_XCASE(64)
 #undef TQ_XCASE
@@ -635,7 +716,8 @@ int32_t gemv_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_
     if (variant == TQ_TERNARY) {
         const Config xc = pick_xreg(cpr);
         if (xc.lpr) {
-            const hipError_t e = dispatch_xreg(xc, codes, scales, x, y, (int)N, (int)K, stream);
+            const hipError_t e =
+                dispatch_xreg<TQ_TERNARY>(xc, codes, scales, nullptr, x, y, (int)N, (int)K, stream);
             if (e != hipSuccess)
                 return fail(TQ_ERR_HIP, "GEMV launch failed: %s", hipGetErrorString(e));
             return TQ_OK;
@@ -651,6 +733,19 @@ int32_t gemv_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_
     if (lds > kMaxLds)
         return fail(TQ_ERR_SHAPE, "K=%lld needs %zu bytes of LDS, above %zu", (long long)K, lds,
                     kMaxLds);
+    if (e != hipSuccess) return fail(TQ_ERR_HIP, "GEMV launch failed: %s", hipGetErrorString(e));
+    return TQ_OK;
+}
+
+// Affine 2-bit levels: the register-activation kernel only (K <= 20480, the
+// widest shape 64 lanes x 5 chunks of 64 weights).
+int32_t gemv_affine_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                            const uint16_t *x, float *y, int64_t N, int64_t K, hipStream_t stream) {
+    const Config xc = pick_xreg((int)(K / 128) * 2);
+    if (!xc.lpr)
+        return fail(TQ_ERR_SHAPE, "K=%lld is above the affine GEMV limit 20480", (long long)K);
+    const hipError_t e =
+        dispatch_xreg<TQ_AFFINE2>(xc, codes, scales, biases, x, y, (int)N, (int)K, stream);
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "GEMV launch failed: %s", hipGetErrorString(e));
     return TQ_OK;
 }

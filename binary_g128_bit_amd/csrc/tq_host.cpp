@@ -5,6 +5,7 @@
 // slot (aitrends.kr, "Ternary-Bonsai-27B-mlx-2bit", section "Technical
 // features") and the 1-bit build's {-1, +1} set (thakicloud.github.io,
 // "Bonsai 27B: ternary and 1-bit quantization", "How the compression works").
+// The affine levels (TQ_AFFINE2) use the same slots with q in {0..3}.
 // The five-trit storage (TQ_TERNARY5) is the native ternary packing the
 // model card names as the next step: 26 bytes per 128-weight group, byte b
 // the base-3 number of trits 5b..5b+4 (least significant digit first).
@@ -126,7 +127,7 @@ extern "C" {
 
 size_t tq_codes_bytes(int64_t N, int64_t K, int32_t variant) {
     if (N < 1 || K < tq::kGroup || K % tq::kGroup) return 0;
-    if (variant == TQ_TERNARY) return size_t(N) * size_t(K / 4);
+    if (variant == TQ_TERNARY || variant == TQ_AFFINE2) return size_t(N) * size_t(K / 4);
     if (variant == TQ_BINARY) return size_t(N) * size_t(K / 8);
     if (variant == TQ_TERNARY5) return size_t(N) * size_t(tq::ternary5_row_bytes(K));
     return 0;
@@ -150,6 +151,23 @@ int32_t tq_pack(const int8_t *t, int64_t N, int64_t K, int32_t group, int32_t va
                 return tq::fail_at(TQ_ERR_VALUE, idx, "t[%lld] = %d is outside {-1,0,+1}",
                                    (long long)idx, int(t[idx]));
             }
+        }
+        return TQ_OK;
+    }
+    if (variant == TQ_AFFINE2) {
+        const int64_t nbytes = N * (K / 4);
+        for (int64_t i = 0; i < nbytes; ++i) {
+            uint32_t v = 0;
+            for (int s = 0; s < 4; ++s) {
+                const int q = t[i * 4 + s];
+                if (static_cast<unsigned>(q) > 3u) {
+                    const int64_t idx = i * 4 + s;
+                    return tq::fail_at(TQ_ERR_VALUE, idx, "q[%lld] = %d is outside {0,1,2,3}",
+                                       (long long)idx, q);
+                }
+                v |= uint32_t(q) << (2 * s);
+            }
+            codes[i] = uint8_t(v);
         }
         return TQ_OK;
     }
@@ -191,6 +209,12 @@ int32_t tq_unpack(const uint8_t *codes, int64_t N, int64_t K, int32_t group, int
                     const int nt = b < 25 ? 5 : 3;
                     for (int i = 0; i < nt; ++i) t[idx + i] = tb.trit[v][i];
                 }
+        return TQ_OK;
+    }
+    if (variant == TQ_AFFINE2) {
+        const int64_t nbytes = N * (K / 4);
+        for (int64_t i = 0; i < nbytes; ++i)
+            for (int s = 0; s < 4; ++s) t[i * 4 + s] = int8_t((codes[i] >> (2 * s)) & 3u);
         return TQ_OK;
     }
     if (variant == TQ_TERNARY) {

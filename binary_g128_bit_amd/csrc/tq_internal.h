@@ -35,9 +35,11 @@ inline int32_t check_shape(int64_t M, int64_t N, int64_t K, int32_t group, int32
                     (long long)kMaxK);
     if (group != kGroup)
         return fail(TQ_ERR_GROUP, "group=%d; only 128 is supported", group);
-    if (variant != TQ_TERNARY && variant != TQ_BINARY && variant != TQ_TERNARY5)
+    if (variant != TQ_TERNARY && variant != TQ_BINARY && variant != TQ_TERNARY5 &&
+        variant != TQ_AFFINE2)
         return fail(TQ_ERR_VARIANT,
-                    "variant=%d is not TQ_TERNARY (0), TQ_BINARY (1) or TQ_TERNARY5 (2)", variant);
+                    "variant=%d is not TQ_TERNARY (0), TQ_BINARY (1), TQ_TERNARY5 (2) or "
+                    "TQ_AFFINE2 (3)", variant);
     return TQ_OK;
 }
 

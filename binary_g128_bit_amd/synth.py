@@ -8,9 +8,12 @@ Distributions (27B-shaped decode weights; the weights themselves are not public)
   * trits t: iid uniform over {-1, 0, +1} (ternary, either storage) or
     {-1, +1} (binary);
   * group scales: float16(exp(N(-4, 0.5))), one per 128 weights along K;
+  * affine levels q: iid uniform over {0, 1, 2, 3}; group biases
+    float16(-exp(N(-3.5, 0.5)));
   * activations: float16(N(0, 1)) drawn in float32, round-to-nearest-even;
-  * integer-exact sets: activations uniform integers in [-8, 8] and scales
-    2^-j with j uniform in [0, 6], so every partial sum is exactly
+  * integer-exact sets: activations uniform integers in [-8, 8], scales
+    2^-j with j uniform in [0, 6] (affine biases -k 2^-j, k in [0, 3]), so
+    every partial sum is exactly
     representable in fp32 and any summation order gives the same bits.
 
 RNG: numpy PCG64, seed = 1000 * config_index + matrix_index; per matrix the
@@ -21,6 +24,7 @@ import numpy as np
 TERNARY = 0
 BINARY = 1
 TERNARY5 = 2  # ternary trits stored five to a byte
+AFFINE2 = 3   # unsigned 2-bit levels with a scale and a bias per group
 GROUP = 128
 
 # Workload shapes (out N, in K).  The 27B-like projection shapes: MLP gate/up
@@ -85,6 +89,31 @@ def int_activations(g, M, K):
 def pow2_scales(g, N, K, group=GROUP):
     """float16 [N][K/group] equal to 2^-j, j uniform in [0, 6]."""
     return np.ldexp(1.0, -g.integers(0, 7, size=(N, K // group))).astype(np.float16)
+
+
+def levels(g, N, K):
+    """int8 [N][K] affine levels, iid uniform over {0, 1, 2, 3}."""
+    return g.integers(0, 4, size=(N, K), dtype=np.int8)
+
+
+def biases(g, N, K, group=GROUP):
+    """float16 [N][K/group] affine offsets, -exp(N(-3.5, 0.5)) (a group minimum)."""
+    return (-np.exp(g.normal(-3.5, 0.5, size=(N, K // group)))).astype(np.float16)
+
+
+def pow2_biases(g, N, K, group=GROUP):
+    """float16 [N][K/group] equal to -k * 2^-j, k in [0, 3], j in [0, 6]."""
+    k = g.integers(0, 4, size=(N, K // group))
+    return (-k * np.ldexp(1.0, -g.integers(0, 7, size=(N, K // group)))).astype(np.float16)
+
+
+def affine_problem(seed, N, K, M=1, exact=False):
+    """(q int8 [N][K], scales f16, biases f16, X f16 [M][K])."""
+    g = rng(seed)
+    q = levels(g, N, K)
+    if exact:
+        return q, pow2_scales(g, N, K), pow2_biases(g, N, K), int_activations(g, M, K)
+    return q, scales(g, N, K), biases(g, N, K), activations(g, M, K)
 
 
 def problem(seed, N, K, M=1, variant=TERNARY, exact=False):

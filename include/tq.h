@@ -69,6 +69,14 @@ extern "C" {
  * tq_gemv and tq_gemm with M == 1 (K <= 40960); other entry points return
  * TQ_ERR_VARIANT. */
 #define TQ_TERNARY5 2
+/* Affine 2-bit levels as the MLX packaging stores them, a scale and a bias
+ * per group (aitrends.kr, "Ternary-Bonsai-27B-mlx-2bit", "Technical
+ * features"): q in {0,1,2,3} in the 2-bit slots of TQ_TERNARY (same bytes,
+ * code 3 allowed), w = s_g * q + b_g with FP16 s_g and b_g per 128-weight
+ * group, 2.25 bits/weight stored.  Ternary weights are q = t + 1 with
+ * b_g = -s_g.  tq_pack / tq_unpack take and return q.  The product is
+ * tq_gemv_affine; the other device entry points return TQ_ERR_VARIANT. */
+#define TQ_AFFINE2 3
 
 /* status codes */
 #define TQ_OK 0
@@ -140,6 +148,18 @@ int32_t tq_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
 int32_t tq_embed(const uint8_t *codes, const uint16_t *scales, const int32_t *ids,
                  uint16_t *out, int64_t n_ids, int64_t N, int64_t K, int32_t group,
                  int32_t variant, void *stream);
+
+/* Device.  y[n] = sum_g (s[n][g] * sum_j q[n][128g+j] * x[128g+j]
+ *                      + b[n][g] * sum_j x[128g+j])
+ * i.e. y = W x with w = s_g * q + b_g (the affine 2-bit levels of
+ * TQ_AFFINE2), accumulated in fp32.  codes as tq_gemv with K/4 bytes per row;
+ * scales and biases are uint16 (fp16 bits) [N][K/128], 2-byte aligned; x and
+ * y as tq_gemv.  Limits: 1 <= N < 2^31, 128 <= K <= 20480 (the activations
+ * of a lane's columns stay in registers); a larger K returns TQ_ERR_SHAPE.
+ * group must be 128. */
+int32_t tq_gemv_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                       const uint16_t *x, float *y, int64_t N, int64_t K, int32_t group,
+                       void *stream);
 
 /* Text of the calling thread's last error ("" if none). */
 const char *tq_last_error(void);

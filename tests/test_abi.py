@@ -55,6 +55,7 @@ FAKE = 0x7f0000000000  # 16-byte aligned address that is never dereferenced
     ((FAKE + 8, FAKE, FAKE, FAKE, 1, 8, 256, 128, 0), 7),
     ((FAKE + 8, FAKE, FAKE, FAKE, 1, 8, 256, 128, 2), 7),
     ((FAKE, FAKE, FAKE, FAKE, 2, 8, 256, 128, 2), 4),       # five-trit bytes: GEMV only
+    ((FAKE, FAKE, FAKE, FAKE, 1, 8, 256, 128, 3), 4),       # affine levels need biases
     ((FAKE, FAKE, FAKE + 2, FAKE, 1, 8, 256, 128, 0), 7),
     ((FAKE, FAKE + 1, FAKE, FAKE, 1, 8, 256, 128, 0), 7),
     ((FAKE, FAKE, FAKE, FAKE + 2, 1, 8, 256, 128, 0), 7),
@@ -83,6 +84,7 @@ def test_device_entry_points_validate_on_host(args, status):
     ((FAKE, FAKE, FAKE, FAKE, 4, 8, 256, 64, 0), 3),
     ((FAKE, FAKE, FAKE, FAKE, 4, 8, 256, 128, 3), 4),
     ((FAKE, FAKE, FAKE, FAKE, 4, 8, 256, 128, 2), 4),       # five-trit tables: not for rows
+    ((FAKE, FAKE, FAKE, FAKE, 4, 8, 256, 128, 3), 4),       # affine tables: not for rows
     ((FAKE + 2, FAKE, FAKE, FAKE, 4, 8, 256, 128, 0), 7),
     ((FAKE, FAKE + 1, FAKE, FAKE, 4, 8, 256, 128, 0), 7),
     ((FAKE, FAKE, FAKE + 2, FAKE, 4, 8, 256, 128, 0), 7),
@@ -105,6 +107,27 @@ def test_embed_validates_on_host(args, status):
         assert rc == 1, L.tq_last_error()
 
 
+@pytest.mark.parametrize("args,status", [
+    # (codes, scales, biases, x, y, N, K, group)
+    ((FAKE, FAKE, 0, FAKE, FAKE, 8, 256, 128), 1),
+    ((0, FAKE, FAKE, FAKE, FAKE, 8, 256, 128), 1),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 0, 256, 128), 2),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 8, 200, 128), 2),
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 8, 20480 + 128, 128), 2),   # above the affine limit
+    ((FAKE, FAKE, FAKE, FAKE, FAKE, 8, 256, 64), 3),
+    ((FAKE, FAKE, FAKE + 1, FAKE, FAKE, 8, 256, 128), 7),
+    ((FAKE + 4, FAKE, FAKE, FAKE, FAKE, 8, 256, 128), 7),
+    ((FAKE, FAKE, FAKE, FAKE + 8, FAKE, 8, 256, 128), 7),
+])
+def test_gemv_affine_validates_on_host(args, status):
+    L = tq.lib()
+    codes, scales, biases, x, y, N, K, group = args
+    p = ctypes.c_void_p
+    rc = L.tq_gemv_affine(p(codes), p(scales), p(biases), p(x), p(y), N, K, group, None)
+    assert rc == status, L.tq_last_error()
+    assert L.tq_last_error()
+
+
 def test_pack_errors():
     t = np.zeros((2, 128), np.int8)
     t[1, 5] = 2
@@ -120,9 +143,9 @@ def test_pack_errors():
         tq.tq_pack(np.zeros((2, 100), np.int8))
     assert e.value.status == 2
     with pytest.raises(tq.TQError) as e:
-        tq.tq_pack(np.zeros((2, 128), np.int8), 3)
+        tq.tq_pack(np.zeros((2, 128), np.int8), 4)
     assert e.value.status == 4
-    assert tq.tq_codes_bytes(2, 128, 3) == 0
+    assert tq.tq_codes_bytes(2, 128, 4) == 0
     L = tq.lib()
     assert L.tq_pack(None, 2, 128, 128, 0, None) == 1
     assert L.tq_pack(t.ctypes.data, 2, 128, 64, 0, t.ctypes.data) == 3

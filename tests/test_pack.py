@@ -84,3 +84,23 @@ def test_ternary5_sizes_and_errors():
     c[:, 78:] = 0xFF
     assert np.all(tq.tq_unpack(c, 2, 384, tq.TQ_TERNARY5) == 1)
 
+
+def test_affine_levels_pack_like_oracle():
+    g = synth.rng(4242)
+    for N, K in ((1, 128), (9, 384), (33, 5120)):
+        q = synth.levels(g, N, K)
+        mine = tq.tq_pack(q, tq.TQ_AFFINE2)
+        assert np.array_equal(mine, oracle.pack(q, oracle.AFFINE2))
+        assert np.array_equal(tq.tq_unpack(mine, N, K, tq.TQ_AFFINE2), q)
+    # the ternary bytes of t are the affine bytes of q = t + 1
+    t = synth.trits(g, 4, 256)
+    assert np.array_equal(tq.tq_pack(t), tq.tq_pack((t + 1).astype(np.int8), tq.TQ_AFFINE2))
+    bad = np.zeros((2, 128), np.int8)
+    bad[1, 3] = 4
+    with pytest.raises(tq.TQError) as e:
+        tq.tq_pack(bad, tq.TQ_AFFINE2)
+    assert e.value.status == 5 and e.value.index == 131
+    allb = np.arange(256, dtype=np.uint8).reshape(8, 32)
+    assert np.array_equal(tq.tq_unpack(allb, 8, 128, tq.TQ_AFFINE2),
+                          oracle.unpack(allb, 8, 128, oracle.AFFINE2))
+
