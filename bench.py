@@ -391,6 +391,38 @@ def ternary5(torch, tq, gen, stream):
     return out
 
 
+def affine2(torch, tq, gen, stream):
+    """Affine 2-bit levels (scale and bias per group) on the MLP and head
+    shapes: back-to-back launches over >= 1 GiB of rotating copies (graph
+    replays as well).  Codes are uniform bytes (iid uniform levels)."""
+    from binary_g128_bit_amd import synth
+    out = {}
+    for name, (N, K) in (("gate_up_34816x5120", (2 * synth.GATE_UP[0], synth.GATE_UP[1])),
+                         ("down_5120x17408", synth.DOWN), ("lm_head_248320x5120", synth.LM_HEAD)):
+        alg = N * K // 4 + 4 * N * (K // 128)
+        copies = max(2, math.ceil((1 << 30) / alg))
+        pool = []
+        for _ in range(copies):
+            c = torch.randint(0, 256, (N, K // 4), device=gen.dev, generator=gen.gen,
+                              dtype=torch.int32).to(torch.uint8)
+            pool.append((c, gen.scales(N, K), -gen.scales(N, K)))
+        x = gen.act(1, K)[0]
+        y = torch.empty(N, dtype=torch.float32, device=gen.dev)
+
+        def launch(i):
+            c, s, b = pool[i % copies]
+            return tq.tq_gemv_affine(c, s, b, x, y)
+
+        ms = back_to_back_ms(torch, stream, launch, 100 if N < 100000 else 30)
+        msg = graph_ms(torch, launch, 4 * copies)
+        out[name] = {"us": round(ms * 1e3, 2), "us_graph": round(msg * 1e3, 2),
+                     "gbs": round(alg / ms / 1e6, 1), "frac_hbm": round(alg / ms / 1e6 / PEAK_HBM_GBS, 4),
+                     "gweights_s": round(N * K / ms / 1e6, 1), "bytes": alg}
+        del pool
+        torch.cuda.empty_cache()
+    return out
+
+
 def copy_calibration():
     import torch
     dev = torch.device("cuda:0")
@@ -539,6 +571,7 @@ def main():
         line["gemm"] = gemm_widths(torch, tq, gen, stream, bufs, slots)
         line["binary_and_lm_head"] = binary_and_lm_head(torch, tq, gen, stream)
         line["ternary5"] = ternary5(torch, tq, gen, stream)
+        line["affine2"] = affine2(torch, tq, gen, stream)
         del bufs
         torch.cuda.empty_cache()
         line["stack_sweep"] = stack_sweep(torch, tq, gen, stream)
