@@ -9,5 +9,6 @@ only builds that file and marshals numpy arrays through ctypes.
 """
 from .oracle import (  # noqa: F401
     TERNARY, BINARY, TERNARY5, AFFINE2, OracleError, build, load, half_to_double, codes_bytes,
-    scales_count, pack, unpack, gemm, gemv, embed, affine_gemm, default_threads,
+    scales_count, pack, unpack, gemm, gemv, embed, affine_gemm, float_to_half, kv_quant,
+    attn_decode, default_threads,
 )

@@ -73,6 +73,12 @@ def load(lib_path=_LIB):
     lib.oracle_embed.restype = ci
     lib.oracle_affine_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, vp, vp, ci]
     lib.oracle_affine_gemm.restype = ci
+    lib.oracle_float_to_half.argtypes = [ctypes.c_float]
+    lib.oracle_float_to_half.restype = ctypes.c_uint16
+    lib.oracle_kv_quant.argtypes = [vp, i64, vp, vp]
+    lib.oracle_kv_quant.restype = ci
+    lib.oracle_attn_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, vp, vp]
+    lib.oracle_attn_decode.restype = ci
     _lib_cache[lib_path] = lib
     return lib
 
@@ -194,4 +200,42 @@ def affine_gemm(codes, scales, biases, X, N, K, group=128, threads=1, lib=None):
     if rc:
         raise OracleError(rc)
     return Y, A
+
+
+def float_to_half(f, lib=None):
+    """binary32 value -> binary16 bits, round to nearest even."""
+    return (lib or load()).oracle_float_to_half(float(f))
+
+
+def kv_quant(x, lib=None):
+    """x float16 [n][256] -> (nibbles uint8 [n][256], scales float16 [n][8])."""
+    lib = lib or load()
+    xb = _bits(x).reshape(-1, 256)
+    n = xb.shape[0]
+    nib = np.empty((n, 256), dtype=np.uint8)
+    sc = np.empty((n, 8), dtype=np.uint16)
+    rc = lib.oracle_kv_quant(_ptr(xb), n, _ptr(nib), _ptr(sc))
+    if rc:
+        raise OracleError(rc)
+    return nib, sc.view(np.float16)
+
+
+def attn_decode(q, knib, ks, vnib, vs, lib=None):
+    """Decode attention from the logical 4-bit cache: q float16 [n_q][256];
+    knib / vnib uint8 [n_kv][T][256]; ks / vs float16 [n_kv][T][8].
+    Returns (out [n_q][256], A [n_q][256]) float64."""
+    lib = lib or load()
+    qb = _bits(q).reshape(-1, 256)
+    n_q = qb.shape[0]
+    knib = np.ascontiguousarray(knib, dtype=np.uint8)
+    vnib = np.ascontiguousarray(vnib, dtype=np.uint8)
+    n_kv, T = knib.shape[0], knib.shape[1]
+    ksb, vsb = _bits(ks), _bits(vs)
+    out = np.empty((n_q, 256), dtype=np.float64)
+    A = np.empty((n_q, 256), dtype=np.float64)
+    rc = lib.oracle_attn_decode(_ptr(qb), _ptr(knib), _ptr(ksb), _ptr(vnib), _ptr(vsb), T, n_q,
+                                n_kv, _ptr(out), _ptr(A))
+    if rc:
+        raise OracleError(rc)
+    return out, A
 

@@ -372,3 +372,129 @@ int oracle_affine_gemm(const uint8_t *codes, const uint16_t *scales, const uint1
     return status;
 }
 
+/* ------------------------------------------------------------------------
+ * 4-bit KV cache and decode attention.
+ *
+ * The model keeps K and V of its 16 full-attention layers (4 KV heads of
+ * dimension 256) in a 4-bit cache that the pages call near-lossless
+ * (aitrends.kr, "Ternary-Bonsai-27B-mlx-2bit", "Technical features";
+ * thakicloud.github.io, "Bonsai 27B: ternary and 1-bit quantization", the
+ * memory section: 64 KiB per token at FP16, a quarter of that at 4 bits;
+ * techtoast.kr, the KV-cache arithmetic: 2 x 4 heads x 256 x 16 layers).
+ * The pages give no 4-bit format.  Reading R9: each head vector of 256 is
+ * cut into 8 groups of 32 consecutive dimensions; a group keeps one FP16
+ * scale d = fp16(amax / 7) (amax = max |x| over the group, the division in
+ * fp32, the conversion round-to-nearest-even) and per element the nibble
+ * q + 8 with q = clamp(rint(x / d), -8, 7) (x / d in fp32, rint half-to-even);
+ * an all-zero group stores d = 0 and nibbles 8.  The dequantized value is
+ * (nibble - 8) * d.  Decode attention for query head h reads KV head
+ * h / (n_q / n_kv): out_h = sum_t softmax_t(q_h . k_t / sqrt(256)) v_t.
+ * Logical layouts here: nibbles [n_vec][256] (one byte each), scales
+ * [n_vec][8].
+ * ------------------------------------------------------------------------ */
+
+/* IEEE binary32 -> binary16 bits, round to nearest even, from the formats'
+ * definitions (finite inputs below 65520 in magnitude). */
+uint16_t oracle_float_to_half(float f)
+{
+    union { float f; uint32_t u; } v = { f };
+    uint32_t sign = (v.u >> 16) & 0x8000u;
+    uint32_t mag = v.u & 0x7FFFFFFFu;
+    if (mag == 0) return (uint16_t)sign;
+    int e = (int)(mag >> 23) - 127;                /* unbiased exponent */
+    uint32_t m = (mag & 0x7FFFFFu) | 0x800000u;    /* 24-bit significand */
+    /* value = m * 2^(e - 23); binary16 keeps 11 bits for e >= -14, and a
+     * fixed quantum of 2^-24 below */
+    int shift = (e >= -14) ? 13 : 13 + (-14 - e);
+    uint32_t q;
+    if (shift >= 32) {
+        q = 0;                                     /* below 2^-32: far under half of 2^-24 */
+    } else {
+        q = m >> shift;
+        uint32_t rem = m & ((1u << shift) - 1u), half = 1u << (shift - 1);
+        if (rem > half || (rem == half && (q & 1u))) q++;
+    }
+    uint32_t h;
+    if (e >= -14) {
+        /* q in [2^10, 2^11]; carry may bump the exponent */
+        int he = e + 15;
+        if (q >= 2048u) { q >>= 1; he++; }
+        h = ((uint32_t)he << 10) | (q & 0x3FFu);
+    } else {
+        h = q;                                     /* subnormal (or 2^-14 on carry) */
+    }
+    return (uint16_t)(sign | h);
+}
+
+int oracle_kv_quant(const uint16_t *x, int64_t n_vec, uint8_t *nib, uint16_t *scales)
+{
+    if (!x || !nib || !scales) return OR_ERR_NULL;
+    if (n_vec < 0) return OR_ERR_SHAPE;
+    for (int64_t v = 0; v < n_vec; v++)
+        for (int g = 0; g < 8; g++) {
+            const uint16_t *xg = x + v * 256 + 32 * g;
+            float amax = 0.0f;
+            for (int j = 0; j < 32; j++) {
+                float a = fabsf((float)oracle_half_to_double(xg[j]));
+                if (a > amax) amax = a;
+            }
+            uint16_t d = oracle_float_to_half(amax / 7.0f);
+            float df = (float)oracle_half_to_double(d);
+            scales[v * 8 + g] = d;
+            for (int j = 0; j < 32; j++) {
+                int q = 0;
+                if (df != 0.0f) {
+                    float r = rintf((float)oracle_half_to_double(xg[j]) / df);
+                    q = r < -8.0f ? -8 : r > 7.0f ? 7 : (int)r;
+                }
+                nib[v * 256 + 32 * g + j] = (uint8_t)(q + 8);
+            }
+        }
+    return OR_OK;
+}
+
+/* out[h][256] (and the bound A[h][256] = sum_t p_t |v_t|) in fp64 from the
+ * logical cache: knib / vnib [n_kv][T][256], ks / vs [n_kv][T][8]. */
+int oracle_attn_decode(const uint16_t *q, const uint8_t *knib, const uint16_t *ks,
+                       const uint8_t *vnib, const uint16_t *vs, int64_t T, int64_t n_q,
+                       int64_t n_kv, double *out, double *A)
+{
+    if (!q || !knib || !ks || !vnib || !vs || !out) return OR_ERR_NULL;
+    if (T < 1 || n_kv < 1 || n_q < 1 || n_q % n_kv) return OR_ERR_SHAPE;
+    int64_t rep = n_q / n_kv;
+    double *s = (double *)malloc((size_t)T * sizeof(double));
+    if (!s) return OR_ERR_NOMEM;
+    for (int64_t h = 0; h < n_q; h++) {
+        int64_t kvh = h / rep;
+        double smax = -INFINITY;
+        for (int64_t t = 0; t < T; t++) {
+            const uint8_t *kn = knib + (kvh * T + t) * 256;
+            const uint16_t *kd = ks + (kvh * T + t) * 8;
+            double dot = 0.0;
+            for (int j = 0; j < 256; j++)
+                dot += oracle_half_to_double(q[h * 256 + j]) *
+                       ((double)kn[j] - 8.0) * oracle_half_to_double(kd[j / 32]);
+            s[t] = dot / 16.0;                     /* 1 / sqrt(256) */
+            if (s[t] > smax) smax = s[t];
+        }
+        double sum = 0.0;
+        for (int64_t t = 0; t < T; t++) {
+            s[t] = exp(s[t] - smax);
+            sum += s[t];
+        }
+        for (int j = 0; j < 256; j++) {
+            double o = 0.0, a = 0.0;
+            for (int64_t t = 0; t < T; t++) {
+                double vv = ((double)vnib[(kvh * T + t) * 256 + j] - 8.0) *
+                            oracle_half_to_double(vs[(kvh * T + t) * 8 + j / 32]);
+                o += s[t] / sum * vv;
+                a += s[t] / sum * fabs(vv);
+            }
+            out[h * 256 + j] = o;
+            if (A) A[h * 256 + j] = a;
+        }
+    }
+    free(s);
+    return OR_OK;
+}
+

@@ -394,7 +394,77 @@ def check_affine(lib):
             assert e.code == 4
 
 
+# ------------------------------------------------------- 4-bit KV cache
+def check_float_to_half(lib):
+    g = np.random.default_rng(31)
+    vals = g.standard_normal(4000).astype(np.float32) * np.float32(10.0) ** g.integers(-9, 4, 4000)
+    vals = np.concatenate([vals, np.float32([0.0, -0.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26,
+                                             1 / 7, 65504.0, 6.1035156e-05, 6.0975552e-05])])
+    vals = vals[np.abs(vals) < 65504]
+    for v in vals:
+        assert oracle.float_to_half(v, lib=lib) == int(np.float32(v).astype(np.float16).view(np.uint16)), v
+
+
+def check_kv_quant(lib):
+    ex = _golden("kv4_examples.json")
+    x = np.zeros((1, 256), np.float16)
+    for gi, grp in enumerate(ex["groups"]):
+        x[0, 32 * gi: 32 * gi + len(grp["x"])] = grp["x"]
+    nib, sc = oracle.kv_quant(x, lib=lib)
+    for gi, grp in enumerate(ex["groups"]):
+        assert int(sc[0, gi].view(np.uint16)) == int(grp["d_hex"], 16), (gi, sc[0, gi])
+        n = len(grp["nibbles"])
+        assert list(nib[0, 32 * gi: 32 * gi + n]) == grp["nibbles"], gi
+        assert all(v == 8 for v in nib[0, 32 * gi + n: 32 * gi + 32]), gi
+    # properties on random vectors: the largest element lands on +-7, every
+    # element is within d / 2 of its dequantized value
+    g = synth.rng(37)
+    xr = (g.standard_normal((64, 256)) * np.exp(g.normal(0, 1.5, (64, 1)))).astype(np.float16)
+    nib, sc = oracle.kv_quant(xr, lib=lib)
+    xv = xr.astype(np.float64).reshape(64, 8, 32)
+    q = nib.astype(np.int64).reshape(64, 8, 32) - 8
+    d = sc.astype(np.float64)[:, :, None]
+    assert q.min() >= -8 and q.max() <= 7
+    assert np.all(np.abs(q * d - xv) <= d / 2 * (1 + 1e-12))
+    am = np.abs(xv).argmax(axis=2)
+    assert np.all(np.abs(np.take_along_axis(q, am[:, :, None], 2)) == 7)
+
+
+def _dequant(nib, sc):
+    return (nib.astype(np.float64) - 8.0) * np.repeat(sc.astype(np.float64), 32, axis=-1)
+
+
+def check_attn_decode(lib):
+    import scipy.special
+    g = synth.rng(41)
+    n_kv, n_q, T = 2, 8, 37
+    q = synth.activations(g, n_q, 256)
+    k = synth.activations(g, n_kv * T, 256)
+    v = synth.activations(g, n_kv * T, 256)
+    kn, ks = oracle.kv_quant(k, lib=lib)
+    vn, vs = oracle.kv_quant(v, lib=lib)
+    kn, ks = kn.reshape(n_kv, T, 256), ks.reshape(n_kv, T, 8)
+    vn, vs = vn.reshape(n_kv, T, 256), vs.reshape(n_kv, T, 8)
+    out, A = oracle.attn_decode(q, kn, ks, vn, vs, lib=lib)
+    K, V = _dequant(kn, ks), _dequant(vn, vs)
+    for h in range(n_q):
+        kvh = h // (n_q // n_kv)
+        p = scipy.special.softmax(K[kvh] @ q[h].astype(np.float64) / 16.0)
+        ref = p @ V[kvh]
+        assert np.allclose(out[h], ref, rtol=1e-12, atol=1e-14), h
+        assert np.allclose(A[h], p @ np.abs(V[kvh]), rtol=1e-12, atol=1e-300)
+    # one token: the output is that token's value; equal keys: the mean value
+    o1, _ = oracle.attn_decode(q[:2], kn[:1, :1], ks[:1, :1], vn[:1, :1], vs[:1, :1], lib=lib)
+    assert np.array_equal(o1, np.repeat(V[0, :1], 2, axis=0))
+    ke = np.repeat(kn[:, :1], T, axis=1)
+    kse = np.repeat(ks[:, :1], T, axis=1)
+    oe, _ = oracle.attn_decode(q, ke, kse, vn, vs, lib=lib)
+    for h in range(n_q):
+        assert np.allclose(oe[h], V[h // (n_q // n_kv)].mean(axis=0), rtol=1e-12, atol=1e-15)
+
+
 ALL_CHECKS = [check_half_decode, check_byte_counts, check_roundtrip_bytes,
               check_golden_layout, check_worked_gemv, check_bruteforce_numpy,
               check_exact_integer, check_special_cases, check_bound, check_errors,
-              check_embed, check_golden_ternary5, check_affine]
+              check_embed, check_golden_ternary5, check_affine, check_float_to_half,
+              check_kv_quant, check_attn_decode]

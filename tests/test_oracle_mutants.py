@@ -48,6 +48,20 @@ MUTANTS = [
     ("affine_level_mask", [("t[n * K + k] = (int8_t)((byte >> (2 * (k % 4))) & 3);",
                             "t[n * K + k] = (int8_t)((byte >> (2 * (k % 4))) & 1);")]),
     ("affine_bound_bias", [("+ fabs(bg) * fabs(x[m * K + k]);", ";")]),
+    ("kv_amax_divisor", [("uint16_t d = oracle_float_to_half(amax / 7.0f);",
+                          "uint16_t d = oracle_float_to_half(amax / 8.0f);")]),
+    ("kv_nibble_offset", [("nib[v * 256 + 32 * g + j] = (uint8_t)(q + 8);",
+                           "nib[v * 256 + 32 * g + j] = (uint8_t)(q + 7);")]),
+    ("kv_round_truncates", [("float r = rintf((float)oracle_half_to_double(xg[j]) / df);",
+                             "float r = truncf((float)oracle_half_to_double(xg[j]) / df);")]),
+    ("half_round_ties_up", [("if (rem > half || (rem == half && (q & 1u))) q++;",
+                             "if (rem >= half) q++;")]),
+    ("attn_scale", [("s[t] = dot / 16.0;", "s[t] = dot / 8.0;")]),
+    ("attn_gqa_map", [("int64_t kvh = h / rep;", "int64_t kvh = h % n_kv;")]),
+    ("attn_group_of_dim", [("((double)kn[j] - 8.0) * oracle_half_to_double(kd[j / 32]);",
+                            "((double)kn[j] - 8.0) * oracle_half_to_double(kd[j / 16 % 8]);")]),
+    ("attn_v_scale", [("oracle_half_to_double(vs[(kvh * T + t) * 8 + j / 32]);",
+                       "oracle_half_to_double(vs[(kvh * T + t) * 8]);")]),
     ("t5_code_map", [("t[n * K + 128 * g + 5 * b + i] = (int8_t)(c - 1);",
                       "t[n * K + 128 * g + 5 * b + i] = (int8_t)(1 - c);"),
                      ("value += (t[n * K + 128 * g + 5 * b + i] + 1) * power;",
