@@ -19,6 +19,7 @@ TQ_BINARY = 1
 TQ_TERNARY5 = 2  # five trits per byte (GEMV only)
 TQ_AFFINE2 = 3   # levels q in {0..3}, scale and bias per group (tq_gemv_affine)
 GROUP = 128
+TQ_KV_K_CODES, TQ_KV_K_SCALES, TQ_KV_V_CODES, TQ_KV_V_SCALES = 0, 1, 2, 3
 
 _STATUS = {0: "TQ_OK", 1: "TQ_ERR_NULL", 2: "TQ_ERR_SHAPE", 3: "TQ_ERR_GROUP",
            4: "TQ_ERR_VARIANT", 5: "TQ_ERR_VALUE", 6: "TQ_ERR_CODE", 7: "TQ_ERR_ALIGN",
@@ -28,7 +29,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 
 # every symbol include/tq.h declares
 EXPORTS = ("tq_codes_bytes", "tq_scales_count", "tq_pack", "tq_unpack", "tq_gemv", "tq_gemm",
-           "tq_embed", "tq_gemv_affine", "tq_last_error", "tq_last_error_index", "tq_version")
+           "tq_embed", "tq_gemv_affine", "tq_kv_bytes", "tq_kv_append", "tq_attn_workspace_bytes",
+           "tq_attn_decode", "tq_last_error", "tq_last_error_index", "tq_version")
 
 
 class TQError(RuntimeError):
@@ -70,6 +72,14 @@ def lib():
     L.tq_embed.restype = i32
     L.tq_gemv_affine.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp]
     L.tq_gemv_affine.restype = i32
+    L.tq_kv_bytes.argtypes = [i64, i64, i32]
+    L.tq_kv_bytes.restype = ctypes.c_size_t
+    L.tq_kv_append.argtypes = [vp, vp, i64, i64, i64, i64, vp, vp, vp, vp, vp]
+    L.tq_kv_append.restype = i32
+    L.tq_attn_workspace_bytes.argtypes = [i64, i64, i64]
+    L.tq_attn_workspace_bytes.restype = ctypes.c_size_t
+    L.tq_attn_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, ctypes.c_size_t, vp]
+    L.tq_attn_decode.restype = i32
     L.tq_last_error.argtypes = []
     L.tq_last_error.restype = ctypes.c_char_p
     L.tq_last_error_index.argtypes = []
@@ -214,4 +224,48 @@ def tq_gemv_affine(codes, scales, biases, x, y=None, group=GROUP, stream=None):
                                 _dev(biases, "biases", half), _dev(x, "x", half),
                                 _dev(y, "y", (torch.float32,)), N, K, group, _stream(stream)))
     return y
+
+
+# ------------------------------------------------------- 4-bit KV cache
+def tq_kv_bytes(n_kv, t_cap, part):
+    return lib().tq_kv_bytes(n_kv, t_cap, part)
+
+
+def tq_attn_workspace_bytes(T, n_q, n_kv):
+    return lib().tq_attn_workspace_bytes(T, n_q, n_kv)
+
+
+def tq_kv_append(k, v, pos, n_kv, t_cap, kc, ks, vc, vs, stream=None):
+    """Quantize k, v (float16 [n_tok][n_kv][256]) into cache positions
+    [pos, pos + n_tok).  kc / vc uint8 and ks / vs float16 (or int16) device
+    arrays of tq_kv_bytes(n_kv, t_cap, part) bytes."""
+    import torch
+    if k.shape != v.shape or k.dim() != 3 or k.shape[1] != n_kv or k.shape[2] != 256:
+        raise ValueError("k and v must be [n_tok][n_kv][256]")
+    half = (torch.float16, torch.int16)
+    for arr, part, name in ((kc, TQ_KV_K_CODES, "kc"), (ks, TQ_KV_K_SCALES, "ks"),
+                            (vc, TQ_KV_V_CODES, "vc"), (vs, TQ_KV_V_SCALES, "vs")):
+        if arr.numel() * arr.element_size() != tq_kv_bytes(n_kv, t_cap, part):
+            raise ValueError("%s holds %d bytes, %d needed" % (
+                name, arr.numel() * arr.element_size(), tq_kv_bytes(n_kv, t_cap, part)))
+    _check(lib().tq_kv_append(_dev(k, "k", half), _dev(v, "v", half), k.shape[0], pos, n_kv, t_cap,
+                              _dev(kc, "kc", (torch.uint8,)), _dev(ks, "ks", half),
+                              _dev(vc, "vc", (torch.uint8,)), _dev(vs, "vs", half), _stream(stream)))
+
+
+def tq_attn_decode(q, kc, ks, vc, vs, T, n_kv, t_cap, workspace, out=None, stream=None):
+    """Decode attention of q (float16 [n_q][256]) over cache positions [0, T).
+    workspace: float32 device array of tq_attn_workspace_bytes(T, n_q, n_kv)
+    bytes or more.  Returns out float32 [n_q][256]."""
+    import torch
+    n_q = q.shape[0]
+    if out is None:
+        out = torch.empty(n_q, 256, dtype=torch.float32, device=q.device)
+    half = (torch.float16, torch.int16)
+    _check(lib().tq_attn_decode(_dev(q, "q", half), _dev(kc, "kc", (torch.uint8,)), _dev(ks, "ks", half),
+                                _dev(vc, "vc", (torch.uint8,)), _dev(vs, "vs", half), T, n_q, n_kv,
+                                t_cap, _dev(out, "out", (torch.float32,)),
+                                _dev(workspace, "workspace", (torch.float32, torch.uint8)),
+                                workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
 

@@ -16,6 +16,13 @@ int32_t gemv5_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16
                       int64_t N, int64_t K, hipStream_t stream);
 int32_t gemv_affine_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
                             const uint16_t *x, float *y, int64_t N, int64_t K, hipStream_t stream);
+int64_t attn_chunk(int64_t T, int64_t n_kv);
+int32_t kv_append_enqueue(const uint16_t *k, const uint16_t *v, int64_t n_tok, int64_t pos, int64_t H,
+                          int64_t TC, uint8_t *kc, uint16_t *ks, uint8_t *vc, uint16_t *vs,
+                          hipStream_t stream);
+int32_t attn_decode_enqueue(const uint16_t *q, const uint8_t *kc, const uint16_t *ks,
+                            const uint8_t *vc, const uint16_t *vs, int64_t T, int64_t TC,
+                            int64_t n_q, int64_t n_kv, float *out, float *ws, hipStream_t stream);
 int32_t embed_enqueue(const uint8_t *codes, const uint16_t *scales, const int32_t *ids,
                       uint16_t *out, int64_t n_ids, int64_t N, int64_t K, int32_t variant,
                       hipStream_t stream);
@@ -30,6 +37,20 @@ int32_t check_device_args(const void *codes, const void *scales, const void *x, 
     if (!aligned(scales, 2)) return fail(TQ_ERR_ALIGN, "scales must be 2-byte aligned");
     if (!aligned(y, 4)) return fail(TQ_ERR_ALIGN, "output must be 4-byte aligned");
     return TQ_OK;
+}
+constexpr int64_t kMaxTC = (int64_t(1) << 31) - 32;
+
+int32_t check_kv(int64_t n_kv, int64_t t_cap) {
+    if (n_kv < 1 || n_kv > 64) return fail(TQ_ERR_SHAPE, "n_kv=%lld outside [1, 64]", (long long)n_kv);
+    if (t_cap < 32 || t_cap % 32 || t_cap > kMaxTC)
+        return fail(TQ_ERR_SHAPE, "t_cap=%lld must be a positive multiple of 32 below 2^31",
+                    (long long)t_cap);
+    return TQ_OK;
+}
+
+size_t attn_ws_bytes(int64_t T, int64_t n_q, int64_t n_kv) {
+    const int64_t chunk = attn_chunk(T, n_kv);
+    return size_t((T + chunk - 1) / chunk) * size_t(n_q) * (256 + 2) * sizeof(float);
 }
 }  // namespace
 }  // namespace tq
@@ -84,6 +105,64 @@ int32_t tq_embed(const uint8_t *codes, const uint16_t *scales, const int32_t *id
     if (!tq::aligned(out, 16)) return tq::fail(TQ_ERR_ALIGN, "output must be 16-byte aligned");
     return tq::embed_enqueue(codes, scales, ids, out, n_ids, N, K, variant,
                              static_cast<hipStream_t>(stream));
+}
+
+size_t tq_kv_bytes(int64_t n_kv, int64_t t_cap, int32_t part) {
+    if (n_kv < 1 || n_kv > 64 || t_cap < 32 || t_cap % 32 || t_cap > tq::kMaxTC) return 0;
+    switch (part) {
+        case TQ_KV_K_CODES:
+        case TQ_KV_V_CODES: return size_t(n_kv) * size_t(t_cap) * 128;
+        case TQ_KV_K_SCALES:
+        case TQ_KV_V_SCALES: return size_t(n_kv) * size_t(t_cap) * 16;
+        default: return 0;
+    }
+}
+
+int32_t tq_kv_append(const uint16_t *k, const uint16_t *v, int64_t n_tok, int64_t pos, int64_t n_kv,
+                     int64_t t_cap, uint8_t *kc, uint16_t *ks, uint8_t *vc, uint16_t *vs,
+                     void *stream) {
+    tq::clear_error();
+    if (int32_t rc = tq::check_kv(n_kv, t_cap)) return rc;
+    if (n_tok < 0 || pos < 0 || pos + n_tok > t_cap)
+        return tq::fail(TQ_ERR_SHAPE, "tokens [%lld, %lld) outside the capacity %lld", (long long)pos,
+                        (long long)(pos + n_tok), (long long)t_cap);
+    if (n_tok * n_kv > (int64_t(1) << 31) - 1)
+        return tq::fail(TQ_ERR_SHAPE, "n_tok * n_kv above 2^31 - 1");
+    if (n_tok == 0) return TQ_OK;
+    if (!k || !v || !kc || !ks || !vc || !vs) return tq::fail(TQ_ERR_NULL, "NULL pointer argument");
+    if (!tq::aligned(k, 2) || !tq::aligned(v, 2)) return tq::fail(TQ_ERR_ALIGN, "k and v must be 2-byte aligned");
+    if (!tq::aligned(kc, 16) || !tq::aligned(ks, 16) || !tq::aligned(vc, 16) || !tq::aligned(vs, 16))
+        return tq::fail(TQ_ERR_ALIGN, "cache arrays must be 16-byte aligned");
+    return tq::kv_append_enqueue(k, v, n_tok, pos, n_kv, t_cap, kc, ks, vc, vs,
+                                 static_cast<hipStream_t>(stream));
+}
+
+size_t tq_attn_workspace_bytes(int64_t T, int64_t n_q, int64_t n_kv) {
+    if (T < 1 || T > tq::kMaxTC || n_kv < 1 || n_kv > 64 || n_q < n_kv || n_q % n_kv || n_q / n_kv > 16)
+        return 0;
+    return tq::attn_ws_bytes(T, n_q, n_kv);
+}
+
+int32_t tq_attn_decode(const uint16_t *q, const uint8_t *kc, const uint16_t *ks, const uint8_t *vc,
+                       const uint16_t *vs, int64_t T, int64_t n_q, int64_t n_kv, int64_t t_cap,
+                       float *out, void *workspace, size_t workspace_bytes, void *stream) {
+    tq::clear_error();
+    if (int32_t rc = tq::check_kv(n_kv, t_cap)) return rc;
+    if (n_q < n_kv || n_q % n_kv || n_q / n_kv > 16)
+        return tq::fail(TQ_ERR_SHAPE, "n_q=%lld must be a multiple of n_kv=%lld, at most 16 times it",
+                        (long long)n_q, (long long)n_kv);
+    if (T < 1 || T > t_cap)
+        return tq::fail(TQ_ERR_SHAPE, "T=%lld outside [1, t_cap=%lld]", (long long)T, (long long)t_cap);
+    if (!q || !kc || !ks || !vc || !vs || !out || !workspace)
+        return tq::fail(TQ_ERR_NULL, "NULL pointer argument");
+    if (!tq::aligned(q, 16) || !tq::aligned(kc, 16) || !tq::aligned(ks, 16) || !tq::aligned(vc, 16) ||
+        !tq::aligned(vs, 16) || !tq::aligned(workspace, 16) || !tq::aligned(out, 4))
+        return tq::fail(TQ_ERR_ALIGN, "q, cache and workspace must be 16-byte aligned, out 4-byte");
+    const size_t need = tq::attn_ws_bytes(T, n_q, n_kv);
+    if (workspace_bytes < need)
+        return tq::fail(TQ_ERR_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    return tq::attn_decode_enqueue(q, kc, ks, vc, vs, T, t_cap, n_q, n_kv, out,
+                                   static_cast<float *>(workspace), static_cast<hipStream_t>(stream));
 }
 
 int32_t tq_gemv_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,

@@ -161,6 +161,63 @@ int32_t tq_gemv_affine(const uint8_t *codes, const uint16_t *scales, const uint1
                        const uint16_t *x, float *y, int64_t N, int64_t K, int32_t group,
                        void *stream);
 
+/* ---- 4-bit KV cache and decode attention (one layer, one sequence) ----
+ * The full-attention layers keep K and V in a 4-bit cache (thakicloud.github.io,
+ * "Bonsai 27B: ternary and 1-bit quantization", memory section: 64 KiB per
+ * token at FP16 for 16 layers x 2 x 4 KV heads x 256; aitrends.kr,
+ * "Ternary-Bonsai-27B-mlx-2bit", "Technical features").  Format (the pages
+ * give none): each head vector of 256 is cut into 8 groups of 32 dimensions,
+ * each with an FP16 scale d = fp16(amax / 7) (amax / 7 in fp32, rounded to
+ * nearest even) and per element the nibble q + 8, q = clamp(rint(x / d),
+ * -8, 7) (x / d in fp32, ties to even); the value is (nibble - 8) * d.
+ * Head dimension 256 only.  The four cache arrays (device, 16-byte aligned,
+ * caller-owned) hold n_kv heads x t_cap tokens (t_cap a multiple of 32):
+ *   K codes  [n_kv][t_cap][32 dwords]: dword 8c + g holds dims 32g + 8c + e,
+ *            e = 2p + h at bits 16h + 4p (p = 0..3, h = 0..1);
+ *   K scales [n_kv][t_cap][8] FP16;
+ *   V codes  [n_kv][t_cap/32][1024 dwords]: for a block of 32 tokens, dword
+ *            (16c + n) * 16 + j holds dim 16j + n of tokens tau(c, s), s = 2p + h
+ *            at bits 16h + 4p, tau(c, s) = 4c + s (s < 4), 16 + 4c + s - 4 (s >= 4);
+ *   V scales [n_kv][t_cap/32][256] FP16: index (8c + g) * 8 + s is group g of
+ *            token tau(c, s).
+ * Tokens at or past T are never read into a result, but the attention reads
+ * whole 32-token blocks: give the arrays finite contents (allocate them
+ * zero-filled). */
+#define TQ_KV_K_CODES 0
+#define TQ_KV_K_SCALES 1
+#define TQ_KV_V_CODES 2
+#define TQ_KV_V_SCALES 3
+
+/* Bytes of one cache array (part TQ_KV_*); 0 for an invalid request
+ * (n_kv outside [1, 64], t_cap not a positive multiple of 32 below 2^31). */
+size_t tq_kv_bytes(int64_t n_kv, int64_t t_cap, int32_t part);
+
+/* Device.  Quantizes n_tok new tokens k, v (uint16 fp16 bits
+ * [n_tok][n_kv][256], 2-byte aligned) into cache positions [pos, pos+n_tok).
+ * Positions outside [0, t_cap) return TQ_ERR_SHAPE; n_tok == 0 does nothing.
+ * Other tokens of the cache are left as they are (value codes of a 32-token
+ * block share dwords; the writes are atomic per dword). */
+int32_t tq_kv_append(const uint16_t *k, const uint16_t *v, int64_t n_tok, int64_t pos,
+                     int64_t n_kv, int64_t t_cap, uint8_t *kc, uint16_t *ks, uint8_t *vc,
+                     uint16_t *vs, void *stream);
+
+/* Bytes of device workspace tq_attn_decode needs for T tokens (0 when the
+ * shape is invalid). */
+size_t tq_attn_workspace_bytes(int64_t T, int64_t n_q, int64_t n_kv);
+
+/* Device.  Decode attention of one query token over cache positions
+ * [0, T): for query head h (KV head h / (n_q / n_kv)),
+ *   out[h] = sum_t softmax_t(q_h . k_t / sqrt(256)) v_t
+ * with k_t, v_t the dequantized cache vectors, in fp32.  q: uint16 fp16
+ * [n_q][256], 16-byte aligned; out: float [n_q][256]; workspace: device,
+ * 16-byte aligned, at least tq_attn_workspace_bytes(T, n_q, n_kv) bytes,
+ * overwritten.  n_q must be a multiple of n_kv, at most 16 times it;
+ * 1 <= T <= t_cap. */
+int32_t tq_attn_decode(const uint16_t *q, const uint8_t *kc, const uint16_t *ks,
+                       const uint8_t *vc, const uint16_t *vs, int64_t T, int64_t n_q,
+                       int64_t n_kv, int64_t t_cap, float *out, void *workspace,
+                       size_t workspace_bytes, void *stream);
+
 /* Text of the calling thread's last error ("" if none). */
 const char *tq_last_error(void);
 

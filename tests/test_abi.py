@@ -128,6 +128,44 @@ def test_gemv_affine_validates_on_host(args, status):
     assert L.tq_last_error()
 
 
+def test_kv_sizes_and_validation():
+    L = tq.lib()
+    assert tq.tq_kv_bytes(4, 262144, tq.TQ_KV_K_CODES) == 4 * 262144 * 128
+    assert tq.tq_kv_bytes(4, 262144, tq.TQ_KV_V_SCALES) == 4 * 262144 * 16
+    # 16 layers x 4 heads x (2 x 128 + 2 x 16) bytes per token: 4.5 bits per element
+    per_token = 16 * sum(tq.tq_kv_bytes(4, 32, p) for p in range(4)) // 32
+    assert per_token == 16 * 4 * 288 and 8 * per_token / (16 * 2 * 4 * 256) == 4.5
+    assert tq.tq_kv_bytes(4, 100, 0) == 0 and tq.tq_kv_bytes(0, 64, 0) == 0
+    assert tq.tq_kv_bytes(4, 64, 4) == 0
+    assert tq.tq_attn_workspace_bytes(0, 24, 4) == 0
+    assert tq.tq_attn_workspace_bytes(100, 25, 4) == 0          # not a multiple
+    assert tq.tq_attn_workspace_bytes(100, 68, 4) == 0          # group above 16
+    assert tq.tq_attn_workspace_bytes(100, 24, 4) > 0
+    p = ctypes.c_void_p
+    F = p(FAKE)
+    ws = tq.tq_attn_workspace_bytes(64, 24, 4)
+    cases = [  # (args to tq_attn_decode, status)
+        ((F, F, F, F, F, 64, 24, 4, 64, F, F, ws, None), 0),
+        ((F, F, F, F, F, 65, 24, 4, 64, F, F, ws, None), 2),
+        ((F, F, F, F, F, 0, 24, 4, 64, F, F, ws, None), 2),
+        ((F, F, F, F, F, 64, 24, 4, 60, F, F, ws, None), 2),
+        ((F, F, F, F, F, 64, 20, 8, 64, F, F, ws, None), 2),
+        ((F, F, F, F, F, 64, 24, 4, 64, F, F, ws - 4, None), 2),
+        ((F, p(0), F, F, F, 64, 24, 4, 64, F, F, ws, None), 1),
+        ((p(FAKE + 8), F, F, F, F, 64, 24, 4, 64, F, F, ws, None), 7),
+        ((F, F, F, F, F, 64, 24, 4, 64, p(FAKE + 2), F, ws, None), 7),
+    ]
+    for args, status in cases:
+        if status == 0:
+            continue            # a valid call would launch
+        assert L.tq_attn_decode(*args) == status, (args, L.tq_last_error())
+    assert L.tq_kv_append(F, F, 0, 0, 4, 64, F, F, F, F, None) == 0       # nothing to do
+    assert L.tq_kv_append(F, F, 2, 63, 4, 64, F, F, F, F, None) == 2
+    assert L.tq_kv_append(F, F, 1, 0, 4, 64, F, F, F, p(0), None) == 1
+    assert L.tq_kv_append(F, F, 1, 0, 4, 64, F, F, p(FAKE + 4), F, None) == 7
+    assert L.tq_kv_append(F, F, 1, 0, 65, 64, F, F, F, F, None) == 2
+
+
 def test_pack_errors():
     t = np.zeros((2, 128), np.int8)
     t[1, 5] = 2
