@@ -423,6 +423,59 @@ def affine2(torch, tq, gen, stream):
     return out
 
 
+def kv_attention(torch, tq, gen, stream):
+    """4-bit KV cache: decode attention of one token over T cached tokens at
+    the full-attention shape (4 KV heads, 24 query heads, head_dim 256),
+    graph-replayed; bytes = T * 4 heads * 288 (K and V codes 128 + 128, scales
+    16 + 16).  Rotating copies of the cache keep it out of the last-level
+    cache.  Also the append of 1 and 512 new tokens."""
+    out = {}
+    n_kv, n_q = 4, 24
+    for T in (4096, 32768, 102400, 262144):
+        per = n_kv * 288
+        copies = max(2, math.ceil((1 << 30) / (T * per)))
+        caches = []
+        for _ in range(copies):
+            parts = []
+            for part in range(4):
+                nb = tq.tq_kv_bytes(n_kv, T, part)
+                a = torch.randint(0, 256, (nb,), device=gen.dev, generator=gen.gen,
+                                  dtype=torch.int32).to(torch.uint8)
+                if part in (tq.TQ_KV_K_SCALES, tq.TQ_KV_V_SCALES):
+                    # finite positive scales: FP16 exponent fields 5..13
+                    h = a.view(torch.int16)
+                    h.copy_(torch.randint(0x1400, 0x3800, (nb // 2,), device=gen.dev,
+                                          generator=gen.gen, dtype=torch.int32).to(torch.int16))
+                parts.append(a)
+            caches.append(parts)
+        q = gen.act(n_q, 256)
+        ws = torch.empty(tq.tq_attn_workspace_bytes(T, n_q, n_kv) // 4, dtype=torch.float32,
+                         device=gen.dev)
+        o = torch.empty(n_q, 256, dtype=torch.float32, device=gen.dev)
+
+        def launch(i):
+            kc, ks, vc, vs = caches[i % copies]
+            tq.tq_attn_decode(q, kc, ks.view(torch.int16), vc, vs.view(torch.int16), T, n_kv, T, ws, o)
+
+        ms = graph_ms(torch, launch, 4 * copies)
+        nbytes = T * per
+        out["T%d" % T] = {"us": round(ms * 1e3, 2), "gbs": round(nbytes / ms / 1e6, 1),
+                          "frac_hbm": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4), "bytes": nbytes,
+                          "us_16_layers": round(16 * ms * 1e3, 1)}
+        del caches
+        torch.cuda.empty_cache()
+    TC = 4096
+    parts = [torch.zeros(tq.tq_kv_bytes(n_kv, TC, p), dtype=torch.uint8, device=gen.dev) for p in range(4)]
+    for n_tok in (1, 512):
+        k = gen.act(n_tok * n_kv, 256).view(n_tok, n_kv, 256)
+        v = gen.act(n_tok * n_kv, 256).view(n_tok, n_kv, 256)
+        ms = graph_ms(torch, lambda i: tq.tq_kv_append(k, v, (i * n_tok) % (TC - n_tok), n_kv, TC,
+                                                       parts[0], parts[1].view(torch.int16), parts[2],
+                                                       parts[3].view(torch.int16)), 32)
+        out["append_%d_tokens" % n_tok] = {"us": round(ms * 1e3, 2)}
+    return out
+
+
 def copy_calibration():
     import torch
     dev = torch.device("cuda:0")
@@ -572,6 +625,7 @@ def main():
         line["binary_and_lm_head"] = binary_and_lm_head(torch, tq, gen, stream)
         line["ternary5"] = ternary5(torch, tq, gen, stream)
         line["affine2"] = affine2(torch, tq, gen, stream)
+        line["kv4_attention"] = kv_attention(torch, tq, gen, stream)
         del bufs
         torch.cuda.empty_cache()
         line["stack_sweep"] = stack_sweep(torch, tq, gen, stream)
