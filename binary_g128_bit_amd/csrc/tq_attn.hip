@@ -24,9 +24,9 @@
 // Decode attention.  Scores come from S^T = K Q^T on v_mfma_f32_16x16x32_f16
 // with the keys as the A operand (16 tokens x 32 dims of one scale group)
 // and the 16-padded query group as B.  A code nibble goes to mantissa bits
-// [6,10) under exponent 15, the exact FP16 1 + nibble/16, so
-// (nibble - 8) = 16 a - 24 and a group's score is d (16 D - 24 sum q): exact
-// products, the scale applied once per group.  The softmax is online in the
+// [6,10) under exponent 19, the exact FP16 16 + nibble, so the MFMA returns
+// sum (16 + nibble) q exactly and a group's score is d (D - 24 sum q): the
+// scale applied once per group and token.  The softmax is online in the
 // log2 domain.  O^T = V^T P^T takes the values as A (16 dims x 32 tokens)
 // and P^T scaled by each token's value scale (FP16) as B; the token order of
 // the K dimension is the one the score tiles leave in each lane, so P needs
@@ -59,12 +59,18 @@ __device__ __forceinline__ f32x4 mfma(half8 a, half8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// 8 nibbles of a code dword as FP16 1 + nibble/16, pairs in order.
-__device__ __forceinline__ half8 decode8(uint32_t w) {
-    constexpr uint32_t kMask = 0x03C003C0u, kExp = 0x3C003C00u;
-    return as_half8(((w << 6) & kMask) | kExp, ((w << 2) & kMask) | kExp, ((w >> 2) & kMask) | kExp,
-                    ((w >> 6) & kMask) | kExp);
+// 8 nibbles of a code dword as FP16 values linear in the nibble, pairs in
+// order: nibble at mantissa bits [6,10) under exponent field E, i.e.
+// 2^(E-15) (1 + nibble/16).  E = 15 gives 1 + nibble/16, E = 19 gives
+// 16 + nibble.  The mask stays in a VGPR (gfx9 VOP3 takes no literal), so each
+// pair is one shift and one v_and_or_b32.
+template <uint32_t EXP2>
+__device__ __forceinline__ half8 decode8(uint32_t w, uint32_t mask) {
+    return as_half8(((w << 6) & mask) | EXP2, ((w << 2) & mask) | EXP2, ((w >> 2) & mask) | EXP2,
+                    ((w >> 6) & mask) | EXP2);
 }
+constexpr uint32_t kExp15 = 0x3C003C00u;  // 1 + nibble/16
+constexpr uint32_t kExp19 = 0x4C004C00u;  // 16 + nibble
 
 // token offset within a 32-token block of K slot s of lane group c
 __device__ __forceinline__ int tau(int c, int s) { return s < 4 ? 4 * c + s : 12 + 4 * c + s; }
@@ -136,6 +142,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
     const int t_begin = ck * chunk, t_end = min(T, t_begin + chunk);
     const int nq = R;  // query heads of this KV head
 
+    uint32_t mask = 0x03C003C0u;
+    asm volatile("" : "+v"(mask));
     // query as the B operand: B[k = 8c + s of group g][n] = q[n][32g + 8c + s]
     half8 qb[8];
     float qs24[8];
@@ -150,7 +158,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
         for (int s = 0; s < 8; ++s) sq += (float)qb[g][s];
         sq += __shfl_xor(sq, 16);
         sq += __shfl_xor(sq, 32);
-        qs24[g] = 24.0f * sq;
+        qs24[g] = -24.0f * sq;
     }
 
     f32x4 oacc[16];
@@ -162,6 +170,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
     const float zs = kLog2e / 16.0f;  // 1 / sqrt(256), log2 domain
 
     for (int tb = t_begin + 32 * wave; tb < t_end; tb += 32 * kWaves) {
+        const int64_t blk = tb >> 5;
         // scores of the tile's two 16-token halves: z[u][i] for token
         // tb + 16u + 4c + i, head n
         float z[2][4];
@@ -179,12 +188,12 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
             float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int g = 0; g < 8; ++g) {
-                const f32x4 D = mfma(decode8(kw[g]), qb[g], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+                const f32x4 D = mfma(decode8<kExp19>(kw[g], mask), qb[g], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t pair = sv[i][g >> 1];
                     const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)(g & 1 ? pair >> 16 : pair));
-                    acc[i] = __builtin_fmaf(d, __builtin_fmaf(16.0f, D[i], -qs24[g]), acc[i]);
+                    acc[i] = __builtin_fmaf(d, D[i] + qs24[g], acc[i]);
                 }
             }
 #pragma unroll
@@ -217,7 +226,6 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
         // P^T scaled by the value scales, per group: B'[k = s][n] = p_s d_V
         const half2_t p2[4] = {half2_t{(_Float16)p[0], (_Float16)p[1]}, half2_t{(_Float16)p[2], (_Float16)p[3]},
                                half2_t{(_Float16)p[4], (_Float16)p[5]}, half2_t{(_Float16)p[6], (_Float16)p[7]}};
-        const int64_t blk = tb >> 5;
         const u32x4 *vsp = reinterpret_cast<const u32x4 *>(vs + ((size_t)h * (TC >> 5) + blk) * 256 + 64 * c);
         half8 bp[8];
 #pragma unroll
@@ -244,7 +252,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
         const uint32_t vw[16] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3],
                                  v2[0], v2[1], v2[2], v2[3], v3[0], v3[1], v3[2], v3[3]};
 #pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[j] = mfma(decode8(vw[j]), bp[j >> 1], oacc[j]);
+        for (int j = 0; j < 16; ++j) oacc[j] = mfma(decode8<kExp15>(vw[j], mask), bp[j >> 1], oacc[j]);
     }
 
     // this wave's (max, sum, output) per head into LDS: O = 16 D - 24 cs
@@ -288,32 +296,60 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
     }
 }
 
-// Merge the chunks: one workgroup per query head, thread = dimension.
+constexpr int kMaxChunks = 1024;
+
+// Merge the chunks: one workgroup per query head.  The chunks' weights
+// 2^(m_c - M) come first, in parallel, into LDS; then thread = dimension
+// sums the chunk outputs with eight loads in flight.
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restrict__ ws, int nchunks,
                                                            int nqh, float *__restrict__ out) {
-    const int hq = blockIdx.x, dim = threadIdx.x;
+    __shared__ float wgt[kMaxChunks];
+    __shared__ float part[2][4];
+    const int hq = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t stride = (size_t)nqh * (kHD + 2);
+    const float *base = ws + (size_t)hq * (kHD + 2);
     float mx = -INFINITY;
-    for (int ck = 0; ck < nchunks; ++ck) mx = fmaxf(mx, ws[((size_t)ck * nqh + hq) * (kHD + 2) + kHD]);
-    float o = 0.0f, l = 0.0f;
-    for (int ck = 0; ck < nchunks; ++ck) {
-        const float *src = ws + ((size_t)ck * nqh + hq) * (kHD + 2);
-        const float e = exp2f(src[kHD] - mx);
-        o += e * src[dim];
-        l += e * src[kHD + 1];
+    for (int ck = tid; ck < nchunks; ck += 256) mx = fmaxf(mx, base[ck * stride + kHD]);
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+    if (lane == 0) part[0][wave] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(part[0][0], part[0][1]), fmaxf(part[0][2], part[0][3]));
+    float l = 0.0f;
+    for (int ck = tid; ck < nchunks; ck += 256) {
+        const float e = exp2f(base[ck * stride + kHD] - mx);
+        wgt[ck] = e;
+        l += e * base[ck * stride + kHD + 1];
     }
-    out[(size_t)hq * kHD + dim] = o / l;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) l += __shfl_xor(l, m);
+    if (lane == 0) part[1][wave] = l;
+    __syncthreads();
+    l = part[1][0] + part[1][1] + part[1][2] + part[1][3];
+    float o = 0.0f;
+    int ck = 0;
+    for (; ck + 8 <= nchunks; ck += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = base[(ck + u) * stride + tid];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o = __builtin_fmaf(wgt[ck + u], v[u], o);
+    }
+    for (; ck < nchunks; ++ck) o = __builtin_fmaf(wgt[ck], base[ck * stride + tid], o);
+    out[(size_t)hq * kHD + tid] = o / l;
 }
 
 }  // namespace
 
-// Tokens per attention chunk: a multiple of 32 * kWaves with at least ~2
-// workgroups per CU over the KV heads, and at most 4096.
+// Tokens per attention chunk: a multiple of 32 * kWaves giving about two
+// workgroups per CU over the KV heads, and never more than kMaxChunks chunks.
 int64_t attn_chunk(int64_t T, int64_t n_kv) {
     const int64_t step = 32 * kWaves;
     int64_t want = (T * n_kv + 511) / 512;
+    const int64_t floor_c = (T + kMaxChunks - 1) / kMaxChunks;
+    if (want < floor_c) want = floor_c;
     int64_t c = (want + step - 1) / step * step;
     if (c < step) c = step;
-    if (c > 4096) c = 4096;
     return c;
 }
 
