@@ -39,6 +39,8 @@
 // DPP moves (quad_perm, row_half_mirror, row_mirror) and swizzles beyond 16.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -72,7 +74,6 @@ struct Masks {
     }
 };
 
-constexpr uint32_t kExp1 = 0x04000400u;  // exponent field 1 in both halves
 
 typedef uint64_t u64;
 
@@ -476,7 +477,17 @@ __device__ __forceinline__ void load_bias(const uint16_t *__restrict__ biases, i
 // columns j, j + LPR, ..., so after the workgroup has staged x into LDS once
 // (permuted, with the chunk constants), each lane copies its NU chunk slots
 // into VGPRs and the block loop reads no LDS at all.
-template <int VARIANT, int LPR, int NU, int WAVES, bool RAGGED>
+//
+// Two block loops.  PIPE (ternary, scales readable as aligned dwords): each
+// chunk's registers are refilled with the block two ahead as soon as the
+// chunk is consumed, every load unconditional (clamped to the range's last
+// block, a cache hit), so the load order is the same on every path and the
+// compiler's wait before each chunk is for that chunk only: about two blocks
+// per wave stay in flight while the wave computes.  The scale comes from the
+// aligned dword that holds it (a genuine 32-bit value: 16-bit registers are
+// packed in pairs, and the packing waits for both loads).  Otherwise a plain
+// ping-pong of two register sets, each loaded whole one block ahead.
+template <int VARIANT, int LPR, int NU, int WAVES, bool RAGGED, bool PIPE>
 __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__restrict__ codes,
                                                                const uint16_t *__restrict__ scales,
                                                                const uint16_t *__restrict__ biases,
@@ -485,6 +496,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
     extern __shared__ uint32_t xs[];
     using XU = XUnit<VARIANT>;
     constexpr bool AFF = VARIANT == TQ_AFFINE2;
+    static_assert(!(PIPE && AFF), "the pipelined loop is for ternary codes");
     constexpr int XN = XReg<VARIANT>::N;
     constexpr int THREADS = 64 * WAVES;
     constexpr int RS = 64 / LPR;  // rows per block (one per lane segment)
@@ -492,7 +504,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
     constexpr int XMAX = (CAP * 4 + THREADS - 1) / THREADS;
     const int G = K >> 7, CPR = 2 * G;
     const int nunits = CPR * 4;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    // wave-uniform (scalar) block bookkeeping: the loops branch on SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int seg = lane / LPR, j = lane % LPR;
     const int nblocks = (N + RS - 1) / RS;
     const int b_begin = (int)(((long long)blockIdx.x * nblocks) / gridDim.x);
@@ -504,64 +518,123 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
     for (int k = 0; k < XMAX; ++k)
         xu[k].load(x, min(min((int)threadIdx.x + k * THREADS, CAP * 4 - 1), nunits - 1));
     __builtin_amdgcn_sched_barrier(0);
-    u32x4 ca[NU][1], cb[NU][1];
-    uint32_t sa[NU][1], sb[NU][1];
-    uint32_t ba[NU][1] = {}, bb_[NU][1] = {};
-    int b = b_begin + wave;
-    int row[1] = {min(min(b, b_end - 1) * RS + seg, N - 1)};
-    if constexpr (AFF) load_bias<LPR, NU, RAGGED>(biases, row[0], j, CPR, G, ba);
-    load_block<VARIANT, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, ca, sa);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int k = 0; k < XMAX; ++k) {
-        const int u = min((int)threadIdx.x + k * THREADS, CAP * 4 - 1);
-        xu[k].store(xs, u, u < nunits);
-    }
-    __syncthreads();
-    uint32_t xr[NU][XN];
-#pragma unroll
-    for (int i = 0; i < NU; ++i) {
-        const uint32_t *slot = xs + (j + i * LPR) * XU::CHUNK_DW;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const u32x4 v = reinterpret_cast<const u32x4 *>(slot)[q];
-            xr[i][4 * q] = v[0];
-            xr[i][4 * q + 1] = v[1];
-            xr[i][4 * q + 2] = v[2];
-            xr[i][4 * q + 3] = v[3];
-        }
-        xr[i][32] = slot[32];
-        if constexpr (AFF) xr[i][33] = slot[33];
-    }
 
-    auto block = [&](const u32x4 (&c)[NU][1], const uint32_t (&sv)[NU][1],
-                     const uint32_t (&bv)[NU][1], int bb) __attribute__((always_inline)) {
-        float acc = 0.0f;
+    // x staged into LDS, then this lane's chunk slots into registers
+    auto stage_x = [&](uint32_t (&xr)[NU][XN]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < XMAX; ++k) {
+            const int u = min((int)threadIdx.x + k * THREADS, CAP * 4 - 1);
+            xu[k].store(xs, u, u < nunits);
+        }
+        __syncthreads();
 #pragma unroll
         for (int i = 0; i < NU; ++i) {
-            chunk_dot_reg<VARIANT>(c[i][0], xr[i], sv[i][0], bv[i][0], acc, km);
-            __builtin_amdgcn_sched_barrier(0);
+            const uint32_t *slot = xs + (j + i * LPR) * XU::CHUNK_DW;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const u32x4 v = reinterpret_cast<const u32x4 *>(slot)[q];
+                xr[i][4 * q] = v[0];
+                xr[i][4 * q + 1] = v[1];
+                xr[i][4 * q + 2] = v[2];
+                xr[i][4 * q + 3] = v[3];
+            }
+            xr[i][32] = slot[32];
+            if constexpr (AFF) xr[i][33] = slot[33];
         }
-        const float out = seg_sum<LPR>(acc) * XU::kRowScale;
-        const int rr = bb * RS + seg;
-        if (j == 0 && rr < N) y[rr] = out;
     };
-    for (; b < b_end; b += 2 * WAVES) {
-        const int b2 = b + WAVES;
-        if (b2 < b_end) {
-            row[0] = b2 * RS + seg < N ? b2 * RS + seg : N - 1;
-            if constexpr (AFF) load_bias<LPR, NU, RAGGED>(biases, row[0], j, CPR, G, bb_);
-            load_block<VARIANT, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, cb, sb);
+    uint32_t xr[NU][XN];
+
+    if constexpr (PIPE) {
+        const int blast = b_end - 1;
+        const int b0 = b_begin + wave;
+        const int nb = b0 < b_end ? (b_end - b0 + WAVES - 1) / WAVES : 0;  // this wave's blocks
+        // chunk columns of this lane (clamped into the row when ragged) and
+        // the half of the scale dword that holds each chunk's group scale
+        int col[NU];
+        uint32_t hsh[NU];
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            col[i] = RAGGED ? min(j + i * LPR, CPR - 1) : j + i * LPR;
+            hsh[i] = ((uint32_t)(col[i] >> 1) & 1u) * 16u;
         }
-        block(ca, sa, ba, b);
-        if (b2 >= b_end) break;
-        const int b3 = b2 + WAVES;
-        if (b3 < b_end) {
-            row[0] = b3 * RS + seg < N ? b3 * RS + seg : N - 1;
-            if constexpr (AFF) load_bias<LPR, NU, RAGGED>(biases, row[0], j, CPR, G, ba);
-            load_block<VARIANT, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, ca, sa);
+        const uint32_t *sc32 = reinterpret_cast<const uint32_t *>(scales);
+        auto load_chunk = [&](int bb, int i, u32x4 (&c)[NU], uint32_t (&sv)[NU])
+                              __attribute__((always_inline)) {
+            const int r = min(min(bb, blast) * RS + seg, N - 1);
+            sv[i] = sc32[((size_t)r * G + (col[i] >> 1)) >> 1];
+            c[i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(codes + (size_t)r * CPR * 16) + col[i]);
+        };
+        u32x4 ca[NU], cb[NU];
+        uint32_t sa[NU], sb[NU];
+#pragma unroll
+        for (int i = 0; i < NU; ++i) load_chunk(b0, i, ca, sa);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_x(xr);
+#pragma unroll
+        for (int i = 0; i < NU; ++i) load_chunk(b0 + WAVES, i, cb, sb);
+
+        auto block = [&](auto refill, u32x4 (&c)[NU], uint32_t (&sv)[NU], int bb, int bn)
+                         __attribute__((always_inline)) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NU; ++i) {
+                chunk_dot_reg<VARIANT>(c[i], xr[i], sv[i] >> hsh[i], 0u, acc, km);
+                if constexpr (decltype(refill)::value) load_chunk(bn, i, c, sv);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const float out = seg_sum<LPR>(acc) * XU::kRowScale;
+            const int rr = bb * RS + seg;
+            if (j == 0 && rr < N) y[rr] = out;
+        };
+        using Refill = std::integral_constant<bool, true>;
+        using Last = std::integral_constant<bool, false>;
+        int k = 0;
+        for (; k + 1 < nb; k += 2) {
+            block(Refill{}, ca, sa, b0 + k * WAVES, b0 + (k + 2) * WAVES);
+            block(Refill{}, cb, sb, b0 + (k + 1) * WAVES, b0 + (k + 3) * WAVES);
         }
-        block(cb, sb, bb_, b2);
+        if (k < nb) block(Last{}, ca, sa, b0 + k * WAVES, 0);
+    } else {
+        u32x4 ca[NU][1], cb[NU][1];
+        uint32_t sa[NU][1], sb[NU][1];
+        uint32_t ba[NU][1] = {}, bb_[NU][1] = {};
+        int b = b_begin + wave;
+        int row[1] = {min(min(b, b_end - 1) * RS + seg, N - 1)};
+        if constexpr (AFF) load_bias<LPR, NU, RAGGED>(biases, row[0], j, CPR, G, ba);
+        load_block<VARIANT, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, ca, sa);
+        __builtin_amdgcn_sched_barrier(0);
+        stage_x(xr);
+
+        auto block = [&](const u32x4 (&c)[NU][1], const uint32_t (&sv)[NU][1],
+                         const uint32_t (&bv)[NU][1], int bb) __attribute__((always_inline)) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int i = 0; i < NU; ++i) {
+                chunk_dot_reg<VARIANT>(c[i][0], xr[i], sv[i][0], bv[i][0], acc, km);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            const float out = seg_sum<LPR>(acc) * XU::kRowScale;
+            const int rr = bb * RS + seg;
+            if (j == 0 && rr < N) y[rr] = out;
+        };
+        for (; b < b_end; b += 2 * WAVES) {
+            const int b2 = b + WAVES;
+            if (b2 < b_end) {
+                row[0] = b2 * RS + seg < N ? b2 * RS + seg : N - 1;
+                if constexpr (AFF) load_bias<LPR, NU, RAGGED>(biases, row[0], j, CPR, G, bb_);
+                load_block<VARIANT, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, cb, sb);
+            }
+            block(ca, sa, ba, b);
+            if (b2 >= b_end) break;
+            const int b3 = b2 + WAVES;
+            if (b3 < b_end) {
+                row[0] = b3 * RS + seg < N ? b3 * RS + seg : N - 1;
+                if constexpr (AFF) load_bias<LPR, NU, RAGGED>(biases, row[0], j, CPR, G, ba);
+                load_block<VARIANT, LPR, NU, 1, RAGGED>(codes, scales, row, j, CPR, G, ca, sa);
+            }
+            block(cb, sb, bb_, b2);
+        }
     }
 }
 
@@ -682,12 +755,23 @@ hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint1
     const int nblocks = (N + RS - 1) / RS;
     const int grid = max(1, min(device_cus(), (nblocks + kXregWaves - 1) / kXregWaves));
     constexpr size_t lds = lds_bytes<VARIANT, LPR, NU>();
-    if ((K / 128) * 2 == LPR * NU)
-        hipLaunchKernelGGL((gemv_xreg_kernel<VARIANT, LPR, NU, kXregWaves, false>), dim3(grid),
-                           dim3(64 * kXregWaves), lds, stream, codes, scales, biases, x, y, N, K);
-    else
-        hipLaunchKernelGGL((gemv_xreg_kernel<VARIANT, LPR, NU, kXregWaves, true>), dim3(grid),
-                           dim3(64 * kXregWaves), lds, stream, codes, scales, biases, x, y, N, K);
+    const bool exact = (K / 128) * 2 == LPR * NU;
+    // the pipelined loop reads each scale from its aligned dword: an even
+    // group count keeps every row's scales dword aligned
+    const bool pipe = VARIANT == TQ_TERNARY && (K / 128) % 2 == 0 &&
+                      (reinterpret_cast<uintptr_t>(scales) & 3) == 0;
+#define TQ_XL(R, P)                                                                               \
+    hipLaunchKernelGGL((gemv_xreg_kernel<VARIANT, LPR, NU, kXregWaves, R, P>), dim3(grid),         \
+                       dim3(64 * kXregWaves), lds, stream, codes, scales, biases, x, y, N, K)
+    if constexpr (VARIANT == TQ_TERNARY) {
+        if (pipe && exact) TQ_XL(false, true);
+        else if (pipe) TQ_XL(true, true);
+        else TQ_XL(true, false);
+    } else {
+        if (exact) TQ_XL(false, false);
+        else TQ_XL(true, false);
+    }
+#undef TQ_XL
     return hipGetLastError();
 }
 

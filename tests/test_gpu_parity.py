@@ -156,6 +156,22 @@ def test_gemv_deterministic_and_canaries():
     assert not torch.isnan(y).any()
 
 
+@pytest.mark.parametrize("N,K", [(96, 5120), (65, 17408)])
+def test_gemv_scales_2byte_aligned(N, K):
+    """A scale array that is only 2-byte aligned (a view one half in) takes
+    the per-scale loads instead of the aligned-dword ones; same results."""
+    codes, s, X = case(9300 + N, N, K, 1, TERN, exact=False)
+    big = torch.zeros(N * (K // 128) + 1, dtype=torch.float16, device="cuda")
+    big[1:] = up(s).reshape(-1)
+    sv = big[1:].view(N, K // 128)
+    y = tq.tq_gemv(up(codes), sv, up(X[0]))
+    y_al = tq.tq_gemv(up(codes), up(s), up(X[0]))
+    torch.cuda.synchronize()
+    yref, A = oracle.gemv(codes, s, X[0], N, K, threads=THREADS)
+    assert_tol(y.cpu().numpy().astype(np.float64), yref, A, "2-byte aligned scales")
+    assert_tol(y_al.cpu().numpy().astype(np.float64), yref, A, "aligned scales")
+
+
 def test_gemv_rejects_k_above_limit():
     N, K = 4, 65536 + 128
     codes = torch.zeros(N * K // 4, dtype=torch.uint8, device="cuda")
