@@ -609,7 +609,7 @@ def main():
                            "gate_17408x5120_unfused": round(packed_bytes(Ng, Kg) / gate_ms / 1e6, 1)},
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_xreg_kernel<0,16,5,8,false> (ternary) on [gate;up] 34816x5120",
+            "kernel": "gemv_xreg_kernel<0,16,5,8,false,true> (ternary, pipelined) on [gate;up] 34816x5120",
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
