@@ -39,6 +39,7 @@ namespace {
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4a __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr size_t kMaxLds5 = 163840;
 constexpr int kUnitDw = 13;      // code dwords per two-group unit
@@ -346,6 +347,243 @@ __global__ __launch_bounds__(64 * WAVES) void gemv5_kernel(const uint8_t *__rest
     }
 }
 
+// ---------------------------------------------------------------------------
+// Register-activation kernel (the common case: even group count, dword-aligned
+// scales, K <= 20480).
+//
+// A chunk is half a group: bytes 13s .. 13s + 12 of group g (s = 0, 1), trits
+// 65s + 5k + i of the group for byte k, digit i.  Each code byte is looked up
+// in a 64 KiB LDS table whose 32-bit entry holds the byte's five digits as
+// 2-bit slots (digit i at bits [2i, 2i+2)); entry v of lane l sits at
+// (v * 64 + l) * 4, so the 64 lanes of a lookup hit 64 different banks.  Two
+// entries merge into one dword (bytes 2q and 2q + 1: low and high half), and
+// the dword is decoded exactly as the 2-bit ternary slots are: copy d gives
+// slot 4 (M4, bits [8,10) under exponent 3) and slot 3 (M16, bits [6,8) under
+// exponent 5); copy d << 6 gives slot 2 (E, bits [10,12)), slot 1 (M4) and
+// slot 0 (M16).  The chunk's 13th byte fills the low half of a seventh dword.
+// Against it stand activation pairs (x[t], x[t + 5]) for t = 65s + 10q + i, or
+// (x[65s + 60 + i], 0) for the 13th byte, with zeros past the group's 128
+// trits; the chunk constant -(sum over the pairs of (1 + offset) (x_lo + x_hi))
+// * 2^-14 removes the slot offsets and the t = c - 1 shift.  Lanes keep their
+// chunks' 35 pairs and constant in registers; loads are unconditional
+// (clamped) refills, as in the 2-bit ternary kernel's pipelined loop.
+constexpr int kC5Pairs = 33;                 // pair dwords per chunk (6 dwords x 5 slots + 3)
+constexpr int kC5SlotDw = 36;                // LDS dwords per chunk slot: pairs, constant, pad
+constexpr int kLut5Bytes = 256 * 64 * 4;     // 64 KiB table, one copy per lane
+constexpr int kC5MaxNU = 5;
+
+// Digits of byte v as 2-bit slots; bytes above 242 hold no code and map to 0.
+__device__ __forceinline__ uint32_t slot_codes(uint32_t v) {
+    if (v >= 243u) return 0u;
+    uint32_t r = 0;
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+        r |= (v % 3u) << (2 * i);
+        v /= 3u;
+    }
+    return r;
+}
+
+// FP16 pair (1 + offset, 1 + offset) of slot i: M16 slots 0 and 3 (17), M4
+// slots 1 and 4 (5), E slot 2 (1).
+__device__ __forceinline__ uint32_t c5_zweight(int i) {
+    return (i == 0 || i == 3) ? 0x4C404C40u : (i == 1 || i == 4) ? 0x45004500u : 0x3C003C00u;
+}
+
+// The 35 decoded slots of one chunk against its registers, into a (units of
+// 2^-14).  w is the chunk's 16-byte window and off the chunk's byte offset in
+// it; lbase is lane * 4.
+__device__ __forceinline__ void c5_chunk(const u32x4 &w, uint32_t off, const uint32_t (&xr)[kC5Pairs],
+                                         const char *lut, uint32_t lbase, float &a,
+                                         uint32_t m8, uint32_t m6) {
+    const uint32_t w0 = __builtin_amdgcn_alignbyte(w[1], w[0], off);
+    const uint32_t w1 = __builtin_amdgcn_alignbyte(w[2], w[1], off);
+    const uint32_t w2 = __builtin_amdgcn_alignbyte(w[3], w[2], off);
+    const uint32_t w3 = __builtin_amdgcn_alignbyte(w[3], w[3], off);
+    const uint32_t wd[4] = {w0, w1, w2, w3};
+    // addresses bytes: [lane * 4, code byte k, 0, 0] = byte * 256 + lane * 4
+    uint32_t ad[13];
+#pragma unroll
+    for (int k = 0; k < 13; ++k)
+        ad[k] = __builtin_amdgcn_perm(wd[k >> 2], lbase, 0x0C0C0000u | ((uint32_t)(4 + (k & 3)) << 8));
+    // bytes 2q and 2q + 1 read straight into the low and high half of one
+    // register (the entries fit in 16 bits): the merge costs no VALU op
+    uint32_t dq[6];
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+        u16x2 v;
+        v.x = *reinterpret_cast<const uint16_t *>(lut + ad[2 * q]);
+        v.y = *reinterpret_cast<const uint16_t *>(lut + ad[2 * q + 1]);
+        dq[q] = __builtin_bit_cast(uint32_t, v);
+    }
+    const uint32_t e12 = *reinterpret_cast<const uint16_t *>(lut + ad[12]);
+#pragma unroll
+    for (int q = 0; q < 6; ++q) {
+        const uint32_t d = dq[q];
+        const uint32_t c6 = d << 6;
+        const uint32_t *xp = xr + 5 * q;
+        a = dot2((d & m8) | 0x0C000C00u, xp[4], a);   // M4  slot 4
+        a = dot2((d & m6) | 0x14001400u, xp[3], a);   // M16 slot 3
+        a = dot2(c6 & 0x0C000C00u, xp[2], a);         // E   slot 2
+        a = dot2((c6 & m8) | 0x0C000C00u, xp[1], a);  // M4  slot 1
+        a = dot2((c6 & m6) | 0x14001400u, xp[0], a);  // M16 slot 0
+    }
+    // the 13th byte: the low half keeps all five digits but only slots 0..2
+    // are decoded (slots 3, 4 shift to bits [12,16), outside every mask);
+    // digits 3, 4 go to the high half's slots 0, 1; three slots of d << 6
+    const uint32_t d7 = e12 | ((e12 >> 6) << 16);
+    const uint32_t c7 = d7 << 6;
+    a = dot2(c7 & 0x0C000C00u, xr[32], a);            // E   slot 2: (x62, 0)
+    a = dot2((c7 & m8) | 0x0C000C00u, xr[31], a);     // M4  slot 1: (x61, x64)
+    a = dot2((c7 & m6) | 0x14001400u, xr[30], a);     // M16 slot 0: (x60, x63)
+}
+
+// dynamic LDS of the register kernel: chunk slots and x (the 64 KiB table is static)
+template <int LPR, int NU>
+constexpr size_t lds5x_bytes(int K) {
+    return (size_t)LPR * NU * kC5SlotDw * 4 + (size_t)K * 2;
+}
+
+template <int LPR, int NU, int WAVES, bool RAGGED>
+__global__ __launch_bounds__(64 * WAVES) void gemv5x_kernel(const uint8_t *__restrict__ codes,
+                                                            const uint16_t *__restrict__ scales,
+                                                            const uint16_t *__restrict__ x,
+                                                            float *__restrict__ y, int N, int K) {
+    // the table is static LDS (offset 0, folded into every lookup's address);
+    // the chunk slots and x follow it in dynamic LDS
+    __shared__ u32x4 lut5[kLut5Bytes / 16];
+    extern __shared__ u32x4 lds5x[];
+    constexpr int THREADS = 64 * WAVES;
+    constexpr int RS = 64 / LPR;  // rows per block
+    constexpr int CAP = LPR * NU;
+    char *lut = reinterpret_cast<char *>(lut5);
+    uint32_t *xs = reinterpret_cast<uint32_t *>(lds5x);
+    uint16_t *xn = reinterpret_cast<uint16_t *>(xs + CAP * kC5SlotDw);
+    const int G = K >> 7, CPR = 2 * G;
+    const int rbytes = (26 * G + 15) & ~15;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int seg = lane / LPR, j = lane % LPR;
+    const int nblocks = (N + RS - 1) / RS;
+    const int b_begin = (int)(((long long)blockIdx.x * nblocks) / gridDim.x);
+    const int b_end = (int)(((long long)(blockIdx.x + 1) * nblocks) / gridDim.x);
+    const int blast = b_end - 1;
+    const int b0 = b_begin + wave;
+    const int nb = b0 < b_end ? (b_end - b0 + WAVES - 1) / WAVES : 0;
+
+    // chunk column of slot i (clamped into the row when ragged), recomputed
+    // where used rather than held: registers are the limit here
+    auto hcol = [&](int i) __attribute__((always_inline)) {
+        return RAGGED ? min(j + i * LPR, CPR - 1) : j + i * LPR;
+    };
+    const uint32_t *sc32 = reinterpret_cast<const uint32_t *>(scales);
+    auto load_chunk = [&](int bb, int i, u32x4 (&c)[NU], uint32_t (&sv)[NU]) __attribute__((always_inline)) {
+        const int r = min(min(bb, blast) * RS + seg, N - 1);
+        const int h = hcol(i);
+        sv[i] = sc32[((size_t)r * G + (h >> 1)) >> 1];
+        c[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4a *>(
+            codes + (size_t)r * rbytes + ((13 * h) & ~3)));
+    };
+
+    // 1. x (natural order) into registers, the first block's codes
+    constexpr int XV = 20480 / 8 / THREADS + 1;        // 16-byte x pieces per thread, K <= 20480
+    u32x4 xv[XV];
+#pragma unroll
+    for (int k = 0; k < XV; ++k) {
+        const int v = threadIdx.x + k * THREADS;
+        xv[k] = v * 8 < K ? reinterpret_cast<const u32x4 *>(x)[v] : u32x4{0u, 0u, 0u, 0u};
+    }
+    u32x4 ca[NU];
+    uint32_t sa[NU];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) load_chunk(b0, i, ca, sa);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. the table (every lane's copy) and x into LDS
+    for (int e = threadIdx.x; e < 256 * 64; e += THREADS)
+        reinterpret_cast<uint32_t *>(lut)[e] = slot_codes((uint32_t)(e >> 6));
+#pragma unroll
+    for (int k = 0; k < XV; ++k) {
+        const int v = threadIdx.x + k * THREADS;
+        if (v * 8 < K) reinterpret_cast<u32x4 *>(xn)[v] = xv[k];
+    }
+    __syncthreads();
+
+    // 3. chunk slots: eight threads per chunk; thread q < 6 builds the five
+    // pairs of byte pair q, thread 6 the three pairs of the 13th byte; the
+    // chunk constant is their reduced weighted sum
+    for (int t = threadIdx.x; t < CAP * 8; t += THREADS) {
+        const int h = t >> 3, q = t & 7;
+        const int g = h >> 1, base = 65 * (h & 1);
+        const bool real = h < CPR;
+        const int np = q < 6 ? 5 : (q == 6 ? 3 : 0);
+        float z = 0.0f;
+        uint32_t pr[5];
+#pragma unroll
+        for (int i = 0; i < 5; ++i) {
+            // trits of the pair within the group; >= 128 means none
+            const int tl = base + (q < 6 ? 10 * q + i : 60 + i);
+            const int th = q < 6 ? base + 10 * q + 5 + i : (i < 2 ? base + 63 + i : 128);
+            const bool on = real && i < np;
+            const uint32_t lo = (on && tl < 128) ? xn[g * 128 + tl] : 0u;
+            const uint32_t hi = (on && th < 128) ? xn[g * 128 + th] : 0u;
+            pr[i] = lo | (hi << 16);
+            z = dot2(pr[i], c5_zweight(i), z);
+        }
+#pragma unroll
+        for (int i = 0; i < 5; ++i)
+            if (i < np) xs[h * kC5SlotDw + (q < 6 ? 5 * q : 30) + i] = pr[i];
+        z = seg_sum<8>(z) * -6.103515625e-05f;
+        if (q == 7) xs[h * kC5SlotDw + kC5Pairs] = __builtin_bit_cast(uint32_t, z);
+    }
+    __syncthreads();
+
+    // 4. this lane's chunk pairs into registers (the chunk constants stay in
+    // LDS and are read once per block)
+    uint32_t xr[NU][kC5Pairs];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+        const uint32_t *slot = xs + (j + i * LPR) * kC5SlotDw;
+#pragma unroll
+        for (int v = 0; v < kC5SlotDw / 4; ++v) {
+            const u32x4 u = reinterpret_cast<const u32x4 *>(slot)[v];
+#pragma unroll
+            for (int w = 0; w < 4; ++w)
+                if (4 * v + w < kC5Pairs) xr[i][4 * v + w] = u[w];
+        }
+    }
+
+    uint32_t m8 = 0x03000300u, m6 = 0x00C000C0u;
+    asm volatile("" : "+v"(m8));
+    asm volatile("" : "+v"(m6));
+    const uint32_t lbase = (uint32_t)lane * 4u;
+    auto block = [&](auto refill, u32x4 (&c)[NU], uint32_t (&sv)[NU], int bb, int bn)
+                     __attribute__((always_inline)) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int h = hcol(i);
+            float a = __builtin_bit_cast(float, xs[(j + i * LPR) * kC5SlotDw + kC5Pairs]);
+            c5_chunk(c[i], (uint32_t)h & 3u, xr[i], lut, lbase, a, m8, m6);   // 13 h mod 4
+            acc = __builtin_fmaf(half_f(sv[i] >> (((uint32_t)(h >> 1) & 1u) * 16u)), a, acc);
+            if constexpr (decltype(refill)::value) load_chunk(bn, i, c, sv);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const float out = seg_sum<LPR>(acc) * 16384.0f;
+        const int rr = bb * RS + seg;
+        if (j == 0 && rr < N) y[rr] = out;
+    };
+    // one register set: each chunk is refilled with the wave's next block as
+    // soon as it is consumed, a block's time ahead of its use (two sets of
+    // 16-byte windows do not fit next to 180 activation registers)
+    using Refill = std::integral_constant<bool, true>;
+    using Last = std::integral_constant<bool, false>;
+    int k = 0;
+    for (; k + 1 < nb; ++k) block(Refill{}, ca, sa, b0 + k * WAVES, b0 + (k + 1) * WAVES);
+    if (k < nb) block(Last{}, ca, sa, b0 + k * WAVES, 0);
+}
+
+
 struct Config5 {
     int lpr, nu;
 };
@@ -417,11 +655,66 @@ hipError_t dispatch5(const Config5 &c, const uint8_t *codes, const uint16_t *sca
     return hipErrorInvalidValue;
 }
 
+// Register-activation kernel shapes: the least LPR * NU >= chunks per row
+// (NU <= 5), ties to fewer chunks per lane; {0, 0} when none fits (K > 20480).
+Config5 pick5x(int cpr) {
+    Config5 best{0, 0};
+    for (int lpr : {8, 16, 32, 64})
+        for (int nu = 1; nu <= kC5MaxNU; ++nu) {
+            const int cap = lpr * nu;
+            if (cap < cpr) continue;
+            if (!best.lpr || cap < best.lpr * best.nu || (cap == best.lpr * best.nu && nu < best.nu))
+                best = Config5{lpr, nu};
+        }
+    return best;
+}
+
+template <int LPR, int NU>
+hipError_t launch5x(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
+                    int N, int K, hipStream_t stream) {
+    constexpr int RS = 64 / LPR;
+    const int nblocks = (N + RS - 1) / RS;
+    const int grid = max(1, min(device_cus5(), (nblocks + kWaves5 - 1) / kWaves5));
+    const size_t lds = lds5x_bytes<LPR, NU>(K);
+    if (2 * (K / 128) == LPR * NU)
+        hipLaunchKernelGGL((gemv5x_kernel<LPR, NU, kWaves5, false>), dim3(grid), dim3(64 * kWaves5),
+                           lds, stream, codes, scales, x, y, N, K);
+    else
+        hipLaunchKernelGGL((gemv5x_kernel<LPR, NU, kWaves5, true>), dim3(grid), dim3(64 * kWaves5),
+                           lds, stream, codes, scales, x, y, N, K);
+    return hipGetLastError();
+}
+
+hipError_t dispatch5x(const Config5 &c, const uint8_t *codes, const uint16_t *scales,
+                      const uint16_t *x, float *y, int N, int K, hipStream_t s) {
+#define TQ5X_CASE(L)                                                             \
+    if (c.lpr == L) switch (c.nu) {                                              \
+        case 1: return launch5x<L, 1>(codes, scales, x, y, N, K, s);             \
+        case 2: return launch5x<L, 2>(codes, scales, x, y, N, K, s);             \
+        case 3: return launch5x<L, 3>(codes, scales, x, y, N, K, s);             \
+        case 4: return launch5x<L, 4>(codes, scales, x, y, N, K, s);             \
+        case 5: return launch5x<L, 5>(codes, scales, x, y, N, K, s);             \
+    }
+    TQ5X_CASE(8) TQ5X_CASE(16) TQ5X_CASE(32) TQ5X_CASE(64)
+#undef TQ5X_CASE
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 int32_t gemv5_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
                       int64_t N, int64_t K, hipStream_t stream) {
-    const int units = (int)((K / 128 + 1) / 2);
+    const int G = (int)(K / 128);
+    // register-activation kernel: half-group chunks, scales read as aligned dwords
+    if (G % 2 == 0 && (reinterpret_cast<uintptr_t>(scales) & 3) == 0) {
+        const Config5 c = pick5x(2 * G);
+        if (c.lpr) {
+            const hipError_t e = dispatch5x(c, codes, scales, x, y, (int)N, (int)K, stream);
+            if (e != hipSuccess) return fail(TQ_ERR_HIP, "GEMV launch failed: %s", hipGetErrorString(e));
+            return TQ_OK;
+        }
+    }
+    const int units = (G + 1) / 2;
     const Config5 c = pick5(units);
     if (!c.lpr || K > kMaxK5)
         return fail(TQ_ERR_SHAPE, "K=%lld is above the five-trit GEMV limit %lld", (long long)K,

@@ -79,7 +79,8 @@ def test_gemv5_full_size_sampled(N, K):
 
 
 def test_gemv5_special_values():
-    """Zero rows give exactly 0 (no offsets to cancel); negative, zero and
+    """Rows of zero trits stay within the bar (A = 0 there, so |y| <= 1e-5:
+    the decode's slot offsets cancel up to fp32 rounding); negative, zero and
     subnormal scales and subnormal activations follow the oracle."""
     N, K = 64, 1024
     g = synth.rng(16000)
@@ -95,7 +96,7 @@ def test_gemv5_special_values():
     codes = oracle.pack(t, T5)
     y = gpu(codes, s, x)
     yref, A = oracle.gemv(codes, s, x, N, K, T5)
-    assert np.all(y[:8] == 0)
+    assert np.all(np.abs(y[:8]) <= 1e-5)
     assert_tol(y, yref, A, "special")
 
 
