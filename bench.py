@@ -44,7 +44,8 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=300)
-    p.add_argument("--warmup", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=1000,
+                   help="untimed steps first; the clocks take about 20 ms of load to settle")
     p.add_argument("--rotate-gib", type=float, default=1.0)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target duration of the oracle's CPU-baseline sample")
