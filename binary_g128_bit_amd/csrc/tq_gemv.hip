@@ -48,6 +48,7 @@ namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr size_t kMaxLds = 163840;  // bytes of LDS one gfx950 workgroup may use
 
@@ -175,10 +176,10 @@ __device__ __forceinline__ float seg_sum(float v) {
 // so chunk c of a row sits at c * CHUNK_DW and the compute loop addresses
 // every chunk with an immediate offset.  Slots past the last real chunk (a
 // ragged row shape) hold zeros, which makes their contribution exactly 0.
-template <int VARIANT>
+template <int VARIANT, int UPC = 4>
 struct XUnit {
     static constexpr int UNIT = VARIANT == TQ_BINARY ? 32 : 16;
-    static constexpr int PAIRS = 4 * UNIT / 2;        // pair dwords per chunk
+    static constexpr int PAIRS = UPC * UNIT / 2;      // pair dwords per chunk of UPC units
     static constexpr int CHUNK_DW = PAIRS + 4;        // 36 or 68: 16-byte aligned, bank-spread
     static constexpr int V4 = UNIT / 8;               // 16-byte loads per unit
     u32x4 v[V4];
@@ -217,8 +218,8 @@ struct XUnit {
     }
 
     // Writes unit u (zeros when !real) into its chunk slot; the lane holding a
-    // chunk's first unit writes the chunk constant.  The four units of a chunk
-    // are four aligned consecutive lanes, so the constant reduces with seg_sum.
+    // chunk's first unit writes the chunk constant.  The UPC units of a chunk
+    // are UPC aligned consecutive lanes, so the constant reduces with seg_sum.
     __device__ __forceinline__ void store(uint32_t *xs, int u, bool real) const {
         uint32_t xp[UNIT / 2];
         // low halves x[0..UNIT/2), high halves x[UNIT/2..UNIT)
@@ -233,20 +234,20 @@ struct XUnit {
         float z = 0.0f;
 #pragma unroll
         for (int i = 0; i < UNIT / 2; ++i) z = dot2(xp[i], zweight(i), z);
-        uint32_t *slot = xs + (u >> 2) * CHUNK_DW;
-        uint32_t *dst = slot + (u & 3) * (UNIT / 2);
+        uint32_t *slot = xs + (u / UPC) * CHUNK_DW;
+        uint32_t *dst = slot + (u % UPC) * (UNIT / 2);
 #pragma unroll
         for (int i = 0; i < UNIT / 8; ++i)
             reinterpret_cast<u32x4 *>(dst)[i] = u32x4{xp[4 * i], xp[4 * i + 1], xp[4 * i + 2], xp[4 * i + 3]};
-        z = seg_sum<4>(z) * -kSeedScale;
-        if ((u & 3) == 0) slot[PAIRS] = __builtin_bit_cast(uint32_t, z);
+        z = seg_sum<UPC>(z) * -kSeedScale;
+        if (u % UPC == 0) slot[PAIRS] = __builtin_bit_cast(uint32_t, z);
         if constexpr (VARIANT == TQ_AFFINE2) {
             // the chunk's plain sum of x, in the accumulator unit, for the bias
             float zs = 0.0f;
 #pragma unroll
             for (int i = 0; i < UNIT / 2; ++i) zs = dot2(xp[i], 0x3C003C00u, zs);
-            zs = seg_sum<4>(zs) * kSeedScale;
-            if ((u & 3) == 0) slot[PAIRS + 1] = __builtin_bit_cast(uint32_t, zs);
+            zs = seg_sum<UPC>(zs) * kSeedScale;
+            if (u % UPC == 0) slot[PAIRS + 1] = __builtin_bit_cast(uint32_t, zs);
         }
     }
 };
@@ -300,10 +301,16 @@ __device__ __forceinline__ void chunk_dot(const u32x4 (&c)[RPL], const uint32_t 
 }
 
 // Registers a lane keeps per chunk column: 32 pair dwords and the seed, plus
-// the chunk's sum of x for affine levels.
+// the chunk's sum of x for affine levels.  A register-kernel chunk is 64
+// weights for every variant: 16 code bytes of 2-bit slots (four 16-weight
+// units) or 8 bytes of binary bits (two 32-weight units).
 template <int VARIANT>
 struct XReg {
     static constexpr int N = VARIANT == TQ_AFFINE2 ? 34 : 33;
+    static constexpr int UPC = VARIANT == TQ_BINARY ? 2 : 4;        // units per chunk
+    static constexpr int CB = VARIANT == TQ_BINARY ? 8 : 16;        // code bytes per chunk
+    using Unit = XUnit<VARIANT, UPC>;
+    using Code = typename std::conditional<VARIANT == TQ_BINARY, u32x2, u32x4>::type;
 };
 
 __device__ __forceinline__ float half_bits(uint32_t bits) {
@@ -311,15 +318,19 @@ __device__ __forceinline__ float half_bits(uint32_t bits) {
 }
 
 // chunk_dot with the chunk's pairs and constants held in registers (one
-// row): xr[0..32) are the pairs of the chunk's four units, xr[32] the seed.
+// row): xr[0..32) are the pairs of the chunk's units, xr[32] the seed.
 // Affine levels add the group's bias times xr[33], the chunk's sum of x in
 // the accumulator unit (w = s q + b: s * sum q x + b * sum x).
 template <int VARIANT>
-__device__ __forceinline__ void chunk_dot_reg(const u32x4 &c, const uint32_t (&xr)[XReg<VARIANT>::N],
+__device__ __forceinline__ void chunk_dot_reg(const typename XReg<VARIANT>::Code &c,
+                                              const uint32_t (&xr)[XReg<VARIANT>::N],
                                               uint32_t sbits, uint32_t bbits, float &acc,
                                               const Masks &km) {
     float a = __builtin_bit_cast(float, xr[32]);
-    if constexpr (VARIANT == TQ_AFFINE2) {
+    if constexpr (VARIANT == TQ_BINARY) {
+        bin_acc64(c[0], c[1], xr, xr + 16, a, km);
+        acc = __builtin_fmaf(half_bits(sbits), a, acc);
+    } else if constexpr (VARIANT == TQ_AFFINE2) {
         aff_acc32(c[0], c[1], xr, xr + 8, a, km);
         aff_acc32(c[2], c[3], xr + 16, xr + 24, a, km);
         acc = __builtin_fmaf(half_bits(sbits), a, acc);
@@ -478,7 +489,8 @@ __device__ __forceinline__ void load_bias(const uint16_t *__restrict__ biases, i
 // (permuted, with the chunk constants), each lane copies its NU chunk slots
 // into VGPRs and the block loop reads no LDS at all.
 //
-// Two block loops.  PIPE (ternary, scales readable as aligned dwords): each
+// Two block loops.  PIPE (ternary or binary, scales readable as aligned
+// dwords; binary chunks are 8 code bytes, two 32-weight units): each
 // chunk's registers are refilled with the block two ahead as soon as the
 // chunk is consumed, every load unconditional (clamped to the range's last
 // block, a cache hit), so the load order is the same on every path and the
@@ -494,16 +506,19 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
                                                                const uint16_t *__restrict__ x,
                                                                float *__restrict__ y, int N, int K) {
     extern __shared__ uint32_t xs[];
-    using XU = XUnit<VARIANT>;
+    using XU = typename XReg<VARIANT>::Unit;
+    using Code = typename XReg<VARIANT>::Code;
     constexpr bool AFF = VARIANT == TQ_AFFINE2;
-    static_assert(!(PIPE && AFF), "the pipelined loop is for ternary codes");
+    static_assert(!(PIPE && AFF), "the pipelined loop is for ternary and binary codes");
+    static_assert(PIPE || VARIANT != TQ_BINARY, "binary codes take the pipelined loop only");
     constexpr int XN = XReg<VARIANT>::N;
+    constexpr int UPC = XReg<VARIANT>::UPC, CB = XReg<VARIANT>::CB;
     constexpr int THREADS = 64 * WAVES;
     constexpr int RS = 64 / LPR;  // rows per block (one per lane segment)
     constexpr int CAP = LPR * NU;
-    constexpr int XMAX = (CAP * 4 + THREADS - 1) / THREADS;
-    const int G = K >> 7, CPR = 2 * G;
-    const int nunits = CPR * 4;
+    constexpr int XMAX = (CAP * UPC + THREADS - 1) / THREADS;
+    const int G = K >> 7, CPR = 2 * G;  // 64-weight chunks per row
+    const int nunits = CPR * UPC;
     const int lane = threadIdx.x & 63;
     // wave-uniform (scalar) block bookkeeping: the loops branch on SGPRs
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -516,14 +531,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
     XU xu[XMAX];
 #pragma unroll
     for (int k = 0; k < XMAX; ++k)
-        xu[k].load(x, min(min((int)threadIdx.x + k * THREADS, CAP * 4 - 1), nunits - 1));
+        xu[k].load(x, min(min((int)threadIdx.x + k * THREADS, CAP * UPC - 1), nunits - 1));
     __builtin_amdgcn_sched_barrier(0);
 
     // x staged into LDS, then this lane's chunk slots into registers
     auto stage_x = [&](uint32_t (&xr)[NU][XN]) __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < XMAX; ++k) {
-            const int u = min((int)threadIdx.x + k * THREADS, CAP * 4 - 1);
+            const int u = min((int)threadIdx.x + k * THREADS, CAP * UPC - 1);
             xu[k].store(xs, u, u < nunits);
         }
         __syncthreads();
@@ -558,14 +573,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
             hsh[i] = ((uint32_t)(col[i] >> 1) & 1u) * 16u;
         }
         const uint32_t *sc32 = reinterpret_cast<const uint32_t *>(scales);
-        auto load_chunk = [&](int bb, int i, u32x4 (&c)[NU], uint32_t (&sv)[NU])
+        auto load_chunk = [&](int bb, int i, Code (&c)[NU], uint32_t (&sv)[NU])
                               __attribute__((always_inline)) {
             const int r = min(min(bb, blast) * RS + seg, N - 1);
             sv[i] = sc32[((size_t)r * G + (col[i] >> 1)) >> 1];
             c[i] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4 *>(codes + (size_t)r * CPR * 16) + col[i]);
+                reinterpret_cast<const Code *>(codes + (size_t)r * CPR * CB) + col[i]);
         };
-        u32x4 ca[NU], cb[NU];
+        Code ca[NU], cb[NU];
         uint32_t sa[NU], sb[NU];
 #pragma unroll
         for (int i = 0; i < NU; ++i) load_chunk(b0, i, ca, sa);
@@ -574,7 +589,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
 #pragma unroll
         for (int i = 0; i < NU; ++i) load_chunk(b0 + WAVES, i, cb, sb);
 
-        auto block = [&](auto refill, u32x4 (&c)[NU], uint32_t (&sv)[NU], int bb, int bn)
+        auto block = [&](auto refill, Code (&c)[NU], uint32_t (&sv)[NU], int bb, int bn)
                          __attribute__((always_inline)) {
             float acc = 0.0f;
 #pragma unroll
@@ -595,7 +610,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
             block(Refill{}, cb, sb, b0 + (k + 1) * WAVES, b0 + (k + 3) * WAVES);
         }
         if (k < nb) block(Last{}, ca, sa, b0 + k * WAVES, 0);
-    } else {
+    } else if constexpr (VARIANT != TQ_BINARY) {
         u32x4 ca[NU][1], cb[NU][1];
         uint32_t sa[NU][1], sb[NU][1];
         uint32_t ba[NU][1] = {}, bb_[NU][1] = {};
@@ -749,16 +764,21 @@ Config pick_xreg(int cpr) {
 }
 
 template <int VARIANT, int LPR, int NU>
+constexpr size_t lds_bytes_xreg() {
+    return (size_t)LPR * NU * XReg<VARIANT>::Unit::CHUNK_DW * sizeof(uint32_t);
+}
+
+template <int VARIANT, int LPR, int NU>
 hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
                        const uint16_t *x, float *y, int N, int K, hipStream_t stream) {
     constexpr int RS = 64 / LPR;
     const int nblocks = (N + RS - 1) / RS;
     const int grid = max(1, min(device_cus(), (nblocks + kXregWaves - 1) / kXregWaves));
-    constexpr size_t lds = lds_bytes<VARIANT, LPR, NU>();
+    constexpr size_t lds = lds_bytes_xreg<VARIANT, LPR, NU>();
     const bool exact = (K / 128) * 2 == LPR * NU;
     // the pipelined loop reads each scale from its aligned dword: an even
     // group count keeps every row's scales dword aligned
-    const bool pipe = VARIANT == TQ_TERNARY && (K / 128) % 2 == 0 &&
+    const bool pipe = VARIANT != TQ_AFFINE2 && (K / 128) % 2 == 0 &&
                       (reinterpret_cast<uintptr_t>(scales) & 3) == 0;
 #define TQ_XL(R, P)                                                                               \
     hipLaunchKernelGGL((gemv_xreg_kernel<VARIANT, LPR, NU, kXregWaves, R, P>), dim3(grid),         \
@@ -767,6 +787,10 @@ hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint1
         if (pipe && exact) TQ_XL(false, true);
         else if (pipe) TQ_XL(true, true);
         else TQ_XL(true, false);
+    } else if constexpr (VARIANT == TQ_BINARY) {
+        if (!pipe) return hipErrorInvalidValue;  // the caller checks: never taken
+        if (exact) TQ_XL(false, true);
+        else TQ_XL(true, true);
     } else {
         if (exact) TQ_XL(false, false);
         else TQ_XL(true, false);
@@ -797,15 +821,18 @@ hipError_t dispatch_xreg(const Config &c, const uint8_t *codes, const uint16_t *
 int32_t gemv_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
                      int64_t N, int64_t K, int32_t variant, hipStream_t stream) {
     const int cpr = (int)(K / 128) * (variant == TQ_TERNARY ? 2 : 1);
-    if (variant == TQ_TERNARY) {
-        const Config xc = pick_xreg(cpr);
-        if (xc.lpr) {
-            const hipError_t e =
-                dispatch_xreg<TQ_TERNARY>(xc, codes, scales, nullptr, x, y, (int)N, (int)K, stream);
-            if (e != hipSuccess)
-                return fail(TQ_ERR_HIP, "GEMV launch failed: %s", hipGetErrorString(e));
-            return TQ_OK;
-        }
+    // register-activation kernel: 64-weight chunks (two per group) for both
+    // variants; binary codes only with dword-aligned scales and an even group
+    // count (its pipelined loop), else the LDS-activation kernel below
+    const Config xc = pick_xreg((int)(K / 128) * 2);
+    const bool bin_ok = (K / 128) % 2 == 0 && (reinterpret_cast<uintptr_t>(scales) & 3) == 0;
+    if (xc.lpr && (variant == TQ_TERNARY || bin_ok)) {
+        const hipError_t e =
+            variant == TQ_TERNARY
+                ? dispatch_xreg<TQ_TERNARY>(xc, codes, scales, nullptr, x, y, (int)N, (int)K, stream)
+                : dispatch_xreg<TQ_BINARY>(xc, codes, scales, nullptr, x, y, (int)N, (int)K, stream);
+        if (e != hipSuccess) return fail(TQ_ERR_HIP, "GEMV launch failed: %s", hipGetErrorString(e));
+        return TQ_OK;
     }
     const Config c = pick(cpr);
     if (!c.lpr)

@@ -41,10 +41,11 @@ def assert_tol(y, yref, A, what=""):
     assert not bad.any(), "%s: %d bad, worst err %.3g" % (what, bad.sum(), err.max())
 
 
-# K spans odd group counts (128, 384, 640, 2176), every capacity class of the
-# shape table, exact and ragged shapes, and the 40960 maximum
+# K spans odd group counts (128, 384, 640, 2176: the table kernel), every
+# capacity class of the register kernel's shape table, exact and ragged shapes,
+# its 20480 maximum (320 chunks, the most LDS) and the table kernel's 40960
 SHAPES = [(1, 128), (7, 256), (33, 384), (100, 640), (1000, 1024), (65, 2176), (257, 5120),
-          (129, 6144), (40, 17408), (3, 29952), (5, 40960), (77, 10240), (300, 3072)]
+          (129, 6144), (40, 17408), (9, 20480), (3, 29952), (5, 40960), (77, 10240), (300, 3072)]
 
 
 @pytest.mark.parametrize("N,K", SHAPES)

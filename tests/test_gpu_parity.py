@@ -50,7 +50,7 @@ def case(seed, N, K, M, variant, exact):
 
 
 SHAPES = [(1, 128), (7, 256), (33, 384), (100, 640), (1000, 1024), (257, 5120),
-          (65, 17408), (3, 29952), (129, 6144), (5, 65536)]
+          (65, 17408), (9, 20480), (3, 29952), (129, 6144), (5, 65536)]
 
 
 @pytest.mark.parametrize("variant", [TERN, BIN])
