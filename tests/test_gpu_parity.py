@@ -238,10 +238,11 @@ def test_lm_head_sampled(M):
 @pytest.mark.parametrize("M,N,K", [(3, 1, 128), (17, 70, 128), (31, 129, 256), (33, 64, 640),
                                    (100, 200, 2176), (5, 1000, 29952), (2, 77, 65536),
                                    (128, 128, 128), (130, 70, 384), (257, 300, 1024),
-                                   (200, 129, 5120)])
+                                   (200, 129, 5120), (7, 33, 640), (6, 129, 17408),
+                                   (8, 65, 5120)])
 def test_gemm_ragged(M, N, K, variant):
     """Ragged activation and weight tiles, K of one group (most waves of a
-    workgroup idle) and the largest K."""
+    workgroup idle), the largest K, and 5..8 rows (eight staged rows)."""
     codes, s, X = case(9700 + M + N + K, N, K, M, variant, exact=True)
     Y = gpu_gemm(codes, s, X, variant, N, K)
     Yref, _ = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
