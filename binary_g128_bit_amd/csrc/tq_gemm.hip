@@ -580,9 +580,11 @@ hipError_t launch(const uint8_t *codes, const uint16_t *scales, const uint16_t *
 
 // Configurations measured on the MLP shapes (17408 x 5120 and 5120 x 17408):
 // M <= 4 takes the stage-pipelined kernel with four staged activation rows,
-// M <= 8 the same kernel with eight (18.0 / 19.5 us at M = 8 against 21.4 /
-// 21.0 for the per-group kernel; sixteen staged rows are slower than the
-// per-group kernel at M = 16); wider batches take the per-group kernel, with
+// M <= 8 the same kernel with eight while N <= 65536 (18.0 / 19.5 us at M = 8
+// against 21.4 / 21.0 for the per-group kernel; on the 248320-row LM head it
+// took 166 us against 116: its waves live for 2.5 stages only, and sixteen
+// staged rows are slower than the per-group kernel at M = 16); wider batches
+// and taller matrices take the per-group kernel, with
 // taller weight tiles and a two-way K split when N leaves enough workgroups
 // (N >= 8192), else shorter tiles and a four-way split.
 template <int VARIANT>
@@ -590,7 +592,7 @@ hipError_t dispatch(const uint8_t *codes, const uint16_t *scales, const uint16_t
                     int M, int N, int K, hipStream_t s) {
     const bool tall = N >= 8192;
     if (M <= 4) return launch_stage<VARIANT, 2, 4, 4, 1>(codes, scales, X, Y, M, N, K, s);
-    if (M <= 8) return launch_stage<VARIANT, 2, 8, 4, 1>(codes, scales, X, Y, M, N, K, s);
+    if (M <= 8 && N <= 65536) return launch_stage<VARIANT, 2, 8, 4, 1>(codes, scales, X, Y, M, N, K, s);
     if (M <= 16)
         return tall ? launch<VARIANT, 4, 1, 2>(codes, scales, X, Y, M, N, K, s)
                     : launch<VARIANT, 2, 1, 4>(codes, scales, X, Y, M, N, K, s);

@@ -239,7 +239,7 @@ def test_lm_head_sampled(M):
                                    (100, 200, 2176), (5, 1000, 29952), (2, 77, 65536),
                                    (128, 128, 128), (130, 70, 384), (257, 300, 1024),
                                    (200, 129, 5120), (7, 33, 640), (6, 129, 17408),
-                                   (8, 65, 5120)])
+                                   (8, 65, 5120), (6, 65600, 256)])
 def test_gemm_ragged(M, N, K, variant):
     """Ragged activation and weight tiles, K of one group (most waves of a
     workgroup idle), the largest K, and 5..8 rows (eight staged rows)."""
