@@ -31,12 +31,15 @@
 // sum x) = 2^-14 sum t*x.
 //
 // Work split.  A wave owns 64/LPR row slots of LPR lanes each; lane j of a
-// slot takes groups j, j+LPR, j+2*LPR, ... of its RPL rows.  Each lane first
-// issues its share of the x loads for staging (L2-resident), then every code
-// and scale load of its rows, so the workgroup's whole HBM share is in flight
-// while x is permuted into LDS; groups are then processed in the order their
-// codes arrive.  Per-row partial sums are reduced across the LPR lanes with
-// DPP moves (quad_perm, row_half_mirror, row_mirror) and swizzles beyond 16.
+// slot takes the chunks j, j+LPR, j+2*LPR, ... of its rows (a chunk is 16
+// code bytes; in the register kernel 64 weights: 16 bytes of 2-bit slots or 8
+// bytes of binary bits).  Workgroups are persistent, one per CU with eight
+// waves, and walk a contiguous range of row blocks round-robin over their
+// waves.  Each lane issues its share of the x loads (L2-resident) and its
+// first block's code and scale loads before x is permuted into LDS; later
+// blocks are loaded while earlier ones are computed.  Per-row partial sums
+// are reduced across the LPR lanes with DPP moves (quad_perm,
+// row_half_mirror, row_mirror) and swizzles beyond 16.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -170,8 +173,9 @@ __device__ __forceinline__ float seg_sum(float v) {
 }
 
 // x staging.  Ternary unit: 16 weights -> 8 pairs (p, p+8); binary unit:
-// 32 weights -> 16 pairs (p, p+16).  Four consecutive units make one 16-byte
-// code chunk (64 ternary or 128 binary weights).  In LDS every chunk has a
+// 32 weights -> 16 pairs (p, p+16).  UPC consecutive units make one chunk:
+// four for a 16-byte code chunk (64 ternary or 128 binary weights), two for
+// the register kernel's 8-byte binary chunk (64 weights).  In LDS every chunk has a
 // slot of CHUNK_DW dwords: its pairs, then its constant (a float), then pad,
 // so chunk c of a row sits at c * CHUNK_DW and the compute loop addresses
 // every chunk with an immediate offset.  Slots past the last real chunk (a
@@ -483,8 +487,8 @@ __device__ __forceinline__ void load_bias(const uint16_t *__restrict__ biases, i
         bv[i][0] = RAGGED ? bp[min(j + i * LPR, CPR - 1) / 2] : bp[j / 2 + i * (LPR / 2)];
 }
 
-// Ternary (and affine 2-bit) GEMV, one row per lane, with the lane's
-// activations in registers.  Lane j of a row segment only ever reads chunk
+// Ternary, binary and affine 2-bit GEMV, one row per lane segment, with the
+// lane's activations in registers.  Lane j of a row segment only ever reads chunk
 // columns j, j + LPR, ..., so after the workgroup has staged x into LDS once
 // (permuted, with the chunk constants), each lane copies its NU chunk slots
 // into VGPRs and the block loop reads no LDS at all.
@@ -493,7 +497,7 @@ __device__ __forceinline__ void load_bias(const uint16_t *__restrict__ biases, i
 // dwords; binary chunks are 8 code bytes, two 32-weight units): each
 // chunk's registers are refilled with the block two ahead as soon as the
 // chunk is consumed, every load unconditional (clamped to the range's last
-// block, a cache hit), so the load order is the same on every path and the
+// block, mostly a cache hit), so the load order is the same on every path and the
 // compiler's wait before each chunk is for that chunk only: about two blocks
 // per wave stay in flight while the wave computes.  The scale comes from the
 // aligned dword that holds it (a genuine 32-bit value: 16-bit registers are

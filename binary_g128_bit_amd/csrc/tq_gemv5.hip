@@ -9,6 +9,12 @@
 // bytes per group (the last one holds three trits), rows padded to 16 bytes.
 // That is 1.75 bits per weight with the scale against 2.125 for 2-bit slots.
 //
+// Two kernels.  The register kernel (gemv5x_kernel, further down: even group
+// count, dword-aligned scales, K <= 20480) looks each byte up as 2-bit slot
+// codes and decodes them like the 2-bit format, with activations in
+// registers.  The table kernel described next (gemv5_kernel) serves the other
+// shapes.
+//
 // Decode.  Base-3 digits do not fall out of shifts and masks, so each code
 // byte is looked up in a table in LDS whose 16-byte entry already holds the
 // byte's five trits as FP16 {-1, 0, +1}, laid out against the activation
