@@ -493,16 +493,19 @@ __device__ __forceinline__ void load_bias(const uint16_t *__restrict__ biases, i
 // (permuted, with the chunk constants), each lane copies its NU chunk slots
 // into VGPRs and the block loop reads no LDS at all.
 //
-// Two block loops.  PIPE (ternary or binary, scales readable as aligned
-// dwords; binary chunks are 8 code bytes, two 32-weight units): each
-// chunk's registers are refilled with the block two ahead as soon as the
-// chunk is consumed, every load unconditional (clamped to the range's last
-// block, mostly a cache hit), so the load order is the same on every path and the
-// compiler's wait before each chunk is for that chunk only: about two blocks
-// per wave stay in flight while the wave computes.  The scale comes from the
-// aligned dword that holds it (a genuine 32-bit value: 16-bit registers are
-// packed in pairs, and the packing waits for both loads).  Otherwise a plain
-// ping-pong of two register sets, each loaded whole one block ahead.
+// Two block loops.  PIPE (scales, and affine biases, readable as aligned
+// dwords; binary chunks are 8 code bytes, two 32-weight units): one register
+// set, each chunk refilled with the wave's next block as soon as it is
+// consumed, a block's compute ahead of its use.  Every load is unconditional
+// (clamped to the range's last block, mostly a cache hit), so the load order
+// is the same on every path and the compiler's wait before each chunk is for
+// that chunk only.  Only the first block is requested before the loop: a
+// second one there (two register sets) doubled the burst every wave waits
+// behind at the start and measured 10 % slower on the MLP shapes.  Scales
+// and biases come from the aligned dword that holds them (a genuine 32-bit
+// value: 16-bit registers are packed in pairs, and the packing waits for both
+// loads).  Otherwise a plain ping-pong of two register sets, each loaded whole
+// one block ahead.
 template <int VARIANT, int LPR, int NU, int WAVES, bool RAGGED, bool PIPE>
 __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__restrict__ codes,
                                                                const uint16_t *__restrict__ scales,
@@ -513,7 +516,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
     using XU = typename XReg<VARIANT>::Unit;
     using Code = typename XReg<VARIANT>::Code;
     constexpr bool AFF = VARIANT == TQ_AFFINE2;
-    static_assert(!(PIPE && AFF), "the pipelined loop is for ternary and binary codes");
     static_assert(PIPE || VARIANT != TQ_BINARY, "binary codes take the pipelined loop only");
     constexpr int XN = XReg<VARIANT>::N;
     constexpr int UPC = XReg<VARIANT>::UPC, CB = XReg<VARIANT>::CB;
@@ -577,29 +579,30 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
             hsh[i] = ((uint32_t)(col[i] >> 1) & 1u) * 16u;
         }
         const uint32_t *sc32 = reinterpret_cast<const uint32_t *>(scales);
-        auto load_chunk = [&](int bb, int i, Code (&c)[NU], uint32_t (&sv)[NU])
+        const uint32_t *bi32 = reinterpret_cast<const uint32_t *>(biases);
+        auto load_chunk = [&](int bb, int i, Code (&c)[NU], uint32_t (&sv)[NU], uint32_t (&bv)[NU])
                               __attribute__((always_inline)) {
             const int r = min(min(bb, blast) * RS + seg, N - 1);
-            sv[i] = sc32[((size_t)r * G + (col[i] >> 1)) >> 1];
+            const size_t h = ((size_t)r * G + (col[i] >> 1)) >> 1;
+            sv[i] = sc32[h];
+            if constexpr (AFF) bv[i] = bi32[h];
             c[i] = __builtin_nontemporal_load(
                 reinterpret_cast<const Code *>(codes + (size_t)r * CPR * CB) + col[i]);
         };
-        Code ca[NU], cb[NU];
-        uint32_t sa[NU], sb[NU];
+        Code ca[NU];
+        uint32_t sa[NU], ba[NU];
 #pragma unroll
-        for (int i = 0; i < NU; ++i) load_chunk(b0, i, ca, sa);
+        for (int i = 0; i < NU; ++i) load_chunk(b0, i, ca, sa, ba);
         __builtin_amdgcn_sched_barrier(0);
         stage_x(xr);
-#pragma unroll
-        for (int i = 0; i < NU; ++i) load_chunk(b0 + WAVES, i, cb, sb);
 
-        auto block = [&](auto refill, Code (&c)[NU], uint32_t (&sv)[NU], int bb, int bn)
-                         __attribute__((always_inline)) {
+        auto block = [&](auto refill, Code (&c)[NU], uint32_t (&sv)[NU], uint32_t (&bv)[NU], int bb,
+                         int bn) __attribute__((always_inline)) {
             float acc = 0.0f;
 #pragma unroll
             for (int i = 0; i < NU; ++i) {
-                chunk_dot_reg<VARIANT>(c[i], xr[i], sv[i] >> hsh[i], 0u, acc, km);
-                if constexpr (decltype(refill)::value) load_chunk(bn, i, c, sv);
+                chunk_dot_reg<VARIANT>(c[i], xr[i], sv[i] >> hsh[i], AFF ? bv[i] >> hsh[i] : 0u, acc, km);
+                if constexpr (decltype(refill)::value) load_chunk(bn, i, c, sv, bv);
                 __builtin_amdgcn_sched_barrier(0);
             }
             const float out = seg_sum<LPR>(acc) * XU::kRowScale;
@@ -609,11 +612,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         using Refill = std::integral_constant<bool, true>;
         using Last = std::integral_constant<bool, false>;
         int k = 0;
-        for (; k + 1 < nb; k += 2) {
-            block(Refill{}, ca, sa, b0 + k * WAVES, b0 + (k + 2) * WAVES);
-            block(Refill{}, cb, sb, b0 + (k + 1) * WAVES, b0 + (k + 3) * WAVES);
-        }
-        if (k < nb) block(Last{}, ca, sa, b0 + k * WAVES, 0);
+        for (; k + 1 < nb; ++k) block(Refill{}, ca, sa, ba, b0 + k * WAVES, b0 + (k + 1) * WAVES);
+        if (k < nb) block(Last{}, ca, sa, ba, b0 + k * WAVES, 0);
     } else if constexpr (VARIANT != TQ_BINARY) {
         u32x4 ca[NU][1], cb[NU][1];
         uint32_t sa[NU][1], sb[NU][1];
@@ -782,8 +782,8 @@ hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint1
     const bool exact = (K / 128) * 2 == LPR * NU;
     // the pipelined loop reads each scale from its aligned dword: an even
     // group count keeps every row's scales dword aligned
-    const bool pipe = VARIANT != TQ_AFFINE2 && (K / 128) % 2 == 0 &&
-                      (reinterpret_cast<uintptr_t>(scales) & 3) == 0;
+    const bool pipe = (K / 128) % 2 == 0 && (reinterpret_cast<uintptr_t>(scales) & 3) == 0 &&
+                      (VARIANT != TQ_AFFINE2 || (reinterpret_cast<uintptr_t>(biases) & 3) == 0);
 #define TQ_XL(R, P)                                                                               \
     hipLaunchKernelGGL((gemv_xreg_kernel<VARIANT, LPR, NU, kXregWaves, R, P>), dim3(grid),         \
                        dim3(64 * kXregWaves), lds, stream, codes, scales, biases, x, y, N, K)
@@ -796,7 +796,8 @@ hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint1
         if (exact) TQ_XL(false, true);
         else TQ_XL(true, true);
     } else {
-        if (exact) TQ_XL(false, false);
+        if (pipe && exact) TQ_XL(false, true);
+        else if (pipe) TQ_XL(true, true);
         else TQ_XL(true, false);
     }
 #undef TQ_XL
