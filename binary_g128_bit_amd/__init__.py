@@ -144,10 +144,17 @@ def _dev(tensor, name, dtypes):
     return tensor.data_ptr()
 
 
-def _stream(stream):
+def _stream(stream, tensor):
+    """The HIP stream to launch on: `stream`, else the current stream of the
+    device that holds `tensor` (read as a raw handle: building a torch Stream
+    object per call costs about 2.5 us of host time)."""
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+    if stream is not None:
+        return ctypes.c_void_p(stream.cuda_stream)
+    try:
+        return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(tensor.get_device()))
+    except AttributeError:  # a torch build without the raw accessor
+        return ctypes.c_void_p(torch.cuda.current_stream(tensor.device).cuda_stream)
 
 
 def _shape_checks(codes, scales, K, variant):
@@ -172,7 +179,7 @@ def tq_gemv(codes, scales, x, y=None, variant=TQ_TERNARY, group=GROUP, stream=No
     half = (torch.float16, torch.int16)
     _check(lib().tq_gemv(_dev(codes, "codes", (torch.uint8,)), _dev(scales, "scales", half),
                          _dev(x, "x", half), _dev(y, "y", (torch.float32,)), N, K, group, variant,
-                         _stream(stream)))
+                         _stream(stream, x)))
     return y
 
 
@@ -186,7 +193,7 @@ def tq_gemm(codes, scales, X, Y=None, variant=TQ_TERNARY, group=GROUP, stream=No
     half = (torch.float16, torch.int16)
     _check(lib().tq_gemm(_dev(codes, "codes", (torch.uint8,)), _dev(scales, "scales", half),
                          _dev(X, "X", half), _dev(Y, "Y", (torch.float32,)), M, N, K, group,
-                         variant, _stream(stream)))
+                         variant, _stream(stream, X)))
     return Y
 
 
@@ -205,7 +212,7 @@ def tq_embed(codes, scales, ids, out=None, variant=TQ_TERNARY, group=GROUP, stre
     half = (torch.float16, torch.int16)
     _check(lib().tq_embed(_dev(codes, "codes", (torch.uint8,)), _dev(scales, "scales", half),
                           _dev(ids, "ids", (torch.int32,)), _dev(out, "out", half), n_ids, N, K,
-                          group, variant, _stream(stream)))
+                          group, variant, _stream(stream, codes)))
     return out
 
 
@@ -222,7 +229,7 @@ def tq_gemv_affine(codes, scales, biases, x, y=None, group=GROUP, stream=None):
     half = (torch.float16, torch.int16)
     _check(lib().tq_gemv_affine(_dev(codes, "codes", (torch.uint8,)), _dev(scales, "scales", half),
                                 _dev(biases, "biases", half), _dev(x, "x", half),
-                                _dev(y, "y", (torch.float32,)), N, K, group, _stream(stream)))
+                                _dev(y, "y", (torch.float32,)), N, K, group, _stream(stream, x)))
     return y
 
 
@@ -250,7 +257,7 @@ def tq_kv_append(k, v, pos, n_kv, t_cap, kc, ks, vc, vs, stream=None):
                 name, arr.numel() * arr.element_size(), tq_kv_bytes(n_kv, t_cap, part)))
     _check(lib().tq_kv_append(_dev(k, "k", half), _dev(v, "v", half), k.shape[0], pos, n_kv, t_cap,
                               _dev(kc, "kc", (torch.uint8,)), _dev(ks, "ks", half),
-                              _dev(vc, "vc", (torch.uint8,)), _dev(vs, "vs", half), _stream(stream)))
+                              _dev(vc, "vc", (torch.uint8,)), _dev(vs, "vs", half), _stream(stream, k)))
 
 
 def tq_attn_decode(q, kc, ks, vc, vs, T, n_kv, t_cap, workspace, out=None, stream=None):
@@ -266,6 +273,6 @@ def tq_attn_decode(q, kc, ks, vc, vs, T, n_kv, t_cap, workspace, out=None, strea
                                 _dev(vc, "vc", (torch.uint8,)), _dev(vs, "vs", half), T, n_q, n_kv,
                                 t_cap, _dev(out, "out", (torch.float32,)),
                                 _dev(workspace, "workspace", (torch.float32, torch.uint8)),
-                                workspace.numel() * workspace.element_size(), _stream(stream)))
+                                workspace.numel() * workspace.element_size(), _stream(stream, q)))
     return out
 
