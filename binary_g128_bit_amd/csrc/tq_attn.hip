@@ -339,6 +339,41 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restri
     out[(size_t)hq * kHD + tid] = o / l;
 }
 
+// Merge for up to kSmallChunks chunks in one pass.  Lane c of every wave
+// loads chunk c's maximum and sum while thread = dimension loads the chunk
+// outputs, all at once; the maximum and the denominator are wave reductions
+// and chunk c's weight reaches every lane by readlane, so the merge costs one
+// memory round trip instead of the three dependent phases of
+// attn_combine_kernel.  Offsets stay below 2^31 (n_q <= 1024, chunks <= 32).
+constexpr int kSmallChunks = 32;
+
+__global__ __launch_bounds__(256) void attn_combine_small_kernel(const float *__restrict__ ws,
+                                                                 int nchunks, int nqh,
+                                                                 float *__restrict__ out) {
+    const int hq = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    const int stride = nqh * (kHD + 2);
+    const float *base = ws + hq * (kHD + 2);
+    const int mine = min(lane, nchunks - 1);
+    const float m = base[mine * stride + kHD];
+    const float l = base[mine * stride + kHD + 1];
+    float o[kSmallChunks];
+#pragma unroll
+    for (int ck = 0; ck < kSmallChunks; ++ck) o[ck] = base[min(ck, nchunks - 1) * stride + tid];
+    float mx = m;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
+    const float e = lane < nchunks ? exp2f(m - mx) : 0.0f;
+    float den = e * l;
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) den += __shfl_xor(den, s);
+    float num = 0.0f;
+#pragma unroll
+    for (int ck = 0; ck < kSmallChunks; ++ck)
+        num = __builtin_fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), ck)),
+                             o[ck], num);
+    out[hq * kHD + tid] = num / den;
+}
+
 }  // namespace
 
 // Tokens per attention chunk: a multiple of 32 * kWaves giving about two
@@ -375,8 +410,12 @@ int32_t attn_decode_enqueue(const uint16_t *q, const uint8_t *kc, const uint16_t
                        (int)chunk, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)n_q), dim3(256), 0, stream, ws,
-                       (int)nchunks, (int)n_q, out);
+    if (nchunks <= kSmallChunks)
+        hipLaunchKernelGGL(attn_combine_small_kernel, dim3((unsigned)n_q), dim3(256), 0, stream, ws,
+                           (int)nchunks, (int)n_q, out);
+    else
+        hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)n_q), dim3(256), 0, stream, ws,
+                           (int)nchunks, (int)n_q, out);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
     return TQ_OK;

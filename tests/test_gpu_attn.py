@@ -153,7 +153,7 @@ def assert_attn(out, ref, A, what):
     assert not bad.any(), "%s: %d bad, worst err %.3g (A %.3g)" % (what, bad.sum(), err.max(), A.max())
 
 
-@pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 127, 128, 129, 513, 1000, 4099])
+@pytest.mark.parametrize("T", [1, 2, 31, 32, 33, 127, 128, 129, 513, 1000, 4096, 4099])
 def test_attn_decode_gqa6(T):
     n_kv, n_q = 4, 24
     q, c, (kn, ks, vn, vs) = attention_case(20000 + T, T, n_kv, n_q)
