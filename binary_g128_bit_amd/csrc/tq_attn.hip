@@ -297,81 +297,73 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
 }
 
 constexpr int kMaxChunks = 1024;
+constexpr int kMergeRound = 32;  // chunk outputs a lane has in flight at once
 
-// Merge the chunks: one workgroup per query head.  The chunks' weights
-// 2^(m_c - M) come first, in parallel, into LDS; then thread = dimension
-// sums the chunk outputs with eight loads in flight.
+// Merge the chunks.  Workgroup (query head, quarter of the dimensions); wave
+// w takes a contiguous quarter of the chunks, lane = dimension.  Per round of
+// up to 32 chunks a lane issues all 32 output loads at once while lane c also
+// loads chunk c's (max, sum); the round's maximum and denominator are wave
+// reductions and chunk c's weight reaches every lane by readlane.  Rounds
+// fold into a running (max, numerator, denominator) by rescaling, and the four
+// waves meet in LDS.  Up to 128 chunks cost one memory round trip.  Offsets
+// stay below 2^31 (n_q <= 1024, chunks <= 1024).
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restrict__ ws, int nchunks,
                                                            int nqh, float *__restrict__ out) {
-    __shared__ float wgt[kMaxChunks];
-    __shared__ float part[2][4];
-    const int hq = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const size_t stride = (size_t)nqh * (kHD + 2);
-    const float *base = ws + (size_t)hq * (kHD + 2);
-    float mx = -INFINITY;
-    for (int ck = tid; ck < nchunks; ck += 256) mx = fmaxf(mx, base[ck * stride + kHD]);
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-    if (lane == 0) part[0][wave] = mx;
-    __syncthreads();
-    mx = fmaxf(fmaxf(part[0][0], part[0][1]), fmaxf(part[0][2], part[0][3]));
-    float l = 0.0f;
-    for (int ck = tid; ck < nchunks; ck += 256) {
-        const float e = exp2f(base[ck * stride + kHD] - mx);
-        wgt[ck] = e;
-        l += e * base[ck * stride + kHD + 1];
-    }
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) l += __shfl_xor(l, m);
-    if (lane == 0) part[1][wave] = l;
-    __syncthreads();
-    l = part[1][0] + part[1][1] + part[1][2] + part[1][3];
-    float o = 0.0f;
-    int ck = 0;
-    for (; ck + 8 <= nchunks; ck += 8) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = base[(ck + u) * stride + tid];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) o = __builtin_fmaf(wgt[ck + u], v[u], o);
-    }
-    for (; ck < nchunks; ++ck) o = __builtin_fmaf(wgt[ck], base[ck * stride + tid], o);
-    out[(size_t)hq * kHD + tid] = o / l;
-}
-
-// Merge for up to kSmallChunks chunks in one pass.  Lane c of every wave
-// loads chunk c's maximum and sum while thread = dimension loads the chunk
-// outputs, all at once; the maximum and the denominator are wave reductions
-// and chunk c's weight reaches every lane by readlane, so the merge costs one
-// memory round trip instead of the three dependent phases of
-// attn_combine_kernel.  Offsets stay below 2^31 (n_q <= 1024, chunks <= 32).
-constexpr int kSmallChunks = 32;
-
-__global__ __launch_bounds__(256) void attn_combine_small_kernel(const float *__restrict__ ws,
-                                                                 int nchunks, int nqh,
-                                                                 float *__restrict__ out) {
-    const int hq = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
+    __shared__ float part_m[kWaves], part_d[kWaves], part_n[kWaves][64];
+    const int hq = blockIdx.x, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int dim = 64 * blockIdx.y + lane;
     const int stride = nqh * (kHD + 2);
     const float *base = ws + hq * (kHD + 2);
-    const int mine = min(lane, nchunks - 1);
-    const float m = base[mine * stride + kHD];
-    const float l = base[mine * stride + kHD + 1];
-    float o[kSmallChunks];
+    const int per = (nchunks + kWaves - 1) / kWaves;
+    const int c0 = wave * per, c1 = min(nchunks, c0 + per);
+    float M = -INFINITY, num = 0.0f, den = 0.0f;
+    for (int r = c0; r < c1; r += kMergeRound) {
+        const int last = min(kMergeRound, c1 - r) - 1;
+        const int mine = r + min(lane, last);
+        const float m = base[mine * stride + kHD];
+        const float l = base[mine * stride + kHD + 1];
+        float o[kMergeRound];
 #pragma unroll
-    for (int ck = 0; ck < kSmallChunks; ++ck) o[ck] = base[min(ck, nchunks - 1) * stride + tid];
-    float mx = m;
+        for (int i = 0; i < kMergeRound; ++i) o[i] = base[(r + min(i, last)) * stride + dim];
+        float mx = m;
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
-    const float e = lane < nchunks ? exp2f(m - mx) : 0.0f;
-    float den = e * l;
+        for (int s = 32; s >= 1; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
+        const float mn = fmaxf(M, mx);
+        const float alpha = exp2f(M - mn);  // 0 on the first round
+        const float e = lane <= last ? exp2f(m - mn) : 0.0f;
+        float dr = e * l;
 #pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) den += __shfl_xor(den, s);
-    float num = 0.0f;
+        for (int s = 32; s >= 1; s >>= 1) dr += __shfl_xor(dr, s);
+        float nr = 0.0f;
 #pragma unroll
-    for (int ck = 0; ck < kSmallChunks; ++ck)
-        num = __builtin_fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), ck)),
-                             o[ck], num);
-    out[hq * kHD + tid] = num / den;
+        for (int i = 0; i < kMergeRound; ++i)
+            nr = __builtin_fmaf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, e), i)),
+                                o[i], nr);
+        num = __builtin_fmaf(num, alpha, nr);
+        den = __builtin_fmaf(den, alpha, dr);
+        M = mn;
+    }
+    part_n[wave][lane] = num;
+    if (lane == 0) {
+        part_m[wave] = M;
+        part_d[wave] = den;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, part_m[w]);
+        float tn = 0.0f, td = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const float mw = part_m[w];
+            const float e = mw == -INFINITY ? 0.0f : exp2f(mw - mx);  // a wave with no chunks
+            tn = __builtin_fmaf(e, part_n[w][lane], tn);
+            td = __builtin_fmaf(e, part_d[w], td);
+        }
+        out[hq * kHD + dim] = tn / td;
+    }
 }
 
 }  // namespace
@@ -410,12 +402,8 @@ int32_t attn_decode_enqueue(const uint16_t *q, const uint8_t *kc, const uint16_t
                        (int)chunk, ws);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
-    if (nchunks <= kSmallChunks)
-        hipLaunchKernelGGL(attn_combine_small_kernel, dim3((unsigned)n_q), dim3(256), 0, stream, ws,
-                           (int)nchunks, (int)n_q, out);
-    else
-        hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)n_q), dim3(256), 0, stream, ws,
-                           (int)nchunks, (int)n_q, out);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)n_q, kHD / 64), dim3(64 * kWaves), 0, stream, ws,
+                       (int)nchunks, (int)n_q, out);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
     return TQ_OK;

@@ -193,6 +193,15 @@ def test_attn_decode_long_context_sampled():
         assert_attn(out[6 * h: 6 * h + 6], ref, A, "32K kv head %d" % h)
 
 
+@pytest.mark.parametrize("T,n_q", [(32768, 4), (65536, 16)])
+def test_attn_decode_one_kv_head_many_chunks(T, n_q):
+    """One KV head splits into 256 and 512 chunks: the chunk merge folds
+    several rounds of 32 chunks per wave."""
+    q, c, (kn, ks, vn, vs) = attention_case(20800 + n_q, T, 1, n_q)
+    ref, A = oracle.attn_decode(q, kn, ks, vn, vs)
+    assert_attn(run_attention(q, c, T, n_q), ref, A, "T=%d n_q=%d" % (T, n_q))
+
+
 def test_attn_decode_errors():
     c = Cache(4, 64)
     q = torch.zeros(24, 256, dtype=torch.float16, device="cuda")
