@@ -24,6 +24,10 @@ COMMON = [
 DEVICE = ["-x", "hip", "--offload-arch=" + ARCH,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fno-gpu-rdc"]
+# Per-file device options.  The attention kernel keeps its MFMA accumulators
+# in ordinary VGPRs: with them in AGPRs the allocator copied all 64 output
+# accumulators into VGPRs on every tile for the (rarely taken) softmax rescale.
+EXTRA = {"tq_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc():
@@ -33,7 +37,7 @@ def _hipcc():
 
 def _compile(src, verbose):
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [_hipcc(), *COMMON, *DEVICE, "-c", src, "-o", obj]
+    cmd = [_hipcc(), *COMMON, *DEVICE, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

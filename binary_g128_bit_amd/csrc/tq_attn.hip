@@ -128,6 +128,50 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t *__restri
 }
 
 // --------------------------------------------------------------- partial
+// A 32-token tile of one KV head is four contiguous pieces of the cache: K
+// codes (4 KiB), V codes of the token block (4 KiB), K scales and V scales
+// (512 B each).  Each wave stages its tiles in LDS with direct global-to-LDS
+// loads (nine dwordx4 loads per tile: lane l of a load fills bytes 16 l of
+// its KiB) into a ring of two slots, and issues tile j + 1 before it computes
+// tile j, so every wave keeps a tile in flight while it works.  The source
+// address of each lane is permuted (16-byte units XOR-swizzled within a row)
+// so that the MFMA operand reads below hit distinct LDS banks.
+constexpr int kSlotBytes = 9216;  // K codes | V codes | K scales | V scales
+constexpr int kOffV = 4096, kOffKs = 8192;
+constexpr int kRingBytes = 2 * kSlotBytes;  // per wave
+static_assert(16 * (kHD + 2) * 4 <= kRingBytes, "a wave's merge rows fit in its ring");
+
+__device__ __forceinline__ u32x4 lds16(const unsigned char *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// Stage tile tb of KV head h into the LDS slot dst (wave-uniform).
+//   K codes: slot unit r * 8 + (j ^ (r & 7)) <- token r, 16-byte unit j;
+//   V codes: slot unit R * 4 + (k ^ ((R >> 1) & 3)) <- row R = 16 c + n of
+//            the block, unit k;
+//   scales:  lanes 0-31 copy the tile's K scales, lanes 32-63 its V scales.
+__device__ __forceinline__ void stage_tile(const uint32_t *__restrict__ kc, const uint16_t *__restrict__ ks,
+                                           const uint32_t *__restrict__ vc, const uint16_t *__restrict__ vs,
+                                           int64_t h, int64_t TC, int tb, unsigned char *dst, int lane) {
+    const int64_t blk = tb >> 5;
+    const unsigned char *kb = reinterpret_cast<const unsigned char *>(kc + (h * TC + tb) * 32);
+    const unsigned char *vb = reinterpret_cast<const unsigned char *>(vc + (h * (TC >> 5) + blk) * 1024);
+    const unsigned char *sb =
+        lane < 32 ? reinterpret_cast<const unsigned char *>(ks + (h * TC + tb) * 8) + 16 * lane
+                  : reinterpret_cast<const unsigned char *>(vs + (h * (TC >> 5) + blk) * 256) + 16 * (lane - 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int L = 64 * i + lane, r = L >> 3, j = (L & 7) ^ (r & 7);
+        __builtin_amdgcn_global_load_lds(kb + 16 * (8 * r + j), dst + 1024 * i, 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int L = 64 * i + lane, R = L >> 2, k = (L & 3) ^ ((R >> 1) & 3);
+        __builtin_amdgcn_global_load_lds(vb + 16 * (4 * R + k), dst + kOffV + 1024 * i, 16, 0, 0);
+    }
+    __builtin_amdgcn_global_load_lds(sb, dst + kOffKs, 16, 0, 0);
+}
+
 // Workgroup (chunk, KV head): 4 waves take consecutive 32-token tiles of the
 // chunk round-robin.  Lane l: head column n = l % 16 (a query head of the
 // group when n < R), lane group c = l / 16.
@@ -135,23 +179,34 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
     const uint16_t *__restrict__ q, const uint32_t *__restrict__ kc, const uint16_t *__restrict__ ks,
     const uint32_t *__restrict__ vc, const uint16_t *__restrict__ vs, int T, int64_t TC, int R,
     int chunk, float *__restrict__ ws) {
-    __shared__ float red[kWaves][16][kHD + 2];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[kWaves * kRingBytes];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, c = lane >> 4;
     const int h = blockIdx.y, ck = blockIdx.x;
     const int t_begin = ck * chunk, t_end = min(T, t_begin + chunk);
     const int nq = R;  // query heads of this KV head
+    unsigned char *ring = lds + wave * kRingBytes;
+    const int tfirst = t_begin + 32 * wave;
+    const int ntiles = tfirst < t_end ? (t_end - tfirst + 32 * kWaves - 1) / (32 * kWaves) : 0;
+
+    // the first two tiles go out before the query, whose wait covers them
+    if (ntiles > 0) stage_tile(kc, ks, vc, vs, h, TC, tfirst, ring, lane);
+    if (ntiles > 1) stage_tile(kc, ks, vc, vs, h, TC, tfirst + 32 * kWaves, ring + kSlotBytes, lane);
+    // query as the B operand: B[k = 8c + s of group g][n] = q[n][32g + 8c + s];
+    // columns n >= R load head R - 1 and are zeroed (one wait for all loads)
+    u32x4 qv[8];
+    const uint16_t *qrow = q + ((size_t)(h * nq + min(n, nq - 1))) * kHD + 8 * c;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) qv[g] = *reinterpret_cast<const u32x4 *>(qrow + 32 * g);
 
     uint32_t mask = 0x03C003C0u;
     asm volatile("" : "+v"(mask));
-    // query as the B operand: B[k = 8c + s of group g][n] = q[n][32g + 8c + s]
     half8 qb[8];
     float qs24[8];
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (n < nq)
-            v = *reinterpret_cast<const u32x4 *>(q + ((size_t)(h * nq + n)) * kHD + 32 * g + 8 * c);
+        const u32x4 v = n < nq ? qv[g] : u32x4{0u, 0u, 0u, 0u};
         qb[g] = __builtin_bit_cast(half8, v);
         float sq = 0.0f;
 #pragma unroll
@@ -169,22 +224,27 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
     for (int g = 0; g < 8; ++g) cs[g] = 0.0f;
     const float zs = kLog2e / 16.0f;  // 1 / sqrt(256), log2 domain
 
-    for (int tb = t_begin + 32 * wave; tb < t_end; tb += 32 * kWaves) {
-        const int64_t blk = tb >> 5;
+    for (int j = 0; j < ntiles; ++j) {
+        const int tb = tfirst + 32 * kWaves * j;
+        // in flight: tile j and, unless j is the last, tile j + 1
+        if (j + 1 < ntiles)
+            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        unsigned char *slot = ring + (j & 1) * kSlotBytes;
         // scores of the tile's two 16-token halves: z[u][i] for token
         // tb + 16u + 4c + i, head n
         float z[2][4];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int trow = tb + 16 * u + n;  // the A row this lane supplies
-            const u32x4 *kr = reinterpret_cast<const u32x4 *>(kc + ((size_t)h * TC + trow) * 32 + 8 * c);
-            const u32x4 k0 = kr[0], k1 = kr[1];
+            const int r = 16 * u + n;  // the A row this lane supplies
+            const u32x4 k0 = lds16(slot + 16 * (8 * r + ((2 * c) ^ (r & 7))));
+            const u32x4 k1 = lds16(slot + 16 * (8 * r + ((2 * c + 1) ^ (r & 7))));
             const uint32_t kw[8] = {k0[0], k0[1], k0[2], k0[3], k1[0], k1[1], k1[2], k1[3]};
-            // scales of the lane's D rows: tokens tb + 16u + 4c + i, all groups
-            const uint16_t *sp = ks + ((size_t)h * TC + tb + 16 * u + 4 * c) * 8;
+            // scales of the lane's D rows: tokens 16u + 4c + i of the tile, all groups
             u32x4 sv[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sv[i] = reinterpret_cast<const u32x4 *>(sp)[i];
+            for (int i = 0; i < 4; ++i) sv[i] = lds16(slot + kOffKs + 16 * (16 * u + 4 * c + i));
             float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int g = 0; g < 8; ++g) {
@@ -208,10 +268,14 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
         mt = xor_max(mt, 16);
         mt = xor_max(mt, 32);
         const float mn = fmaxf(m, mt);
-        if (__any(mn > m)) {
+        // the running maximum moves only when a score passes it by more than
+        // 2 (log2 domain): the probabilities below stay <= 4, so p d_V stays
+        // inside the FP16 range for every finite FP16 value (4 * 65504 / 7),
+        // and most tiles skip the rescale
+        if (__any(mn > m + 2.0f)) {
             const float alpha = exp2f(m - mn);  // 0 on the first tile (m = -inf)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) oacc[j] *= alpha;
+            for (int jj = 0; jj < 16; ++jj) oacc[jj] *= alpha;
             lsum *= alpha;
 #pragma unroll
             for (int g = 0; g < 8; ++g) cs[g] *= alpha;
@@ -226,13 +290,12 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
         // P^T scaled by the value scales, per group: B'[k = s][n] = p_s d_V
         const half2_t p2[4] = {half2_t{(_Float16)p[0], (_Float16)p[1]}, half2_t{(_Float16)p[2], (_Float16)p[3]},
                                half2_t{(_Float16)p[4], (_Float16)p[5]}, half2_t{(_Float16)p[6], (_Float16)p[7]}};
-        const u32x4 *vsp = reinterpret_cast<const u32x4 *>(vs + ((size_t)h * (TC >> 5) + blk) * 256 + 64 * c);
         half8 bp[8];
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
             // (the elements go through plain uint32_t: a bit cast taken directly
             // of a vector element has read element 0 for every index)
-            const u32x4 dv = vsp[g];
+            const u32x4 dv = lds16(slot + kOffKs + 512 + 128 * c + 16 * g);
             const uint32_t d0 = dv[0], d1 = dv[1], d2 = dv[2], d3 = dv[3];
             const half2_t b0 = p2[0] * __builtin_bit_cast(half2_t, d0);
             const half2_t b1 = p2[1] * __builtin_bit_cast(half2_t, d1);
@@ -247,15 +310,26 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
             cs[g] = __builtin_amdgcn_fdot2(b3, one2, sum, false) + cs[g];
         }
         // O^T += V^T P'^T over 16 tiles of 16 dimensions
-        const u32x4 *vr = reinterpret_cast<const u32x4 *>(vc + ((size_t)h * (TC >> 5) + blk) * 1024 + (16 * c + n) * 16);
-        const u32x4 v0 = vr[0], v1 = vr[1], v2 = vr[2], v3 = vr[3];
-        const uint32_t vw[16] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3],
-                                 v2[0], v2[1], v2[2], v2[3], v3[0], v3[1], v3[2], v3[3]};
+        const int Rv = 16 * c + n;
+        uint32_t vw[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) oacc[j] = mfma(decode8<kExp15>(vw[j], mask), bp[j >> 1], oacc[j]);
+        for (int k = 0; k < 4; ++k) {
+            const u32x4 v = lds16(slot + kOffV + 16 * (4 * Rv + (k ^ ((Rv >> 1) & 3))));
+            vw[4 * k] = v[0];
+            vw[4 * k + 1] = v[1];
+            vw[4 * k + 2] = v[2];
+            vw[4 * k + 3] = v[3];
+        }
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) oacc[jj] = mfma(decode8<kExp15>(vw[jj], mask), bp[jj >> 1], oacc[jj]);
+        // tile j + 2 into this slot: every read of it above has returned (its
+        // value is in use)
+        if (j + 2 < ntiles) stage_tile(kc, ks, vc, vs, h, TC, tb + 64 * kWaves, slot, lane);
     }
 
-    // this wave's (max, sum, output) per head into LDS: O = 16 D - 24 cs
+    // this wave's (max, sum, output) per head into LDS, over its own ring
+    // once every load into it has landed: O = 16 D - 24 cs
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
 #pragma unroll
@@ -263,14 +337,15 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
         cs[g] += __shfl_xor(cs[g], 16);
         cs[g] += __shfl_xor(cs[g], 32);
     }
+    float *red = reinterpret_cast<float *>(ring);  // [16][kHD + 2]
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int jj = 0; jj < 16; ++jj)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            red[wave][n][16 * j + 4 * c + i] = 16.0f * oacc[j][i] - 24.0f * cs[j >> 1];
+            red[n * (kHD + 2) + 16 * jj + 4 * c + i] = 16.0f * oacc[jj][i] - 24.0f * cs[jj >> 1];
     if (c == 0) {
-        red[wave][n][kHD] = m;
-        red[wave][n][kHD + 1] = lsum;
+        red[n * (kHD + 2) + kHD] = m;
+        red[n * (kHD + 2) + kHD + 1] = lsum;
     }
     __syncthreads();
     // merge the waves: thread = dimension, loop over the query heads
@@ -278,14 +353,16 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
     for (int hn = 0; hn < nq; ++hn) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) mx = fmaxf(mx, red[w][hn][kHD]);
+        for (int w = 0; w < kWaves; ++w)
+            mx = fmaxf(mx, reinterpret_cast<const float *>(lds + w * kRingBytes)[hn * (kHD + 2) + kHD]);
         float o = 0.0f, l = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float mw = red[w][hn][kHD];
+            const float *rw = reinterpret_cast<const float *>(lds + w * kRingBytes) + hn * (kHD + 2);
+            const float mw = rw[kHD];
             const float e = mw == -INFINITY ? 0.0f : exp2f(mw - mx);
-            o += e * red[w][hn][dim];
-            l += e * red[w][hn][kHD + 1];
+            o += e * rw[dim];
+            l += e * rw[kHD + 1];
         }
         float *dst = ws + ((size_t)ck * gridDim.y * nq + h * nq + hn) * (kHD + 2);
         dst[dim] = o;
