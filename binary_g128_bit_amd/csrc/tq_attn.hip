@@ -27,12 +27,13 @@
 // [6,10) under exponent 19, the exact FP16 16 + nibble, so the MFMA returns
 // sum (16 + nibble) q exactly and a group's score is d (D - 24 sum q): the
 // scale applied once per group and token.  The softmax is online in the
-// log2 domain.  O^T = V^T P^T takes the values as A (16 dims x 32 tokens)
-// and P^T scaled by each token's value scale (FP16) as B; the token order of
-// the K dimension is the one the score tiles leave in each lane, so P needs
-// no data movement.  A workgroup of 4 waves splits a chunk of the sequence,
-// merges its waves in LDS and writes (max, sum, output) per query head; a
-// second kernel merges the chunks.
+// log2 domain.  O^T = V^T P^T takes the values as A (16 dims x 32 tokens,
+// the same 16 + nibble decode) and P^T scaled by each token's value scale
+// (FP16) as B; the token order of the K dimension is the one the score tiles
+// leave in each lane, so P needs no data movement, and O = D - 24 sum B.  A
+// workgroup of 4 waves splits a chunk of the sequence, stages its tiles in
+// LDS, merges its waves there and writes (max, sum, output) per query head;
+// a second kernel merges the chunks.
 #include <hip/hip_runtime.h>
 
 #include "tq_internal.h"
@@ -59,21 +60,15 @@ __device__ __forceinline__ f32x4 mfma(half8 a, half8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
-// 8 nibbles of a code dword as FP16 values linear in the nibble, pairs in
-// order: nibble at mantissa bits [6,10) under exponent field E, i.e.
-// 2^(E-15) (1 + nibble/16).  E = 15 gives 1 + nibble/16, E = 19 gives
-// 16 + nibble.  The mask stays in a VGPR (gfx9 VOP3 takes no literal), so each
-// pair is one shift and one v_and_or_b32.
-template <uint32_t EXP2>
+// 8 nibbles of a code dword as FP16 values, pairs in order: the nibble at
+// mantissa bits [6,10) under exponent field 19 is exactly 16 + nibble.  The
+// mask stays in a VGPR (gfx9 VOP3 takes no literal), so each pair is one
+// shift and one v_and_or_b32.
+constexpr uint32_t kExp19 = 0x4C004C00u;
 __device__ __forceinline__ half8 decode8(uint32_t w, uint32_t mask) {
-    return as_half8(((w << 6) & mask) | EXP2, ((w << 2) & mask) | EXP2, ((w >> 2) & mask) | EXP2,
-                    ((w >> 6) & mask) | EXP2);
+    return as_half8(((w << 6) & mask) | kExp19, ((w << 2) & mask) | kExp19, ((w >> 2) & mask) | kExp19,
+                    ((w >> 6) & mask) | kExp19);
 }
-constexpr uint32_t kExp15 = 0x3C003C00u;  // 1 + nibble/16
-constexpr uint32_t kExp19 = 0x4C004C00u;  // 16 + nibble
-
-// token offset within a 32-token block of K slot s of lane group c
-__device__ __forceinline__ int tau(int c, int s) { return s < 4 ? 4 * c + s : 12 + 4 * c + s; }
 
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
 
@@ -208,9 +203,12 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
     for (int g = 0; g < 8; ++g) {
         const u32x4 v = n < nq ? qv[g] : u32x4{0u, 0u, 0u, 0u};
         qb[g] = __builtin_bit_cast(half8, v);
-        float sq = 0.0f;
-#pragma unroll
-        for (int s = 0; s < 8; ++s) sq += (float)qb[g][s];
+        const half2_t one2 = {(_Float16)1.0f, (_Float16)1.0f};
+        const uint32_t v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+        float sq = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v0), one2, 0.0f, false);
+        sq = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v1), one2, sq, false);
+        sq = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v2), one2, sq, false);
+        sq = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v3), one2, sq, false);
         sq += __shfl_xor(sq, 16);
         sq += __shfl_xor(sq, 32);
         qs24[g] = -24.0f * sq;
@@ -248,7 +246,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
             float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int g = 0; g < 8; ++g) {
-                const f32x4 D = mfma(decode8<kExp19>(kw[g], mask), qb[g], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
+                const f32x4 D = mfma(decode8(kw[g], mask), qb[g], f32x4{0.0f, 0.0f, 0.0f, 0.0f});
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t pair = sv[i][g >> 1];
@@ -273,7 +271,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
         // inside the FP16 range for every finite FP16 value (4 * 65504 / 7),
         // and most tiles skip the rescale
         if (__any(mn > m + 2.0f)) {
-            const float alpha = exp2f(m - mn);  // 0 on the first tile (m = -inf)
+            const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first tile (m = -inf)
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) oacc[jj] *= alpha;
             lsum *= alpha;
@@ -284,7 +282,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
         float p[8];
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-            p[s] = exp2f(z[s >> 2][s & 3] - m);
+            p[s] = __builtin_amdgcn_exp2f(z[s >> 2][s & 3] - m);
             lsum += p[s];
         }
         // P^T scaled by the value scales, per group: B'[k = s][n] = p_s d_V
@@ -321,14 +319,14 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
             vw[4 * k + 3] = v[3];
         }
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) oacc[jj] = mfma(decode8<kExp15>(vw[jj], mask), bp[jj >> 1], oacc[jj]);
+        for (int jj = 0; jj < 16; ++jj) oacc[jj] = mfma(decode8(vw[jj], mask), bp[jj >> 1], oacc[jj]);
         // tile j + 2 into this slot: every read of it above has returned (its
         // value is in use)
         if (j + 2 < ntiles) stage_tile(kc, ks, vc, vs, h, TC, tb + 64 * kWaves, slot, lane);
     }
 
     // this wave's (max, sum, output) per head into LDS, over its own ring
-    // once every load into it has landed: O = 16 D - 24 cs
+    // once every load into it has landed: O = D - 24 cs
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lsum += __shfl_xor(lsum, 16);
     lsum += __shfl_xor(lsum, 32);
@@ -342,33 +340,44 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
     for (int jj = 0; jj < 16; ++jj)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            red[n * (kHD + 2) + 16 * jj + 4 * c + i] = 16.0f * oacc[jj][i] - 24.0f * cs[jj >> 1];
+            red[n * (kHD + 2) + 16 * jj + 4 * c + i] = __builtin_fmaf(-24.0f, cs[jj >> 1], oacc[jj][i]);
     if (c == 0) {
         red[n * (kHD + 2) + kHD] = m;
         red[n * (kHD + 2) + kHD + 1] = lsum;
     }
     __syncthreads();
+    // the waves' weights per query head, once: thread (head hn, wave w) of wave 0
+    __shared__ float wgt[16][kWaves];
+    __shared__ float head_m[16], head_l[16];
+    if (wave == 0) {
+        const int hn = lane >> 2, w = lane & 3;
+        const float *rw = reinterpret_cast<const float *>(lds + w * kRingBytes) + hn * (kHD + 2);
+        const float mw = rw[kHD];
+        float mx = fmaxf(mw, __shfl_xor(mw, 1));
+        mx = fmaxf(mx, __shfl_xor(mx, 2));
+        const float e = mw == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(mw - mx);  // a wave with no tile
+        float l = e * rw[kHD + 1];
+        l += __shfl_xor(l, 1);
+        l += __shfl_xor(l, 2);
+        wgt[hn][w] = e;
+        if (w == 0) {
+            head_m[hn] = mx;
+            head_l[hn] = l;
+        }
+    }
+    __syncthreads();
     // merge the waves: thread = dimension, loop over the query heads
     const int dim = threadIdx.x;
     for (int hn = 0; hn < nq; ++hn) {
-        float mx = -INFINITY;
+        float o = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)
-            mx = fmaxf(mx, reinterpret_cast<const float *>(lds + w * kRingBytes)[hn * (kHD + 2) + kHD]);
-        float o = 0.0f, l = 0.0f;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float *rw = reinterpret_cast<const float *>(lds + w * kRingBytes) + hn * (kHD + 2);
-            const float mw = rw[kHD];
-            const float e = mw == -INFINITY ? 0.0f : exp2f(mw - mx);
-            o += e * rw[dim];
-            l += e * rw[kHD + 1];
-        }
+            o = __builtin_fmaf(wgt[hn][w], reinterpret_cast<const float *>(lds + w * kRingBytes)[hn * (kHD + 2) + dim], o);
         float *dst = ws + ((size_t)ck * gridDim.y * nq + h * nq + hn) * (kHD + 2);
         dst[dim] = o;
         if (dim == 0) {
-            dst[kHD] = mx;
-            dst[kHD + 1] = l;
+            dst[kHD] = head_m[hn];
+            dst[kHD + 1] = head_l[hn];
         }
     }
 }
