@@ -12,6 +12,9 @@ int32_t gemv_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_
                      int64_t N, int64_t K, int32_t variant, hipStream_t stream);
 int32_t gemm_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
                      int64_t M, int64_t N, int64_t K, int32_t variant, hipStream_t stream);
+int32_t gemm_mcol_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
+                          int64_t M, int64_t N, int64_t K, int32_t variant, hipStream_t stream,
+                          bool *handled);
 int32_t gemv5_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
                       int64_t N, int64_t K, hipStream_t stream);
 int32_t gemv_affine_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
@@ -84,6 +87,10 @@ int32_t tq_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
     if (M == 1)
         return tq::gemv_enqueue(codes, scales, X, Y, N, K, variant,
                                 static_cast<hipStream_t>(stream));
+    bool handled = false;
+    const int32_t rc = tq::gemm_mcol_enqueue(codes, scales, X, Y, M, N, K, variant,
+                                             static_cast<hipStream_t>(stream), &handled);
+    if (handled || rc != TQ_OK) return rc;
     return tq::gemm_enqueue(codes, scales, X, Y, M, N, K, variant,
                             static_cast<hipStream_t>(stream));
 }

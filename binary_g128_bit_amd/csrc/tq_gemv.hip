@@ -823,6 +823,300 @@ hipError_t dispatch_xreg(const Config &c, const uint8_t *codes, const uint16_t *
 
 }  // namespace
 
+namespace {
+
+// ---------------------------------------------------------------------------
+// Small-batch GEMM on the VALU: the LDS-activation GEMV above with up to MC
+// activation rows.  A code dword is decoded into its slot values once (the
+// mask ops of tern_acc32 / bin_slots) and each value meets the MC rows with
+// one v_dot2 apiece, so 16 ternary weights cost about 10 + 8 MC VALU ops
+// instead of padding a two-row batch to the 16-row MFMA operand.  The
+// activations of row m sit in LDS as pair quads
+// xq[(m * QPC + q) * CAP + c] (quad q of chunk c, consecutive chunks
+// adjacent, so the LPR lanes of a weight row read consecutive 16 bytes) and a
+// seed per (row, chunk); rows m >= M and chunks past the row are zeros and
+// add exactly nothing.
+template <int VARIANT>
+struct MCol {
+    using XU = XUnit<VARIANT>;                        // 4 units per 16-byte chunk
+    static constexpr int UNIT = XU::UNIT;             // weights per unit: 16 or 32
+    static constexpr int QPU = UNIT / 8;              // pair quads per unit: 2 or 4
+    static constexpr int QPC = 4 * QPU;               // pair quads per chunk: 8 or 16
+    static constexpr int CPG = VARIANT == TQ_BINARY ? 1 : 2;  // chunks per group
+};
+
+template <int VARIANT, int MC, int LPR, int NU>
+constexpr size_t mcol_lds_bytes() {
+    return (size_t)MC * LPR * NU * (MCol<VARIANT>::QPC * 16 + 4);
+}
+
+// Pairs and the chunk's seed contribution of one staged unit (the pairing of
+// XUnit::store), written as quads; lanes holding the 4 units of a chunk are
+// 4 aligned consecutive lanes, so the seed reduces with seg_sum<4>.
+template <int VARIANT, int CAP>
+__device__ __forceinline__ void mcol_store(const XUnit<VARIANT> &xu, u32x4 *xq, float *xseed, int m,
+                                           int u, bool real) {
+    using MF = MCol<VARIANT>;
+    constexpr int UNIT = MF::UNIT, V4 = UNIT / 8;
+    uint32_t xp[UNIT / 2];
+#pragma unroll
+    for (int i = 0; i < UNIT / 4; ++i) {
+        const uint32_t l = xu.v[i / 4][i % 4], h = xu.v[V4 / 2 + i / 4][i % 4];
+        xp[2 * i] = real ? (l & 0xFFFFu) | (h << 16) : 0u;
+        xp[2 * i + 1] = real ? (l >> 16) | (h & 0xFFFF0000u) : 0u;
+    }
+    float z = 0.0f;
+#pragma unroll
+    for (int i = 0; i < UNIT / 2; ++i) z = dot2(xp[i], XUnit<VARIANT>::zweight(i), z);
+    const int c = u / 4, k = u % 4;
+#pragma unroll
+    for (int qq = 0; qq < MF::QPU; ++qq)
+        xq[(m * MF::QPC + k * MF::QPU + qq) * CAP + c] =
+            u32x4{xp[4 * qq], xp[4 * qq + 1], xp[4 * qq + 2], xp[4 * qq + 3]};
+    z = seg_sum<4>(z) * -XUnit<VARIANT>::kSeedScale;
+    if (k == 0) xseed[m * CAP + c] = z;
+}
+
+// One code dword (16 ternary or 32 binary weights) against MC rows of pairs
+// xp[m][...] (unit-local pair order), accumulated into a[m].
+template <int VARIANT, int MC>
+__device__ __forceinline__ void mcol_dword(uint32_t d, const uint32_t (&xp)[MC][MCol<VARIANT>::UNIT / 2],
+                                           float (&a)[MC], const Masks &k) {
+    if constexpr (VARIANT == TQ_TERNARY) {
+        const uint32_t c6 = d << 6, r4 = d >> 4;
+        // slot values (pair p in the low half, p + 8 in the high half), as in tern_acc32
+        const uint32_t w[8] = {(c6 & k.m6) | 0x14001400u, (c6 & k.m8) | 0x0C000C00u, c6 & 0x0C000C00u,
+                               (d & k.m6) | 0x14001400u,  (d & k.m8) | 0x0C000C00u,  d & 0x0C000C00u,
+                               (r4 & k.m8) | 0x0C000C00u, r4 & 0x0C000C00u};
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+#pragma unroll
+            for (int m = 0; m < MC; ++m) a[m] = dot2(w[p], xp[m][p], a[m]);
+    } else {
+        // bit slots as in bin_slots: copy d reads bits 11..6 (pairs 11..6),
+        // d << 6 bits 5..0 (pairs 5..0), d >> 4 bits 15..12 (pairs 15..12)
+        const uint32_t c6 = d << 6, r4 = d >> 4;
+        const uint32_t src[3] = {d, c6, r4};
+        const int p0[3] = {11, 5, 15}, cnt[3] = {6, 6, 4};
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            const uint32_t c = src[s];
+            const uint32_t w[6] = {c & 0x08000800u, (c & k.b10) | 0x08000800u, (c & k.b9) | 0x0C000C00u,
+                                   (c & k.b8) | 0x10001000u, (c & k.b7) | 0x14001400u,
+                                   (c & k.b6) | 0x18001800u};
+#pragma unroll
+            for (int b = 0; b < cnt[s]; ++b)
+#pragma unroll
+                for (int m = 0; m < MC; ++m) a[m] = dot2(w[b], xp[m][p0[s] - b], a[m]);
+        }
+    }
+}
+
+// Persistent workgroups as in gemv_kernel (one per CU, WAVES waves walking a
+// contiguous range of row blocks, two register sets of codes in ping-pong).
+// A block is RPL * 64/LPR weight rows: lane segment seg takes rows seg,
+// seg + 64/LPR, ...; every activation quad read from LDS serves the RPL rows.
+// Y[m][n] for m < M.
+template <int VARIANT, int MC, int LPR, int NU, int RPL, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) void gemm_mcol_kernel(const uint8_t *__restrict__ codes,
+                                                               const uint16_t *__restrict__ scales,
+                                                               const uint16_t *__restrict__ X,
+                                                               float *__restrict__ Y, int M, int N,
+                                                               int K) {
+    extern __shared__ uint32_t xs[];
+    using MF = MCol<VARIANT>;
+    using XU = XUnit<VARIANT>;
+    constexpr int THREADS = 64 * WAVES, RS = 64 / LPR, RB = RS * RPL, CAP = LPR * NU;
+    constexpr int TOTAL = MC * CAP * 4;  // staged units
+    constexpr int XMAX = (TOTAL + THREADS - 1) / THREADS;
+    constexpr int HP = MF::UNIT / 2;     // pairs per unit (per code dword)
+    u32x4 *xq = reinterpret_cast<u32x4 *>(xs);
+    float *xseed = reinterpret_cast<float *>(xs + MC * MF::QPC * CAP * 4);
+    const int G = K >> 7, CPR = G * MF::CPG;
+    const int nunits = CPR * 4;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int seg = lane / LPR, j = lane % LPR;
+    const int nblocks = (N + RB - 1) / RB;
+    const int b_begin = (int)(((long long)blockIdx.x * nblocks) / gridDim.x);
+    const int b_end = (int)(((long long)(blockIdx.x + 1) * nblocks) / gridDim.x);
+    const Masks km;
+    auto rows_of = [&](int bb, int (&row)[RPL]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) row[r] = min(bb * RB + r * RS + seg, N - 1);
+    };
+
+    // 1. activation loads (L2-resident), then the first block's codes
+    XU xu[XMAX];
+    int xm[XMAX], xu_i[XMAX];
+#pragma unroll
+    for (int k = 0; k < XMAX; ++k) {
+        const int it = min((int)threadIdx.x + k * THREADS, TOTAL - 1);
+        xm[k] = it / (CAP * 4);
+        xu_i[k] = it % (CAP * 4);
+        xu[k].load(X + (size_t)min(xm[k], M - 1) * K, min(xu_i[k], nunits - 1));
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 ca[NU][RPL], cb[NU][RPL];
+    uint32_t sa[NU][RPL], sb[NU][RPL];
+    int b = b_begin + wave;
+    int row[RPL];
+    rows_of(min(b, b_end - 1), row);
+    load_block<VARIANT, LPR, NU, RPL, true>(codes, scales, row, j, CPR, G, ca, sa);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // 2. pairs and seeds into LDS (threads past the last unit redo it; only
+    // the first unit of a chunk writes its seed)
+#pragma unroll
+    for (int k = 0; k < XMAX; ++k)
+        mcol_store<VARIANT, CAP>(xu[k], xq, xseed, xm[k], xu_i[k], xu_i[k] < nunits && xm[k] < M);
+    __syncthreads();
+
+    auto block = [&](const u32x4 (&c)[NU][RPL], const uint32_t (&sv)[NU][RPL], int bb)
+                     __attribute__((always_inline)) {
+        // the activation reads are the same for every block: an opaque base
+        // keeps them inside the loop (hoisted, they would pin NU * 4 * MC * QPU
+        // quads in registers across it)
+        uint32_t base = 0;
+        asm volatile("" : "+v"(base));
+        const u32x4 *xqb = xq + base;
+        const float *xsb = xseed + base;
+        float acc[RPL][MC];
+#pragma unroll
+        for (int r = 0; r < RPL; ++r)
+#pragma unroll
+            for (int m = 0; m < MC; ++m) acc[r][m] = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+            const int col = j + i * LPR;  // x slot (zeros past the row)
+            float a[RPL][MC];
+#pragma unroll
+            for (int m = 0; m < MC; ++m) {
+                const float sd = xsb[m * CAP + col];
+#pragma unroll
+                for (int r = 0; r < RPL; ++r) a[r][m] = sd;
+            }
+#pragma unroll
+            for (int dw = 0; dw < 4; ++dw) {
+                uint32_t xp[MC][HP];
+#pragma unroll
+                for (int m = 0; m < MC; ++m)
+#pragma unroll
+                    for (int qq = 0; qq < MF::QPU; ++qq) {
+                        const u32x4 v = xqb[(m * MF::QPC + dw * MF::QPU + qq) * CAP + col];
+                        xp[m][4 * qq] = v[0];
+                        xp[m][4 * qq + 1] = v[1];
+                        xp[m][4 * qq + 2] = v[2];
+                        xp[m][4 * qq + 3] = v[3];
+                    }
+#pragma unroll
+                for (int r = 0; r < RPL; ++r) {
+                    mcol_dword<VARIANT, MC>(c[i][r][dw], xp, a[r], km);
+                    // one dword's slot values and pairs live at a time: left
+                    // free, the compiler sinks the later rows' dot products to
+                    // the end of the block and keeps every decoded value for them
+#pragma unroll
+                    for (int m = 0; m < MC; ++m) asm volatile("" : "+v"(a[r][m]));
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < RPL; ++r) {
+                const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)sv[i][r]);
+#pragma unroll
+                for (int m = 0; m < MC; ++m) acc[r][m] = __builtin_fmaf(sc, a[r][m], acc[r][m]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const int rr = bb * RB + r * RS + seg;
+#pragma unroll
+            for (int m = 0; m < MC; ++m) {
+                const float out = seg_sum<LPR>(acc[r][m]) * XU::kRowScale;
+                if (j == 0 && rr < N && m < M) Y[(size_t)m * N + rr] = out;
+            }
+        }
+    };
+
+    // 3. ping-pong over this wave's blocks
+    for (; b < b_end; b += 2 * WAVES) {
+        const int b2 = b + WAVES;
+        if (b2 < b_end) {
+            rows_of(b2, row);
+            load_block<VARIANT, LPR, NU, RPL, true>(codes, scales, row, j, CPR, G, cb, sb);
+        }
+        block(ca, sa, b);
+        if (b2 >= b_end) break;
+        const int b3 = b2 + WAVES;
+        if (b3 < b_end) {
+            rows_of(b3, row);
+            load_block<VARIANT, LPR, NU, RPL, true>(codes, scales, row, j, CPR, G, ca, sa);
+        }
+        block(cb, sb, b2);
+    }
+}
+
+template <int VARIANT, int MC, int LPR, int NU, int RPL>
+hipError_t launch_mcol(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
+                       int M, int N, int K, hipStream_t stream) {
+    constexpr int WAVES = 8, RB = 64 / LPR * RPL;
+    const int nblocks = (N + RB - 1) / RB;
+    const int grid = max(1, min(device_cus(), (nblocks + WAVES - 1) / WAVES));
+    constexpr size_t lds = mcol_lds_bytes<VARIANT, MC, LPR, NU>();
+    static_assert(lds <= kMaxLds, "activation tile above the LDS of a workgroup");
+    hipLaunchKernelGGL((gemm_mcol_kernel<VARIANT, MC, LPR, NU, RPL, WAVES>), dim3(grid),
+                       dim3(64 * WAVES), lds, stream, codes, scales, X, Y, M, N, K);
+    return hipGetLastError();
+}
+
+// Shapes (LPR, NU): the least chunk capacity LPR * NU that covers the row and
+// whose MC-row activation tile fits the workgroup's LDS.
+struct McolShape {
+    int lpr, nu;
+};
+constexpr McolShape kMcolShapes[] = {{8, 5}, {16, 5}, {16, 9}, {32, 5}, {32, 9}, {64, 5}, {64, 9}};
+constexpr int kMcolRpl = 2;  // weight rows per lane segment (one at nine chunks per lane)
+
+template <int VARIANT, int MC>
+hipError_t dispatch_mcol(int cpr, const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
+                         float *Y, int M, int N, int K, hipStream_t s, bool *handled) {
+    constexpr size_t per_chunk = (size_t)MC * (MCol<VARIANT>::QPC * 16 + 4);
+    for (const McolShape &sh : kMcolShapes) {
+        if (sh.lpr * sh.nu < cpr || (size_t)sh.lpr * sh.nu * per_chunk > kMaxLds) continue;
+        *handled = true;
+#define TQ_MC(L, U)                                                                      \
+    if constexpr (mcol_lds_bytes<VARIANT, MC, L, U>() <= kMaxLds)                          \
+        if (sh.lpr == L && sh.nu == U)                                                     \
+            return launch_mcol<VARIANT, MC, L, U, (U < 9 ? kMcolRpl : 1)>(codes, scales, X, Y, M, N, K, s);
+        TQ_MC(8, 5) TQ_MC(16, 5) TQ_MC(16, 9) TQ_MC(32, 5) TQ_MC(32, 9) TQ_MC(64, 5) TQ_MC(64, 9)
+#undef TQ_MC
+    }
+    *handled = false;
+    return hipSuccess;
+}
+
+}  // namespace
+
+// Small-batch GEMM on the VALU for M = 2 (ternary and binary) where the
+// activation tile fits LDS; *handled is false otherwise (the caller then takes
+// the MFMA kernels).  From M = 3 the v_dot2 per weight pair and row make this
+// kernel VALU-bound above the MFMA kernels: at M = 4 it measured 15.2 us on
+// 17408 x 5120 against 13.5 us, with the VALU busy 70 % of the time.
+int32_t gemm_mcol_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
+                          int64_t M, int64_t N, int64_t K, int32_t variant, hipStream_t stream,
+                          bool *handled) {
+    *handled = false;
+    if (M != 2 || (variant != TQ_TERNARY && variant != TQ_BINARY)) return TQ_OK;
+    const int cpr = (int)(K / 128) * (variant == TQ_TERNARY ? 2 : 1);
+    const int m = (int)M, n = (int)N, k = (int)K;
+    const hipError_t e =
+        variant == TQ_TERNARY
+            ? dispatch_mcol<TQ_TERNARY, 2>(cpr, codes, scales, X, Y, m, n, k, stream, handled)
+            : dispatch_mcol<TQ_BINARY, 2>(cpr, codes, scales, X, Y, m, n, k, stream, handled);
+    if (e != hipSuccess) return fail(TQ_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));
+    return TQ_OK;
+}
+
 int32_t gemv_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y,
                      int64_t N, int64_t K, int32_t variant, hipStream_t stream) {
     const int cpr = (int)(K / 128) * (variant == TQ_TERNARY ? 2 : 1);

@@ -211,7 +211,7 @@ def _sampled_rows(N, n, seed):
     return rows
 
 
-@pytest.mark.parametrize("M", [4, 16, 64, 512])
+@pytest.mark.parametrize("M", [2, 4, 16, 64, 512])
 @pytest.mark.parametrize("N,K", [synth.GATE_UP, synth.DOWN])
 def test_gemm_full_size_sampled(M, N, K):
     """Speculative-verify / prefill widths on the MLP shapes: the full GEMM on
@@ -239,10 +239,12 @@ def test_lm_head_sampled(M):
                                    (100, 200, 2176), (5, 1000, 29952), (2, 77, 65536),
                                    (128, 128, 128), (130, 70, 384), (257, 300, 1024),
                                    (200, 129, 5120), (7, 33, 640), (6, 129, 17408),
-                                   (8, 65, 5120), (6, 65600, 256)])
+                                   (8, 65, 5120), (6, 65600, 256), (2, 1001, 17408),
+                                   (2, 33, 30080)])
 def test_gemm_ragged(M, N, K, variant):
     """Ragged activation and weight tiles, K of one group (most waves of a
-    workgroup idle), the largest K, and 5..8 rows (eight staged rows)."""
+    workgroup idle), the largest K, 5..8 rows (eight staged rows) and two-row
+    batches near the capacity of the two-row VALU kernel's LDS tile."""
     codes, s, X = case(9700 + M + N + K, N, K, M, variant, exact=True)
     Y = gpu_gemm(codes, s, X, variant, N, K)
     Yref, _ = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
@@ -253,7 +255,7 @@ def test_gemm_ragged(M, N, K, variant):
     assert_tol(Y, Yref, A, "gemm M=%d N=%d K=%d" % (M, N, K))
 
 
-@pytest.mark.parametrize("M", [4, 16])
+@pytest.mark.parametrize("M", [2, 4, 16])
 @pytest.mark.parametrize("N,K", [synth.GATE_UP, synth.DOWN])
 def test_gemm_binary_full_size_sampled(M, N, K):
     codes, s, X = case(synth.seed_for(4, 50 + M + N % 7), N, K, M, BIN, exact=False)
@@ -263,10 +265,11 @@ def test_gemm_binary_full_size_sampled(M, N, K):
     assert_tol(Y[:, rows], Yref, A, "binary gemm M=%d %dx%d" % (M, N, K))
 
 
-def test_gemm_zero_rows_and_special_scales():
+@pytest.mark.parametrize("M", [2, 8])
+def test_gemm_zero_rows_and_special_scales(M):
     """All-zero trit rows give |y| <= 1e-5 (the bound with A = 0); zero,
     subnormal and large scales pass through the FP32 group scaling."""
-    N, K, M = 96, 1024, 8
+    N, K = 96, 1024
     t, s, X = synth.problem(9900, N, K, M, TERN, False)
     t[:32] = 0
     s[40, :] = 0
