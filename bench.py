@@ -297,7 +297,8 @@ def gemm_widths(torch, tq, gen, stream, bufs, slots):
         pool = [(c[:N], s[:N]) for c, s in (bufs[r][m] for r in range(slots))]
         X = gen.act(512, K)
         Y = torch.empty(512, N, dtype=torch.float32, device=gen.dev)
-        for M in synth.GEMM_WIDTHS:
+        # the configured widths and a two-row batch (the VALU kernel's width)
+        for M in (2,) + tuple(synth.GEMM_WIDTHS):
             Xm, Ym = X[:M], Y[:M]
             ms = back_to_back_ms(torch, stream,
                                  lambda i: tq.tq_gemm(pool[i % len(pool)][0], pool[i % len(pool)][1],
