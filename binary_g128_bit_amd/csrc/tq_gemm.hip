@@ -82,7 +82,8 @@ struct Fmt<TQ_TERNARY> {
     // weight index (of the lane's 32) in the low half of pair q
     static constexpr int lo(int q) { return 16 * (q / 8) + kOrder[q % 8]; }
     // correction weight of pair q: E slots (1 + 0), M slots (1 + 4)
-    static constexpr uint32_t corr(int q) { return pair(neg_units(q % 2 ? 5 : 1)); }
+    static constexpr int wt(int q) { return q % 2 ? 5 : 1; }
+    static constexpr uint32_t corr(int q) { return pair(neg_units(wt(q))); }
 };
 
 // Binary: 16 code bytes per row and group.  A lane's 32 weights are one code
@@ -96,7 +97,8 @@ struct Fmt<TQ_BINARY> {
     static constexpr int lo(int q) { return kLo[q]; }
     // slot offset in units of 2^-13: 0 at bit 11, 2^(10 - p) at bit p <= 10
     static constexpr int off(int s) { return s == 11 ? 0 : 1 << (10 - s); }
-    static constexpr uint32_t corr(int q) { return pair(neg_units(2 * off(kSlot[q]) + 1)); }
+    static constexpr int wt(int q) { return 2 * off(kSlot[q]) + 1; }
+    static constexpr uint32_t corr(int q) { return pair(neg_units(wt(q))); }
 };
 
 // Constants of v_and_or_b32 stay in VGPRs (gfx9 VOP3 takes no literal and
@@ -560,6 +562,201 @@ __global__ __launch_bounds__(64 * KW) void gemm_stage_kernel(const uint8_t *__re
     }
 }
 
+// Tiled variant for wide batches (M >= 64).  A workgroup owns a BM x BN
+// output tile.  Per group of K it decodes the BN weight rows once into LDS as
+// exact FP16 s * t (t is ternary, so s * t is an FP16 value: the slot value v
+// of the decode above becomes t with one packed FMA, v * 2^14 - wt(q), and
+// t * s with one packed multiply), and stages the BM activation rows beside
+// them, permuted into the decode's pair order (permute_x), so that both MFMA
+// operands read the same K order.  With the scale inside B the accumulators
+// run across all groups: no correction MFMAs and no per-group scale FMAs.
+// The eight waves specialise: four consumers run the MFMAs of group g from
+// one LDS buffer (2 x 2 waves of (BM/2) x (BN/2), v_mfma_f32_32x32x16_f16)
+// while four producers load, decode and stage group g + 1 into the other, one
+// barrier per group; a producer and a consumer share each SIMD, so the decode
+// and the MFMAs overlap (with all eight waves doing both in turn, the phases
+// ran one after the other and the kernel was slower than the per-group one).
+// Producers load group g + 2 into registers as they finish g + 1.
+constexpr int kTilePitch = 272;  // LDS bytes per staged row: 256 + 16 of skew
+static_assert(pair(neg_units(1) + (14u << 10)) == 0xBC00BC00u, "-1 in FP16");
+static_assert(pair(neg_units(5) + (14u << 10)) == 0xC500C500u, "-5 in FP16");
+static_assert(pair(neg_units(33) + (14u << 10)) == 0xD020D020u, "-33 in FP16");
+
+template <int BM, int BN>
+constexpr size_t tile_lds_bytes() {
+    return (size_t)2 * (BM + BN) * kTilePitch;
+}
+
+// FP16 pair of -wt(q), the integer that turns pair q's slot value v into t:
+// t = v * 2^14 - wt(q) (ternary wt = offset + 1: 1 or 5; binary 2 offset + 1).
+// neg_units(w) is -w * 2^-14; 14 more in the exponent field makes it -w.
+template <int VARIANT>
+constexpr uint32_t tile_bias(int q) {
+    return pair(neg_units(Fmt<VARIANT>::wt(q)) + (14u << 10));
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int VARIANT, int BM, int BN>
+__global__ __launch_bounds__(512) void gemm_tile_kernel(const uint8_t *__restrict__ codes,
+                                                        const uint16_t *__restrict__ scales,
+                                                        const uint16_t *__restrict__ X,
+                                                        float *__restrict__ Y, int M, int N, int K) {
+    using F = Fmt<VARIANT>;
+    constexpr int GB = F::kGroupBytes;
+    constexpr int WM = BM / 2, WN = BN / 2;      // consumer wave tile
+    static_assert(WM % 32 == 0 && WN % 32 == 0, "consumer tiles are 32 x 32 MFMA tiles");
+    // producer work: ternary rows take two threads (16 code bytes each, two
+    // 32-weight chunks), binary rows one (16 bytes, four chunks)
+    constexpr int CPT = VARIANT == TQ_TERNARY ? 2 : 4;   // chunks decoded per thread
+    constexpr int WTHREADS = BN * 4 / CPT;               // producer threads decoding weights
+    constexpr int XTHREADS = BM * 2;                     // producer threads staging activations
+    static_assert(WTHREADS <= 256 && XTHREADS <= 256, "one staging item per producer thread");
+    __shared__ __attribute__((aligned(16))) uint8_t smem[tile_lds_bytes<BM, BN>()];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const bool producer = wave >= 4;
+    const int G = K >> 7;
+    const size_t RB = (size_t)G * GB;
+    const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+
+    if (producer) {
+        const int tid = threadIdx.x - 256;
+        const bool w_role = tid < WTHREADS, x_role = tid < XTHREADS;
+        const int w_row = tid / (4 / CPT), w_part = tid % (4 / CPT);  // 16-byte part of the row's group
+        const int x_row = tid >> 1, x_part = tid & 1;                 // 64-activation half of the row's group
+        const uint8_t *wsrc = codes + (size_t)min(n0 + min(w_row, BN - 1), N - 1) * RB + 16 * w_part;
+        const uint16_t *ssrc = scales + (size_t)min(n0 + min(w_row, BN - 1), N - 1) * G;
+        const uint16_t *xsrc = X + (size_t)min(m0 + min(x_row, BM - 1), M - 1) * K + 64 * x_part;
+        u32x4 wc;          // 16 code bytes
+        uint32_t sbits;    // the row's scale
+        u32x4 xr[2][4];    // 64 activations (two 32-activation chunks)
+        auto load = [&](int g) __attribute__((always_inline)) {
+            wc = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(wsrc + (size_t)g * GB));
+            sbits = ssrc[g];
+#pragma unroll
+            for (int c = 0; c < 2; ++c)
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    xr[c][k] = *reinterpret_cast<const u32x4 *>(xsrc + (size_t)g * 128 + 32 * c + 8 * k);
+        };
+        const Decoder<VARIANT> dec;
+        const uint32_t two14 = vreg(0x74007400u);  // FP16 16384, both halves
+        auto stage = [&](int b) __attribute__((always_inline)) {
+            uint8_t *ws = smem + (size_t)b * (BM + BN) * kTilePitch;
+            uint8_t *xs = ws + (size_t)BN * kTilePitch;
+            if (w_role) {
+                const uint32_t s2 = (sbits & 0xFFFFu) | (sbits << 16);
+#pragma unroll
+                for (int c = 0; c < CPT; ++c) {
+                    uint32_t d[2];
+                    if (VARIANT == TQ_TERNARY) {
+                        d[0] = wc[2 * c];
+                        d[1] = wc[2 * c + 1];
+                    } else {
+                        d[0] = wc[c];
+                        d[1] = 0;
+                    }
+                    uint32_t w[16];
+                    dec(d, w);
+#pragma unroll
+                    for (int qq = 0; qq < 16; ++qq) {
+                        // t = v * 2^14 - wt(q) and t * s: every step exact in FP16
+                        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+                        const h2 v = __builtin_bit_cast(h2, w[qq]);
+                        const h2 t = v * __builtin_bit_cast(h2, two14) +
+                                     __builtin_bit_cast(h2, tile_bias<VARIANT>(qq));
+                        w[qq] = __builtin_bit_cast(uint32_t, t * __builtin_bit_cast(h2, s2));
+                    }
+                    const int chunk = CPT * w_part + c;  // 32-weight chunk of the group
+                    u32x4 *dst = reinterpret_cast<u32x4 *>(ws + (size_t)w_row * kTilePitch + 64 * chunk);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) dst[k] = u32x4{w[4 * k], w[4 * k + 1], w[4 * k + 2], w[4 * k + 3]};
+                }
+            }
+            if (x_role) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    uint32_t xa[16];
+                    permute_x<VARIANT>(xr[c], xa);
+                    u32x4 *dst = reinterpret_cast<u32x4 *>(xs + (size_t)x_row * kTilePitch + 64 * (2 * x_part + c));
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) dst[k] = u32x4{xa[4 * k], xa[4 * k + 1], xa[4 * k + 2], xa[4 * k + 3]};
+                }
+            }
+        };
+        load(0);
+        stage(0);
+        load(min(1, G - 1));
+        __syncthreads();
+        for (int g = 0; g < G; ++g) {
+            // the other buffer was last read before the previous barrier
+            if (g + 1 < G) {
+                stage((g + 1) & 1);
+                load(min(g + 2, G - 1));
+            }
+            __syncthreads();
+        }
+    } else {
+        // v_mfma_f32_32x32x16_f16: lane l supplies A row / B column l % 32 and
+        // the K half l / 32 of each 16-wide slice; D element i of lane l is
+        // row 8 (i / 4) + 4 (l / 32) + i % 4, column l % 32
+        constexpr int UM = WM / 32, UN = WN / 32;
+        const int wm = wave >> 1, wn = wave & 1;
+        const int l32 = lane & 31, h2 = lane >> 5;
+        f32x16 acc[UM][UN];
+#pragma unroll
+        for (int a = 0; a < UM; ++a)
+#pragma unroll
+            for (int b = 0; b < UN; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+        __syncthreads();
+        for (int g = 0; g < G; ++g) {
+            const uint8_t *ws = smem + (size_t)(g & 1) * (BM + BN) * kTilePitch;
+            const uint8_t *xs = ws + (size_t)BN * kTilePitch;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {  // 16-wide K slice of the group
+                half8 av[UM], bv[UN];
+#pragma unroll
+                for (int a = 0; a < UM; ++a)
+                    av[a] = *reinterpret_cast<const half8 *>(
+                        xs + (size_t)(wm * WM + 32 * a + l32) * kTilePitch + 32 * j + 16 * h2);
+#pragma unroll
+                for (int b = 0; b < UN; ++b)
+                    bv[b] = *reinterpret_cast<const half8 *>(
+                        ws + (size_t)(wn * WN + 32 * b + l32) * kTilePitch + 32 * j + 16 * h2);
+#pragma unroll
+                for (int a = 0; a < UM; ++a)
+#pragma unroll
+                    for (int b = 0; b < UN; ++b)
+                        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av[a], bv[b], acc[a][b], 0, 0, 0);
+            }
+            __syncthreads();
+        }
+#pragma unroll
+        for (int a = 0; a < UM; ++a)
+#pragma unroll
+            for (int b = 0; b < UN; ++b)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int m = m0 + wm * WM + 32 * a + 8 * (i / 4) + 4 * h2 + i % 4;
+                    const int n = n0 + wn * WN + 32 * b + l32;
+                    if (m < M && n < N) Y[(size_t)m * N + n] = acc[a][b][i];
+                }
+    }
+}
+
+template <int VARIANT, int BM, int BN>
+hipError_t launch_tile(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
+                       int M, int N, int K, hipStream_t stream) {
+    const dim3 grid((N + BN - 1) / BN, (M + BM - 1) / BM);
+    hipLaunchKernelGGL((gemm_tile_kernel<VARIANT, BM, BN>), grid, dim3(512), 0, stream, codes, scales,
+                       X, Y, M, N, K);
+    return hipGetLastError();
+}
+
 template <int VARIANT, int NT, int MR, int KW, int PC>
 hipError_t launch_stage(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
                         int M, int N, int K, hipStream_t stream) {
@@ -579,6 +776,10 @@ hipError_t launch(const uint8_t *codes, const uint16_t *scales, const uint16_t *
 }
 
 // Configurations measured on the MLP shapes (17408 x 5120 and 5120 x 17408):
+// M >= 128 with at least 128 output tiles of 128 x 128 takes the tiled kernel
+// (M = 128 / 512 on 17408 x 5120: 67 / 189 us against 81 / 213 for the
+// per-group kernel; 5120 x 17408 at M = 512: 204 against 225; with fewer
+// tiles, 5120 x 17408 at M = 256 is 205 against 135),
 // M <= 4 takes the stage-pipelined kernel with four staged activation rows,
 // M <= 8 the same kernel with eight while N <= 65536 (18.0 / 19.5 us at M = 8
 // against 21.4 / 21.0 for the per-group kernel; on the 248320-row LM head it
@@ -591,6 +792,9 @@ template <int VARIANT>
 hipError_t dispatch(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
                     int M, int N, int K, hipStream_t s) {
     const bool tall = N >= 8192;
+    // the tiled kernel needs a grid of about half the CUs to pay off
+    if (M >= 128 && (int64_t)((N + 127) / 128) * ((M + 127) / 128) >= 128)
+        return launch_tile<VARIANT, 128, 128>(codes, scales, X, Y, M, N, K, s);
     if (M <= 4) return launch_stage<VARIANT, 2, 4, 4, 1>(codes, scales, X, Y, M, N, K, s);
     if (M <= 8 && N <= 65536) return launch_stage<VARIANT, 2, 8, 4, 1>(codes, scales, X, Y, M, N, K, s);
     if (M <= 16)

@@ -255,6 +255,22 @@ def test_gemm_ragged(M, N, K, variant):
     assert_tol(Y, Yref, A, "gemm M=%d N=%d K=%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("variant", [TERN, BIN])
+@pytest.mark.parametrize("M,N,K", [(200, 16500, 640), (128, 16384, 128), (300, 8200, 256)])
+def test_gemm_tiled_ragged(M, N, K, variant):
+    """Wide batches on the tiled kernel (at least 128 output tiles of 128 x 128):
+    ragged activation and weight tiles, a single group of K, exact and
+    tolerance cases."""
+    codes, s, X = case(9850 + M + K, N, K, M, variant, exact=True)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, _ = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert np.array_equal(Y.astype(np.float64), Yref)
+    codes, s, X = case(9860 + M + K, N, K, M, variant, exact=False)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, A = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert_tol(Y, Yref, A, "tiled gemm M=%d N=%d K=%d" % (M, N, K))
+
+
 @pytest.mark.parametrize("M", [2, 4, 16])
 @pytest.mark.parametrize("N,K", [synth.GATE_UP, synth.DOWN])
 def test_gemm_binary_full_size_sampled(M, N, K):
