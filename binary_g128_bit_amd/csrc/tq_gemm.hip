@@ -161,6 +161,30 @@ __device__ __forceinline__ f32x4 mfma(half8 a, half8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
+// FP16 pair of -wt(q), the integer that turns pair q's slot value v into t:
+// t = v * 2^14 - wt(q) (ternary wt = offset + 1: 1 or 5; binary 2 offset + 1).
+// neg_units(w) is -w * 2^-14; 14 more in the exponent field makes it -w.
+template <int VARIANT>
+constexpr uint32_t tile_bias(int q) {
+    return pair(neg_units(Fmt<VARIANT>::wt(q)) + (14u << 10));
+}
+static_assert(pair(neg_units(1) + (14u << 10)) == 0xBC00BC00u, "-1 in FP16");
+static_assert(pair(neg_units(5) + (14u << 10)) == 0xC500C500u, "-5 in FP16");
+static_assert(pair(neg_units(33) + (14u << 10)) == 0xD020D020u, "-33 in FP16");
+
+// The decode's 16 slot pairs as exact FP16 s * t (t is ternary or +-1, so
+// s * t is an FP16 value): t = v * 2^14 - wt(q), then t * s, each exact.
+template <int VARIANT>
+__device__ __forceinline__ void exact_st(uint32_t (&w)[16], uint32_t s2, uint32_t two14) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int qq = 0; qq < 16; ++qq) {
+        const h2 t = __builtin_bit_cast(h2, w[qq]) * __builtin_bit_cast(h2, two14) +
+                     __builtin_bit_cast(h2, tile_bias<VARIANT>(qq));
+        w[qq] = __builtin_bit_cast(uint32_t, t * __builtin_bit_cast(h2, s2));
+    }
+}
+
 // Pair q of the lane's 32 activations: low half = activation lo(q), high
 // half = activation lo(q) + kHiOffset (xw holds them as 16 dwords).
 template <int VARIANT>
@@ -578,21 +602,10 @@ __global__ __launch_bounds__(64 * KW) void gemm_stage_kernel(const uint8_t *__re
 // ran one after the other and the kernel was slower than the per-group one).
 // Producers load group g + 2 into registers as they finish g + 1.
 constexpr int kTilePitch = 272;  // LDS bytes per staged row: 256 + 16 of skew
-static_assert(pair(neg_units(1) + (14u << 10)) == 0xBC00BC00u, "-1 in FP16");
-static_assert(pair(neg_units(5) + (14u << 10)) == 0xC500C500u, "-5 in FP16");
-static_assert(pair(neg_units(33) + (14u << 10)) == 0xD020D020u, "-33 in FP16");
 
 template <int BM, int BN>
 constexpr size_t tile_lds_bytes() {
     return (size_t)2 * (BM + BN) * kTilePitch;
-}
-
-// FP16 pair of -wt(q), the integer that turns pair q's slot value v into t:
-// t = v * 2^14 - wt(q) (ternary wt = offset + 1: 1 or 5; binary 2 offset + 1).
-// neg_units(w) is -w * 2^-14; 14 more in the exponent field makes it -w.
-template <int VARIANT>
-constexpr uint32_t tile_bias(int q) {
-    return pair(neg_units(Fmt<VARIANT>::wt(q)) + (14u << 10));
 }
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -660,15 +673,7 @@ __global__ __launch_bounds__(512) void gemm_tile_kernel(const uint8_t *__restric
                     }
                     uint32_t w[16];
                     dec(d, w);
-#pragma unroll
-                    for (int qq = 0; qq < 16; ++qq) {
-                        // t = v * 2^14 - wt(q) and t * s: every step exact in FP16
-                        typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-                        const h2 v = __builtin_bit_cast(h2, w[qq]);
-                        const h2 t = v * __builtin_bit_cast(h2, two14) +
-                                     __builtin_bit_cast(h2, tile_bias<VARIANT>(qq));
-                        w[qq] = __builtin_bit_cast(uint32_t, t * __builtin_bit_cast(h2, s2));
-                    }
+                    exact_st<VARIANT>(w, s2, two14);
                     const int chunk = CPT * w_part + c;  // 32-weight chunk of the group
                     u32x4 *dst = reinterpret_cast<u32x4 *>(ws + (size_t)w_row * kTilePitch + 64 * chunk);
 #pragma unroll
