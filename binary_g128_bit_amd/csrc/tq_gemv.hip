@@ -913,10 +913,11 @@ __device__ __forceinline__ void mcol_dword(uint32_t d, const uint32_t (&xp)[MC][
 }
 
 // Persistent workgroups as in gemv_kernel (one per CU, WAVES waves walking a
-// contiguous range of row blocks, two register sets of codes in ping-pong).
-// A block is RPL * 64/LPR weight rows: lane segment seg takes rows seg,
-// seg + 64/LPR, ...; every activation quad read from LDS serves the RPL rows.
-// Y[m][n] for m < M.
+// contiguous range of row blocks) with the register kernel's pipelined loop:
+// one register set of codes, each chunk refilled with the wave's next block
+// as soon as it is used.  A block is RPL * 64/LPR weight rows: lane segment
+// seg takes rows seg, seg + 64/LPR, ...; every activation quad read from LDS
+// serves the RPL rows.  Y[m][n] for m < M.
 template <int VARIANT, int MC, int LPR, int NU, int RPL, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) void gemm_mcol_kernel(const uint8_t *__restrict__ codes,
                                                                const uint16_t *__restrict__ scales,
@@ -941,11 +942,6 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_mcol_kernel(const uint8_t *__
     const int b_begin = (int)(((long long)blockIdx.x * nblocks) / gridDim.x);
     const int b_end = (int)(((long long)(blockIdx.x + 1) * nblocks) / gridDim.x);
     const Masks km;
-    auto rows_of = [&](int bb, int (&row)[RPL]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) row[r] = min(bb * RB + r * RS + seg, N - 1);
-    };
-
     // 1. activation loads (L2-resident), then the first block's codes
     XU xu[XMAX];
     int xm[XMAX], xu_i[XMAX];
@@ -957,12 +953,28 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_mcol_kernel(const uint8_t *__
         xu[k].load(X + (size_t)min(xm[k], M - 1) * K, min(xu_i[k], nunits - 1));
     }
     __builtin_amdgcn_sched_barrier(0);
-    u32x4 ca[NU][RPL], cb[NU][RPL];
-    uint32_t sa[NU][RPL], sb[NU][RPL];
-    int b = b_begin + wave;
-    int row[RPL];
-    rows_of(min(b, b_end - 1), row);
-    load_block<VARIANT, LPR, NU, RPL, true>(codes, scales, row, j, CPR, G, ca, sa);
+    // one register set: chunk i of the next block is requested as soon as
+    // chunk i of this one is used; every load is clamped into the range, so
+    // the load order (and the compiler's wait before each chunk) never varies
+    const int blast = b_end - 1;
+    const int b0 = b_begin + wave;
+    const int nb = b0 < b_end ? (b_end - b0 + WAVES - 1) / WAVES : 0;
+    int ccol[NU];
+#pragma unroll
+    for (int i = 0; i < NU; ++i) ccol[i] = min(j + i * LPR, CPR - 1);
+    u32x4 ca[NU][RPL];
+    uint32_t sa[NU][RPL];
+    auto load_chunk = [&](int bb, int i) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            const int row = min(min(bb, blast) * RB + r * RS + seg, N - 1);
+            sa[i][r] = scales[(size_t)row * G + ccol[i] / MF::CPG];
+            ca[i][r] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(codes + (size_t)row * CPR * 16) + ccol[i]);
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < NU; ++i) load_chunk(b0, i);
     __builtin_amdgcn_sched_barrier(0);
 
     // 2. pairs and seeds into LDS (threads past the last unit redo it; only
@@ -972,8 +984,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_mcol_kernel(const uint8_t *__
         mcol_store<VARIANT, CAP>(xu[k], xq, xseed, xm[k], xu_i[k], xu_i[k] < nunits && xm[k] < M);
     __syncthreads();
 
-    auto block = [&](const u32x4 (&c)[NU][RPL], const uint32_t (&sv)[NU][RPL], int bb)
-                     __attribute__((always_inline)) {
+    auto block = [&](auto refill, int bb, int bn) __attribute__((always_inline)) {
         // the activation reads are the same for every block: an opaque base
         // keeps them inside the loop (hoisted, they would pin NU * 4 * MC * QPU
         // quads in registers across it)
@@ -1011,7 +1022,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_mcol_kernel(const uint8_t *__
                     }
 #pragma unroll
                 for (int r = 0; r < RPL; ++r) {
-                    mcol_dword<VARIANT, MC>(c[i][r][dw], xp, a[r], km);
+                    mcol_dword<VARIANT, MC>(ca[i][r][dw], xp, a[r], km);
                     // one dword's slot values and pairs live at a time: left
                     // free, the compiler sinks the later rows' dot products to
                     // the end of the block and keeps every decoded value for them
@@ -1021,10 +1032,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_mcol_kernel(const uint8_t *__
             }
 #pragma unroll
             for (int r = 0; r < RPL; ++r) {
-                const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)sv[i][r]);
+                const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)sa[i][r]);
 #pragma unroll
                 for (int m = 0; m < MC; ++m) acc[r][m] = __builtin_fmaf(sc, a[r][m], acc[r][m]);
             }
+            if constexpr (decltype(refill)::value) load_chunk(bn, i);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -1038,22 +1050,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemm_mcol_kernel(const uint8_t *__
         }
     };
 
-    // 3. ping-pong over this wave's blocks
-    for (; b < b_end; b += 2 * WAVES) {
-        const int b2 = b + WAVES;
-        if (b2 < b_end) {
-            rows_of(b2, row);
-            load_block<VARIANT, LPR, NU, RPL, true>(codes, scales, row, j, CPR, G, cb, sb);
-        }
-        block(ca, sa, b);
-        if (b2 >= b_end) break;
-        const int b3 = b2 + WAVES;
-        if (b3 < b_end) {
-            rows_of(b3, row);
-            load_block<VARIANT, LPR, NU, RPL, true>(codes, scales, row, j, CPR, G, ca, sa);
-        }
-        block(cb, sb, b2);
-    }
+    // 3. this wave's blocks, each refilling the register set for the next
+    using Refill = std::integral_constant<bool, true>;
+    using Last = std::integral_constant<bool, false>;
+    int k = 0;
+    for (; k + 1 < nb; ++k) block(Refill{}, b0 + k * WAVES, b0 + (k + 1) * WAVES);
+    if (k < nb) block(Last{}, b0 + k * WAVES, 0);
 }
 
 template <int VARIANT, int MC, int LPR, int NU, int RPL>
