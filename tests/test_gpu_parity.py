@@ -271,6 +271,27 @@ def test_gemm_tiled_ragged(M, N, K, variant):
     assert_tol(Y, Yref, A, "tiled gemm M=%d N=%d K=%d" % (M, N, K))
 
 
+def _random_gemm_shapes():
+    """Seeded shapes over every GEMM path: two-row VALU, staged, per-group and
+    tiled MFMA kernels, with ragged M, N and K."""
+    g = np.random.default_rng(4242)
+    out = []
+    for lo, hi, nlo, nhi, kmax in ((2, 3, 1, 3000, 160), (3, 9, 1, 3000, 100), (9, 128, 1, 2000, 60),
+                                   (128, 400, 8200, 20000, 12)):
+        for _ in range(3):
+            out.append((int(g.integers(lo, hi)), int(g.integers(nlo, nhi)), 128 * int(g.integers(1, kmax))))
+    return out
+
+
+@pytest.mark.parametrize("variant", [TERN, BIN])
+@pytest.mark.parametrize("M,N,K", _random_gemm_shapes())
+def test_gemm_random_shapes(M, N, K, variant):
+    codes, s, X = case(9990 + M + N + K, N, K, M, variant, exact=False)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, A = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert_tol(Y, Yref, A, "random gemm M=%d N=%d K=%d" % (M, N, K))
+
+
 @pytest.mark.parametrize("M", [2, 4, 16])
 @pytest.mark.parametrize("N,K", [synth.GATE_UP, synth.DOWN])
 def test_gemm_binary_full_size_sampled(M, N, K):
