@@ -43,8 +43,11 @@
 // which streams from HBM at well under half the rate.  Two kernels share this
 // structure: gemm_kernel loads each group's activations (small, L2-resident)
 // straight into registers one group ahead and holds up to 64 activation rows
-// per wave; gemm_stage_kernel (M <= 4) issues all loads of a stage in one
-// batch and stages the activations in LDS (see its comment).
+// per wave; gemm_stage_kernel (M <= 8) issues all loads of a stage in one
+// batch and stages the activations in LDS (see its comment).  For wide
+// batches gemm_tile_kernel instead decodes each weight once per workgroup into
+// LDS as exact FP16 s * t and runs 32x32x16 MFMAs across all groups (see its
+// comment).  Two-row batches take a VALU kernel in tq_gemv.hip.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
