@@ -505,13 +505,28 @@ __global__ __launch_bounds__(64 * WAVES) void gemv5x_kernel(const uint8_t *__res
     for (int i = 0; i < NU; ++i) load_chunk(b0, i, ca, sa);
     __builtin_amdgcn_sched_barrier(0);
 
-    // 2. the table (every lane's copy) and x into LDS
-    for (int e = threadIdx.x; e < 256 * 64; e += THREADS)
-        reinterpret_cast<uint32_t *>(lut)[e] = slot_codes((uint32_t)(e >> 6));
+    // 2. the 256 table entries, once each, staged where the chunk slots will
+    // go (at least 288 dwords, ahead of x), and x into LDS; then every wave
+    // copies its 256 / WAVES entries into all 64 lane copies (one broadcast
+    // read and one conflict-free write per copy, no arithmetic)
+    static_assert(256 % WAVES == 0 && LPR * kC5SlotDw >= 256, "table staging");
+    if (threadIdx.x < 256) xs[threadIdx.x] = slot_codes(threadIdx.x);
 #pragma unroll
     for (int k = 0; k < XV; ++k) {
         const int v = threadIdx.x + k * THREADS;
         if (v * 8 < K) reinterpret_cast<u32x4 *>(xn)[v] = xv[k];
+    }
+    __syncthreads();
+    {
+        constexpr int PER = 256 / WAVES;
+        const int v0 = wave * PER;
+        uint32_t *dst = reinterpret_cast<uint32_t *>(lut) + v0 * 64 + lane;
+#pragma unroll
+        for (int k = 0; k < PER; k += 4) {
+            const u32x4 e = reinterpret_cast<const u32x4 *>(xs + v0)[k / 4];
+#pragma unroll
+            for (int w = 0; w < 4; ++w) dst[(k + w) * 64] = e[w];
+        }
     }
     __syncthreads();
 
