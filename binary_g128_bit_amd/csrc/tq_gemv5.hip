@@ -532,28 +532,34 @@ __global__ __launch_bounds__(64 * WAVES) void gemv5x_kernel(const uint8_t *__res
 
     // 3. chunk slots: eight threads per chunk; thread q < 6 builds the five
     // pairs of byte pair q, thread 6 the three pairs of the 13th byte; the
-    // chunk constant is their reduced weighted sum
-    for (int t = threadIdx.x; t < CAP * 8; t += THREADS) {
+    // chunk constant is their reduced weighted sum.  Without branches: reads
+    // are clamped into x and masked, and the writes that have no pair (thread
+    // 6's last two, all of thread 7's) store zeros into the slot's two pad
+    // dwords
+#pragma unroll
+    for (int t0 = 0; t0 < CAP * 8; t0 += THREADS) {
+        const int t = t0 + (int)threadIdx.x;
+        if (CAP * 8 % THREADS != 0 && t >= CAP * 8) break;
         const int h = t >> 3, q = t & 7;
-        const int g = h >> 1, base = 65 * (h & 1);
+        const int g = min(h >> 1, G - 1), base = 65 * (h & 1);
         const bool real = h < CPR;
         const int np = q < 6 ? 5 : (q == 6 ? 3 : 0);
         float z = 0.0f;
-        uint32_t pr[5];
 #pragma unroll
         for (int i = 0; i < 5; ++i) {
             // trits of the pair within the group; >= 128 means none
             const int tl = base + (q < 6 ? 10 * q + i : 60 + i);
             const int th = q < 6 ? base + 10 * q + 5 + i : (i < 2 ? base + 63 + i : 128);
             const bool on = real && i < np;
-            const uint32_t lo = (on && tl < 128) ? xn[g * 128 + tl] : 0u;
-            const uint32_t hi = (on && th < 128) ? xn[g * 128 + th] : 0u;
-            pr[i] = lo | (hi << 16);
-            z = dot2(pr[i], c5_zweight(i), z);
+            const uint32_t lv = xn[g * 128 + min(tl, 127)];
+            const uint32_t hv = xn[g * 128 + min(th, 127)];
+            const uint32_t lo = (on && tl < 128) ? lv : 0u;
+            const uint32_t hi = (on && th < 128) ? hv : 0u;
+            const uint32_t pr = lo | (hi << 16);
+            z = dot2(pr, c5_zweight(i), z);
+            const int d = q < 6 ? 5 * q + i : (q == 6 && i < 3 ? 30 + i : kC5Pairs + 1 + (i & 1));
+            xs[h * kC5SlotDw + d] = pr;
         }
-#pragma unroll
-        for (int i = 0; i < 5; ++i)
-            if (i < np) xs[h * kC5SlotDw + (q < 6 ? 5 * q : 30) + i] = pr[i];
         z = seg_sum<8>(z) * -6.103515625e-05f;
         if (q == 7) xs[h * kC5SlotDw + kC5Pairs] = __builtin_bit_cast(uint32_t, z);
     }
