@@ -509,7 +509,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv5x_kernel(const uint8_t *__res
     // go (at least 288 dwords, ahead of x), and x into LDS; then every wave
     // copies its 256 / WAVES entries into all 64 lane copies (one broadcast
     // read and one conflict-free write per copy, no arithmetic)
-    static_assert(256 % WAVES == 0 && LPR * kC5SlotDw >= 256, "table staging");
+    static_assert(THREADS >= 256 && 256 % WAVES == 0 && LPR * kC5SlotDw >= 256, "table staging");
     if (threadIdx.x < 256) xs[threadIdx.x] = slot_codes(threadIdx.x);
 #pragma unroll
     for (int k = 0; k < XV; ++k) {
