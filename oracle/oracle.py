@@ -149,8 +149,9 @@ def gemm(codes, scales, X, N, K, variant=TERNARY, group=128, threads=1, lib=None
     M = X.shape[0]
     if X.shape[1] != K:
         raise ValueError("X has %d columns, expected K=%d" % (X.shape[1], K))
-    Y = np.empty((M, N), dtype=np.float64)
-    A = np.empty((M, N), dtype=np.float64)
+    # NaN-filled, so an output the C code never writes cannot pass for a result
+    Y = np.full((M, N), np.nan, dtype=np.float64)
+    A = np.full((M, N), np.nan, dtype=np.float64)
     rc = lib.oracle_gemm(_ptr(codes), _ptr(s), _ptr(X), M, N, K, group, variant,
                          _ptr(Y), _ptr(A), int(threads))
     if rc:
@@ -193,8 +194,8 @@ def affine_gemm(codes, scales, biases, X, N, K, group=128, threads=1, lib=None):
     if X.ndim == 1:
         X = X.reshape(1, -1)
     M = X.shape[0]
-    Y = np.empty((M, N), dtype=np.float64)
-    A = np.empty((M, N), dtype=np.float64)
+    Y = np.full((M, N), np.nan, dtype=np.float64)
+    A = np.full((M, N), np.nan, dtype=np.float64)
     rc = lib.oracle_affine_gemm(_ptr(codes), _ptr(s), _ptr(b), _ptr(X), M, N, K, group,
                                 _ptr(Y), _ptr(A), int(threads))
     if rc:

@@ -188,10 +188,17 @@ def check_worked_gemv(lib):
 
 
 # ------------------------------------------------------------ the product
+def _thread_counts():
+    """Row-split widths the oracle is pinned at: one thread, an odd count that
+    leaves a remainder on the test shapes, and every core this process may
+    use (what the GPU parity tests run the oracle with)."""
+    return sorted({1, 3, max(2, oracle.default_threads())})
+
+
 def check_bruteforce_numpy(lib):
     g = synth.rng(11)
     for variant in (oracle.TERNARY, oracle.BINARY, oracle.TERNARY5):
-        for N, K, M in ((1, 128, 1), (3, 256, 2), (8, 384, 4), (5, 128, 3)):
+        for N, K, M in ((1, 128, 1), (3, 256, 2), (8, 384, 4), (5, 128, 3), (37, 256, 2)):
             t = synth.trits(g, N, K, variant)
             s = synth.scales(g, N, K)
             s[0, 0] = -s[0, 0]                       # negative scale
@@ -199,26 +206,32 @@ def check_bruteforce_numpy(lib):
                 s[-1, -1] = np.float16(2.0 ** -20)   # subnormal scale
             X = synth.activations(g, M, K)
             X[0, 0] = np.float16(2.0 ** -22)         # subnormal activation
-            Y, _ = oracle.gemm(oracle.pack(t, variant, lib=lib), s, X, N, K, variant, lib=lib)
             ref = X.astype(np.float64) @ _dense(t, s).T
-            err = np.abs(Y - ref)
             scale = np.abs(X.astype(np.float64)) @ np.abs(_dense(t, s)).T
-            assert np.all(err <= 1e-12 * scale + 1e-300), (variant, N, K, M, err.max())
+            for threads in _thread_counts():
+                Y, A = oracle.gemm(oracle.pack(t, variant, lib=lib), s, X, N, K, variant,
+                                   threads=threads, lib=lib)
+                err = np.abs(Y - ref)
+                assert np.all(err <= 1e-12 * scale + 1e-300), (variant, N, K, M, threads, err.max())
+                assert np.allclose(A, scale, rtol=1e-12, atol=0), (variant, N, K, M, threads)
 
 
 def check_exact_integer(lib):
     g = synth.rng(13)
     for variant in (oracle.TERNARY, oracle.BINARY, oracle.TERNARY5):
-        N, K, M = 4, 384, 3
-        t = synth.trits(g, N, K, variant)
-        s = np.ones((N, K // 128), dtype=np.float16)
-        X = synth.int_activations(g, M, K)
-        Y, _ = oracle.gemm(oracle.pack(t, variant, lib=lib), s, X, N, K, variant, lib=lib)
-        xi = X.astype(np.int64)
-        for m in range(M):
-            for n in range(N):
-                exact = sum(int(t[n, k]) * int(xi[m, k]) for k in range(K))
-                assert Y[m, n] == exact, (variant, m, n, Y[m, n], exact)
+        for N, K, M in ((4, 384, 3), (29, 256, 2)):
+            t = synth.trits(g, N, K, variant)
+            s = np.ones((N, K // 128), dtype=np.float16)
+            X = synth.int_activations(g, M, K)
+            xi = X.astype(np.int64)
+            exact = [[sum(int(t[n, k]) * int(xi[m, k]) for k in range(K)) for n in range(N)]
+                     for m in range(M)]
+            for threads in _thread_counts():
+                Y, _ = oracle.gemm(oracle.pack(t, variant, lib=lib), s, X, N, K, variant,
+                                   threads=threads, lib=lib)
+                for m in range(M):
+                    for n in range(N):
+                        assert Y[m, n] == exact[m][n], (variant, threads, m, n, Y[m, n], exact[m][n])
 
 
 def check_special_cases(lib):
@@ -359,13 +372,23 @@ def check_affine(lib):
     b[2, 0] = np.float16(2.0 ** -21)
     X = synth.activations(g, M, K)
     c = oracle.pack(qr, oracle.AFFINE2, lib=lib)
-    Y, A = oracle.affine_gemm(c, s, b, X, N, K, lib=lib)
     W = _affine_dense(qr, s, b)
     ref = X.astype(np.float64) @ W.T
-    assert np.all(np.abs(Y - ref) <= 1e-12 * A), np.abs(Y - ref).max()
     refA = (np.abs(X.astype(np.float64)) @ (np.abs(np.repeat(s.astype(np.float64), 128, 1)) * qr).T
             + np.abs(X.astype(np.float64)) @ np.abs(np.repeat(b.astype(np.float64), 128, 1)).T)
-    assert np.allclose(A, refA, rtol=1e-12, atol=0)
+    for threads in _thread_counts():
+        Y, A = oracle.affine_gemm(c, s, b, X, N, K, threads=threads, lib=lib)
+        assert np.all(np.abs(Y - ref) <= 1e-12 * A), (threads, np.abs(Y - ref).max())
+        assert np.allclose(A, refA, rtol=1e-12, atol=0), threads
+    # a row count that leaves a remainder on every split
+    N2 = 41
+    q2 = g.integers(0, 4, size=(N2, K)).astype(np.int8)
+    s2, b2 = synth.scales(g, N2, K), -synth.scales(g, N2, K)
+    c2 = oracle.pack(q2, oracle.AFFINE2, lib=lib)
+    ref2 = X.astype(np.float64) @ _affine_dense(q2, s2, b2).T
+    for threads in _thread_counts():
+        Y2, A2 = oracle.affine_gemm(c2, s2, b2, X, N2, K, threads=threads, lib=lib)
+        assert np.all(np.abs(Y2 - ref2) <= 1e-12 * A2), (threads, np.abs(Y2 - ref2).max())
     # one-hot x: y = s * q_k + b exactly
     for k in (0, 5, 127, 128, 300, 383):
         x = np.zeros(K, np.float16)

@@ -62,6 +62,18 @@ MUTANTS = [
                             "((double)kn[j] - 8.0) * oracle_half_to_double(kd[j / 16 % 8]);")]),
     ("attn_v_scale", [("oracle_half_to_double(vs[(kvh * T + t) * 8 + j / 32]);",
                        "oracle_half_to_double(vs[(kvh * T + t) * 8]);")]),
+    # a hand-made row split that drops the remainder rows when the thread
+    # count does not divide N (single-threaded runs are unaffected)
+    ("omp_split_drops_rows", [("#include <math.h>", "#include <math.h>\n#include <omp.h>"),
+                              ("#pragma omp for schedule(static)\n        for (int64_t n = 0; n < N; n++) {\n            if (!t) continue;",
+                               "for (int64_t n = omp_get_thread_num() * (N / omp_get_num_threads()); "
+                               "n < (omp_get_thread_num() + 1) * (N / omp_get_num_threads()); n++) {\n"
+                               "            if (!t) continue;")]),
+    ("omp_split_drops_rows_affine", [("#include <math.h>", "#include <math.h>\n#include <omp.h>"),
+                                     ("#pragma omp for schedule(static)\n        for (int64_t n = 0; n < N; n++) {\n            if (!q) continue;",
+                                      "for (int64_t n = omp_get_thread_num() * (N / omp_get_num_threads()); "
+                                      "n < (omp_get_thread_num() + 1) * (N / omp_get_num_threads()); n++) {\n"
+                                      "            if (!q) continue;")]),
     ("t5_code_map", [("t[n * K + 128 * g + 5 * b + i] = (int8_t)(c - 1);",
                       "t[n * K + 128 * g + 5 * b + i] = (int8_t)(1 - c);"),
                      ("value += (t[n * K + 128 * g + 5 * b + i] + 1) * power;",
