@@ -30,7 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 # every symbol include/tq.h declares
 EXPORTS = ("tq_codes_bytes", "tq_scales_count", "tq_pack", "tq_unpack", "tq_gemv", "tq_gemm",
            "tq_embed", "tq_gemv_affine", "tq_kv_bytes", "tq_kv_append", "tq_attn_workspace_bytes",
-           "tq_attn_decode", "tq_last_error", "tq_last_error_index", "tq_version")
+           "tq_attn_decode", "tq_stream_read", "tq_last_error", "tq_last_error_index", "tq_version")
 
 
 class TQError(RuntimeError):
@@ -80,6 +80,8 @@ def lib():
     L.tq_attn_workspace_bytes.restype = ctypes.c_size_t
     L.tq_attn_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, ctypes.c_size_t, vp]
     L.tq_attn_decode.restype = i32
+    L.tq_stream_read.argtypes = [vp, ctypes.c_size_t, vp, i32, vp]
+    L.tq_stream_read.restype = i32
     L.tq_last_error.argtypes = []
     L.tq_last_error.restype = ctypes.c_char_p
     L.tq_last_error_index.argtypes = []
@@ -168,14 +170,21 @@ def _shape_checks(codes, scales, K, variant):
     return N
 
 
+def _out_check(out, name, numel):
+    if out.numel() != numel:
+        raise ValueError("%s holds %d elements, %d needed" % (name, out.numel(), numel))
+
+
 def tq_gemv(codes, scales, x, y=None, variant=TQ_TERNARY, group=GROUP, stream=None):
     """y[N] = W x on the current stream.  codes uint8, scales float16 [N][K/128],
     x float16 [K], y float32 [N] (allocated if None)."""
     import torch
     K = x.shape[-1]
+    _out_check(x, "x", K)
     N = _shape_checks(codes, scales, K, variant)
     if y is None:
         y = torch.empty(N, dtype=torch.float32, device=x.device)
+    _out_check(y, "y", N)
     half = (torch.float16, torch.int16)
     _check(lib().tq_gemv(_dev(codes, "codes", (torch.uint8,)), _dev(scales, "scales", half),
                          _dev(x, "x", half), _dev(y, "y", (torch.float32,)), N, K, group, variant,
@@ -190,6 +199,8 @@ def tq_gemm(codes, scales, X, Y=None, variant=TQ_TERNARY, group=GROUP, stream=No
     N = _shape_checks(codes, scales, K, variant)
     if Y is None:
         Y = torch.empty((M, N), dtype=torch.float32, device=X.device)
+    if tuple(Y.shape) != (M, N):
+        raise ValueError("Y has shape %s, (%d, %d) needed" % (tuple(Y.shape), M, N))
     half = (torch.float16, torch.int16)
     _check(lib().tq_gemm(_dev(codes, "codes", (torch.uint8,)), _dev(scales, "scales", half),
                          _dev(X, "X", half), _dev(Y, "Y", (torch.float32,)), M, N, K, group,
@@ -221,16 +232,33 @@ def tq_gemv_affine(codes, scales, biases, x, y=None, group=GROUP, stream=None):
     stream.  codes uint8 [N][K/4], scales / biases float16 [N][K/128]."""
     import torch
     K = x.shape[-1]
+    _out_check(x, "x", K)
     N = _shape_checks(codes, scales, K, TQ_AFFINE2)
     if tuple(biases.shape) != tuple(scales.shape):
         raise ValueError("biases must have the shape of scales")
     if y is None:
         y = torch.empty(N, dtype=torch.float32, device=x.device)
+    _out_check(y, "y", N)
     half = (torch.float16, torch.int16)
     _check(lib().tq_gemv_affine(_dev(codes, "codes", (torch.uint8,)), _dev(scales, "scales", half),
                                 _dev(biases, "biases", half), _dev(x, "x", half),
                                 _dev(y, "y", (torch.float32,)), N, K, group, _stream(stream, x)))
     return y
+
+
+# ------------------------------------------------------- measurement aid
+def tq_stream_read(buf, sink, blocks_per_cu=1, stream=None):
+    """Plain streaming read of the whole device tensor `buf` (a multiple of 16
+    bytes): the bandwidth ceiling for a launch of the same size.  `sink` is a
+    device tensor of at least 4 bytes."""
+    import torch
+    if sink.numel() * sink.element_size() < 4:
+        raise ValueError("sink needs 4 bytes")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().tq_stream_read(_dev(buf, "buf", (torch.uint8, torch.int32, torch.int16, torch.float16,
+                                                  torch.float32)),
+                                nbytes, _dev(sink, "sink", (torch.int32, torch.uint8, torch.float32)),
+                                blocks_per_cu, _stream(stream, buf)))
 
 
 # ------------------------------------------------------- 4-bit KV cache
@@ -242,6 +270,16 @@ def tq_attn_workspace_bytes(T, n_q, n_kv):
     return lib().tq_attn_workspace_bytes(T, n_q, n_kv)
 
 
+def _cache_checks(n_kv, t_cap, kc, ks, vc, vs):
+    """Each cache array must hold exactly tq_kv_bytes(n_kv, t_cap, part) bytes."""
+    for arr, part, name in ((kc, TQ_KV_K_CODES, "kc"), (ks, TQ_KV_K_SCALES, "ks"),
+                            (vc, TQ_KV_V_CODES, "vc"), (vs, TQ_KV_V_SCALES, "vs")):
+        need = tq_kv_bytes(n_kv, t_cap, part)
+        if need and arr.numel() * arr.element_size() != need:  # 0: the C call reports the shape
+            raise ValueError("%s holds %d bytes, %d needed" % (
+                name, arr.numel() * arr.element_size(), need))
+
+
 def tq_kv_append(k, v, pos, n_kv, t_cap, kc, ks, vc, vs, stream=None):
     """Quantize k, v (float16 [n_tok][n_kv][256]) into cache positions
     [pos, pos + n_tok).  kc / vc uint8 and ks / vs float16 (or int16) device
@@ -250,11 +288,7 @@ def tq_kv_append(k, v, pos, n_kv, t_cap, kc, ks, vc, vs, stream=None):
     if k.shape != v.shape or k.dim() != 3 or k.shape[1] != n_kv or k.shape[2] != 256:
         raise ValueError("k and v must be [n_tok][n_kv][256]")
     half = (torch.float16, torch.int16)
-    for arr, part, name in ((kc, TQ_KV_K_CODES, "kc"), (ks, TQ_KV_K_SCALES, "ks"),
-                            (vc, TQ_KV_V_CODES, "vc"), (vs, TQ_KV_V_SCALES, "vs")):
-        if arr.numel() * arr.element_size() != tq_kv_bytes(n_kv, t_cap, part):
-            raise ValueError("%s holds %d bytes, %d needed" % (
-                name, arr.numel() * arr.element_size(), tq_kv_bytes(n_kv, t_cap, part)))
+    _cache_checks(n_kv, t_cap, kc, ks, vc, vs)
     _check(lib().tq_kv_append(_dev(k, "k", half), _dev(v, "v", half), k.shape[0], pos, n_kv, t_cap,
                               _dev(kc, "kc", (torch.uint8,)), _dev(ks, "ks", half),
                               _dev(vc, "vc", (torch.uint8,)), _dev(vs, "vs", half), _stream(stream, k)))
@@ -265,9 +299,13 @@ def tq_attn_decode(q, kc, ks, vc, vs, T, n_kv, t_cap, workspace, out=None, strea
     workspace: float32 device array of tq_attn_workspace_bytes(T, n_q, n_kv)
     bytes or more.  Returns out float32 [n_q][256]."""
     import torch
+    if q.dim() != 2 or q.shape[1] != 256:
+        raise ValueError("q must be [n_q][256], got %s" % (tuple(q.shape),))
     n_q = q.shape[0]
     if out is None:
         out = torch.empty(n_q, 256, dtype=torch.float32, device=q.device)
+    _out_check(out, "out", n_q * 256)
+    _cache_checks(n_kv, t_cap, kc, ks, vc, vs)
     half = (torch.float16, torch.int16)
     _check(lib().tq_attn_decode(_dev(q, "q", half), _dev(kc, "kc", (torch.uint8,)), _dev(ks, "ks", half),
                                 _dev(vc, "vc", (torch.uint8,)), _dev(vs, "vs", half), T, n_q, n_kv,

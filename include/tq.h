@@ -91,21 +91,35 @@ extern "C" {
 
 /* Size of the packed code array: N*K/4 bytes (ternary), N*K/8 (binary) or
  * N * roundup(26*K/128, 16) (five-trit bytes).  Returns 0 for an invalid
- * shape or variant. */
+ * shape or variant.  Passage: each trit sits in a 2-bit slot (aitrends.kr,
+ * "Ternary-Bonsai-27B-mlx-2bit", "Technical features"); the 1-bit build keeps
+ * one bit per weight (thakicloud.github.io, "Bonsai 27B: ternary and 1-bit
+ * quantization", "How the compression works", whose bits-per-weight figures
+ * 1.71 and 1.125 include the 16-bit scale of every 128 weights). */
 size_t tq_codes_bytes(int64_t N, int64_t K, int32_t variant);
 
-/* Number of FP16 scales: N*K/group.  Returns 0 for an invalid shape/group. */
+/* Number of FP16 scales: N*K/group, one per 128 weights of a row along K
+ * (thakicloud.github.io, "Bonsai 27B: ternary and 1-bit quantization", "How
+ * the compression works": one FP16 scale shared by each group of 128
+ * weights).  Returns 0 for an invalid shape/group. */
 size_t tq_scales_count(int64_t N, int64_t K, int32_t group);
 
 /* Host -> host.  Pack t (int8 [N][K], row-major) into `codes`
  * (tq_codes_bytes(N,K,variant) bytes, fully overwritten).  Scales are not
- * touched: they pass through unchanged.  A value outside the variant's set
- * returns TQ_ERR_VALUE; tq_last_error_index() gives its flat index n*K+k and
- * `codes` is left in an unspecified state. */
+ * touched: they pass through unchanged.  The value sets are the pages'
+ * ternary {-1, 0, +1} and binary {-1, +1} (thakicloud.github.io, "Bonsai 27B:
+ * ternary and 1-bit quantization", "How the compression works"), stored as
+ * 2-bit slots (aitrends.kr, "Ternary-Bonsai-27B-mlx-2bit", "Technical
+ * features"); the code map and bit order are this header's stated layout.
+ * Arguments: t host, N*K bytes; codes host, caller-owned.  A value outside
+ * the variant's set returns TQ_ERR_VALUE; tq_last_error_index() gives its
+ * flat index n*K+k and `codes` is left in an unspecified state.  NULL
+ * pointers return TQ_ERR_NULL, bad shapes TQ_ERR_SHAPE / TQ_ERR_GROUP. */
 int32_t tq_pack(const int8_t *t, int64_t N, int64_t K, int32_t group,
                 int32_t variant, uint8_t *codes);
 
-/* Host -> host.  Inverse of tq_pack: writes t (int8 [N][K]).  A ternary
+/* Host -> host.  Inverse of tq_pack: writes t (int8 [N][K], caller-owned)
+ * from the slots of the layout above (passages as tq_pack).  A ternary
  * code 3 returns TQ_ERR_CODE; tq_last_error_index() gives the flat weight
  * index of the first such slot.  TQ_TERNARY5: a byte >= 243, or a last byte
  * of a group >= 27, returns TQ_ERR_CODE with the flat index of the byte's
@@ -114,7 +128,13 @@ int32_t tq_unpack(const uint8_t *codes, int64_t N, int64_t K, int32_t group,
                   int32_t variant, int8_t *t);
 
 /* Device.  y[n] = sum_g s[n][g] * sum_{j<128} t[n][128g+j] * x[128g+j],
- * accumulated in fp32 (batch-1 decode GEMV).
+ * accumulated in fp32 (batch-1 decode GEMV).  Passage: w_i = s_g * t_i with
+ * one FP16 scale per 128 weights (thakicloud.github.io, "Bonsai 27B: ternary
+ * and 1-bit quantization", "How the compression works"), the packed slots
+ * read directly and the scale applied inside the matmul (aitrends.kr,
+ * "Ternary-Bonsai-27B-mlx-2bit", "Technical features"); decoding one token
+ * is bound by memory bandwidth (thakicloud.github.io, same page,
+ * "Throughput and speculative decoding").
  *   codes  : device, tq_codes_bytes(N,K,variant) bytes, 16-byte aligned
  *   scales : device, uint16 [N][K/128] (fp16 bits), 2-byte aligned
  *   x      : device, uint16 [K] (fp16 bits), 16-byte aligned
@@ -126,7 +146,11 @@ int32_t tq_gemv(const uint8_t *codes, const uint16_t *scales, const uint16_t *x,
                 void *stream);
 
 /* Device.  Y[m][n] = sum_g s[n][g] * sum_j t[n][128g+j] * X[m][128g+j]
- * for m < M (small-batch GEMM: speculative-verify and prefill-chunk widths).
+ * for m < M (small-batch GEMM: speculative-verify and prefill-chunk widths:
+ * thakicloud.github.io, "Bonsai 27B: ternary and 1-bit quantization",
+ * "Throughput and speculative decoding", which verifies k = 4 drafted
+ * tokens at once and measures 512-token prefill; the product is the one of
+ * tq_gemv for every row of X).
  * X is uint16 [M][K] (16-byte aligned), Y is float [M][N]; other arguments as
  * tq_gemv.  M == 1 is the GEMV.  Limits: 1 <= M <= 65536, N and K as tq_gemv. */
 int32_t tq_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
@@ -217,6 +241,16 @@ int32_t tq_attn_decode(const uint16_t *q, const uint8_t *kc, const uint16_t *ks,
                        const uint8_t *vc, const uint16_t *vs, int64_t T, int64_t n_q,
                        int64_t n_kv, int64_t t_cap, float *out, void *workspace,
                        size_t workspace_bytes, void *stream);
+
+/* Measurement aid, not part of the matmul: a plain streaming read of `bytes`
+ * (a positive multiple of 16) of the device buffer `buf` (16-byte aligned),
+ * each 16-byte unit loaded once, on `blocks_per_cu` (1..8) workgroups of 512
+ * threads per compute unit.  It gives the ceiling that a bandwidth-bound
+ * launch reading as many bytes is measured against.  `sink`: 4 bytes of
+ * device memory the kernel may write (in practice never).  Errors:
+ * TQ_ERR_NULL, TQ_ERR_SHAPE, TQ_ERR_ALIGN, TQ_ERR_HIP. */
+int32_t tq_stream_read(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks_per_cu,
+                       void *stream);
 
 /* Text of the calling thread's last error ("" if none). */
 const char *tq_last_error(void);

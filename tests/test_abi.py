@@ -197,3 +197,55 @@ def test_unpack_rejects_code3_with_index():
     assert e.value.status == 6
     assert e.value.index == 2 * 256 + 10 * 4 + 3
     assert "code 3" in str(e.value)
+
+
+def _cpu_problem(N=8, K=256):
+    import torch
+    codes = torch.zeros(tq.tq_codes_bytes(N, K, tq.TQ_TERNARY), dtype=torch.uint8)
+    scales = torch.zeros(N, K // 128, dtype=torch.float16)
+    return codes, scales
+
+
+def test_binding_checks_output_sizes_before_the_call():
+    """Wrong-sized outputs and activations are refused in Python, before any
+    pointer reaches the library (a short y would be written past its end on
+    the device).  CPU tensors pass the size checks and then fail the
+    device-tensor check, so no GPU is touched here."""
+    import torch
+    N, K = 8, 256
+    codes, scales = _cpu_problem(N, K)
+    x = torch.zeros(K, dtype=torch.float16)
+    with pytest.raises(ValueError, match="y holds 7"):
+        tq.tq_gemv(codes, scales, x, torch.zeros(N - 1))
+    with pytest.raises(ValueError, match="device tensor"):
+        tq.tq_gemv(codes, scales, x, torch.zeros(N))
+    with pytest.raises(ValueError, match="x holds"):
+        tq.tq_gemv(codes, scales, torch.zeros(2, K, dtype=torch.float16), torch.zeros(N))
+    X = torch.zeros(4, K, dtype=torch.float16)
+    with pytest.raises(ValueError, match="Y has shape"):
+        tq.tq_gemm(codes, scales, X, torch.zeros(4, N - 1))
+    with pytest.raises(ValueError, match="Y has shape"):
+        tq.tq_gemm(codes, scales, X, torch.zeros(N, 4))
+    with pytest.raises(ValueError, match="device tensor"):
+        tq.tq_gemm(codes, scales, X, torch.zeros(4, N))
+    with pytest.raises(ValueError, match="y holds"):
+        tq.tq_gemv_affine(codes, scales, scales.clone(), x, torch.zeros(N + 1))
+
+
+def test_binding_checks_attention_shapes():
+    import torch
+    n_kv, t_cap, n_q = 2, 64, 8
+    parts = [torch.zeros(tq.tq_kv_bytes(n_kv, t_cap, p), dtype=torch.uint8) for p in range(4)]
+    kc, ks, vc, vs = parts[0], parts[1].view(torch.int16), parts[2], parts[3].view(torch.int16)
+    q = torch.zeros(n_q, 256, dtype=torch.float16)
+    ws = torch.zeros(1 << 16, dtype=torch.float32)
+    with pytest.raises(ValueError, match="q must be"):
+        tq.tq_attn_decode(torch.zeros(n_q, 128, dtype=torch.float16), kc, ks, vc, vs, 10, n_kv, t_cap, ws)
+    with pytest.raises(ValueError, match="out holds"):
+        tq.tq_attn_decode(q, kc, ks, vc, vs, 10, n_kv, t_cap, ws, out=torch.zeros(n_q - 1, 256))
+    with pytest.raises(ValueError, match="kc holds"):
+        tq.tq_attn_decode(q, kc[:-16], ks, vc, vs, 10, n_kv, t_cap, ws)
+    with pytest.raises(ValueError, match="vs holds"):
+        tq.tq_attn_decode(q, kc, ks, vc, vs[:-8], 10, n_kv, t_cap, ws)
+    with pytest.raises(ValueError, match="device tensor"):
+        tq.tq_attn_decode(q, kc, ks, vc, vs, 10, n_kv, t_cap, ws)
