@@ -133,6 +133,12 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint16_t *__restri
 // so that the MFMA operand reads below hit distinct LDS banks.
 constexpr int kSlotBytes = 9216;  // K codes | V codes | K scales | V scales
 constexpr int kOffV = 4096, kOffKs = 8192;
+// direct-to-LDS loads per tile: one 1 KiB load (64 lanes x 16 bytes) per KiB
+// of K codes and of V codes, and one for both scale pieces
+constexpr int kKLoads = kOffV / 1024, kVLoads = (kOffKs - kOffV) / 1024, kScaleLoads = 1;
+constexpr int kTileLoads = kKLoads + kVLoads + kScaleLoads;
+static_assert(kSlotBytes - kOffKs == 64 * 16 * kScaleLoads, "one load carries both scale pieces");
+static_assert(kTileLoads < 64, "vmcnt counts at most 63 loads");
 constexpr int kRingBytes = 2 * kSlotBytes;  // per wave
 static_assert(16 * (kHD + 2) * 4 <= kRingBytes, "a wave's merge rows fit in its ring");
 
@@ -155,12 +161,12 @@ __device__ __forceinline__ void stage_tile(const uint32_t *__restrict__ kc, cons
         lane < 32 ? reinterpret_cast<const unsigned char *>(ks + (h * TC + tb) * 8) + 16 * lane
                   : reinterpret_cast<const unsigned char *>(vs + (h * (TC >> 5) + blk) * 256) + 16 * (lane - 32);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kKLoads; ++i) {
         const int L = 64 * i + lane, r = L >> 3, j = (L & 7) ^ (r & 7);
         __builtin_amdgcn_global_load_lds(kb + 16 * (8 * r + j), dst + 1024 * i, 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < kVLoads; ++i) {
         const int L = 64 * i + lane, R = L >> 2, k = (L & 3) ^ ((R >> 1) & 3);
         __builtin_amdgcn_global_load_lds(vb + 16 * (4 * R + k), dst + kOffV + 1024 * i, 16, 0, 0);
     }
@@ -224,9 +230,10 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
 
     for (int j = 0; j < ntiles; ++j) {
         const int tb = tfirst + 32 * kWaves * j;
-        // in flight: tile j and, unless j is the last, tile j + 1
+        // in flight: tile j and, unless j is the last, tile j + 1 (whose
+        // kTileLoads loads are the youngest: loads complete in order)
         if (j + 1 < ntiles)
-            asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+            asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kTileLoads) : "memory");
         else
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         unsigned char *slot = ring + (j & 1) * kSlotBytes;
@@ -288,13 +295,27 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
         // P^T scaled by the value scales, per group: B'[k = s][n] = p_s d_V
         const half2_t p2[4] = {half2_t{(_Float16)p[0], (_Float16)p[1]}, half2_t{(_Float16)p[2], (_Float16)p[3]},
                                half2_t{(_Float16)p[4], (_Float16)p[5]}, half2_t{(_Float16)p[6], (_Float16)p[7]}};
+        // Tokens at or past the chunk's end have p = 0, but their value
+        // scales are whatever the cache holds there (a NaN or Inf would turn
+        // 0 * d into NaN): in a tile that crosses the end, the scales of those
+        // tokens are replaced by +0 before they meet p.  Token of pair half
+        // (s & 1) of dword s / 2: tb + 16 (s / 4) + 4 c + (s % 4).
+        uint32_t vmask[4] = {~0u, ~0u, ~0u, ~0u};
+        if (tb + 32 > t_end) {
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const int t0 = tb + 16 * (s2 >> 1) + 4 * c + 2 * (s2 & 1);
+                vmask[s2] = (t0 < t_end ? 0x0000FFFFu : 0u) | (t0 + 1 < t_end ? 0xFFFF0000u : 0u);
+            }
+        }
         half8 bp[8];
 #pragma unroll
         for (int g = 0; g < 8; ++g) {
             // (the elements go through plain uint32_t: a bit cast taken directly
             // of a vector element has read element 0 for every index)
             const u32x4 dv = lds16(slot + kOffKs + 512 + 128 * c + 16 * g);
-            const uint32_t d0 = dv[0], d1 = dv[1], d2 = dv[2], d3 = dv[3];
+            const uint32_t d0 = dv[0] & vmask[0], d1 = dv[1] & vmask[1], d2 = dv[2] & vmask[2],
+                           d3 = dv[3] & vmask[3];
             const half2_t b0 = p2[0] * __builtin_bit_cast(half2_t, d0);
             const half2_t b1 = p2[1] * __builtin_bit_cast(half2_t, d1);
             const half2_t b2 = p2[2] * __builtin_bit_cast(half2_t, d2);

@@ -218,3 +218,30 @@ def test_attn_decode_errors():
                         torch.zeros(2, 4, 256, dtype=torch.float16, device="cuda"), 63, 4, 64,
                         c.kc, c.ks, c.vc, c.vs)                               # past the capacity
     assert e.value.status == 2
+
+
+@pytest.mark.parametrize("T", [1, 37, 100, 4099])
+def test_attn_decode_ignores_cache_contents_past_T(T):
+    """The cache memory past T holds NaN and Inf scale patterns and random
+    codes (as after torch.empty and an earlier sequence): the outputs must
+    still match the oracle on the first T tokens.  Tokens past T only sit in
+    the same 32-token blocks as the last real ones; nothing past t_cap is
+    read."""
+    n_kv, n_q = 4, 24
+    TC = (T + 31) // 32 * 32 + 64
+    k, v = kv_inputs(21000 + T, T, n_kv)
+    g = synth.rng(21100 + T)
+    q = g.standard_normal((n_q, 256)).astype(np.float16)
+    c = Cache(n_kv, TC)
+    specials = torch.tensor([0x7E00, 0x7C00, -1024, 0x7FFF], dtype=torch.int32)  # NaN, Inf, -Inf, NaN
+    for arr in (c.ks, c.vs):
+        idx = torch.from_numpy(g.integers(0, 4, arr.numel())).long()
+        arr.copy_(specials[idx].to(torch.int16).cuda())
+    for arr in (c.kc, c.vc):
+        arr.copy_(torch.from_numpy(g.integers(0, 256, arr.numel()).astype(np.uint8)).cuda())
+    c.append(k, v, 0)
+    kn, ks, vn, vs = oracle_cache(k, v)
+    ref, A = oracle.attn_decode(q, kn, ks, vn, vs)
+    out = run_attention(q, c, T, n_q)
+    assert np.isfinite(out).all(), "non-finite output"
+    assert_attn(out, ref, A, "garbage past T=%d" % T)
