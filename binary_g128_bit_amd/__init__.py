@@ -30,7 +30,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 # every symbol include/tq.h declares
 EXPORTS = ("tq_codes_bytes", "tq_scales_count", "tq_pack", "tq_unpack", "tq_gemv", "tq_gemm",
            "tq_embed", "tq_gemv_affine", "tq_kv_bytes", "tq_kv_append", "tq_attn_workspace_bytes",
-           "tq_attn_decode", "tq_stream_read", "tq_last_error", "tq_last_error_index", "tq_version")
+           "tq_attn_decode", "tq_attn_decode_noalloc", "tq_stream_read", "tq_last_error", "tq_last_error_index", "tq_version")
 
 
 class TQError(RuntimeError):
@@ -80,6 +80,8 @@ def lib():
     L.tq_attn_workspace_bytes.restype = ctypes.c_size_t
     L.tq_attn_decode.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp, ctypes.c_size_t, vp]
     L.tq_attn_decode.restype = i32
+    L.tq_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, vp, vp]
+    L.tq_attn_decode_noalloc.restype = i32
     L.tq_stream_read.argtypes = [vp, ctypes.c_size_t, vp, i32, vp]
     L.tq_stream_read.restype = i32
     L.tq_last_error.argtypes = []
@@ -314,3 +316,22 @@ def tq_attn_decode(q, kc, ks, vc, vs, T, n_kv, t_cap, workspace, out=None, strea
                                 workspace.numel() * workspace.element_size(), _stream(stream, q)))
     return out
 
+
+def tq_attn_decode_noalloc(q, kc, ks, vc, vs, T, n_kv, t_cap, out=None, stream=None):
+    """tq_attn_decode on the library's own device scratch: no workspace
+    argument, nothing allocated by the call (pass `out` to allocate nothing
+    here either).  Calls that overlap on one GPU race."""
+    import torch
+    if q.dim() != 2 or q.shape[1] != 256:
+        raise ValueError("q must be [n_q][256], got %s" % (tuple(q.shape),))
+    n_q = q.shape[0]
+    if out is None:
+        out = torch.empty(n_q, 256, dtype=torch.float32, device=q.device)
+    _out_check(out, "out", n_q * 256)
+    _cache_checks(n_kv, t_cap, kc, ks, vc, vs)
+    half = (torch.float16, torch.int16)
+    _check(lib().tq_attn_decode_noalloc(_dev(q, "q", half), _dev(kc, "kc", (torch.uint8,)),
+                                        _dev(ks, "ks", half), _dev(vc, "vc", (torch.uint8,)),
+                                        _dev(vs, "vs", half), T, n_q, n_kv, t_cap,
+                                        _dev(out, "out", (torch.float32,)), _stream(stream, q)))
+    return out

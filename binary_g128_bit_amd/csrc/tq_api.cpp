@@ -26,6 +26,8 @@ int32_t kv_append_enqueue(const uint16_t *k, const uint16_t *v, int64_t n_tok, i
 int32_t attn_decode_enqueue(const uint16_t *q, const uint8_t *kc, const uint16_t *ks,
                             const uint8_t *vc, const uint16_t *vs, int64_t T, int64_t TC,
                             int64_t n_q, int64_t n_kv, float *out, float *ws, hipStream_t stream);
+size_t attn_scratch_bytes();
+int32_t attn_scratch(float **out);
 int32_t embed_enqueue(const uint8_t *codes, const uint16_t *scales, const int32_t *ids,
                       uint16_t *out, int64_t n_ids, int64_t N, int64_t K, int32_t variant,
                       hipStream_t stream);
@@ -150,26 +152,61 @@ size_t tq_attn_workspace_bytes(int64_t T, int64_t n_q, int64_t n_kv) {
     return tq::attn_ws_bytes(T, n_q, n_kv);
 }
 
+}  // extern "C"
+
+namespace tq {
+namespace {
+// Shape, pointer and alignment checks shared by the two attention entry points
+// (the workspace pointer is checked by the one that takes it).
+int32_t check_attn(const uint16_t *q, const uint8_t *kc, const uint16_t *ks, const uint8_t *vc,
+                   const uint16_t *vs, int64_t T, int64_t n_q, int64_t n_kv, int64_t t_cap,
+                   const float *out) {
+    if (int32_t rc = check_kv(n_kv, t_cap)) return rc;
+    if (n_q < n_kv || n_q % n_kv || n_q / n_kv > 16)
+        return fail(TQ_ERR_SHAPE, "n_q=%lld must be a multiple of n_kv=%lld, at most 16 times it",
+                    (long long)n_q, (long long)n_kv);
+    if (T < 1 || T > t_cap)
+        return fail(TQ_ERR_SHAPE, "T=%lld outside [1, t_cap=%lld]", (long long)T, (long long)t_cap);
+    if (!q || !kc || !ks || !vc || !vs || !out) return fail(TQ_ERR_NULL, "NULL pointer argument");
+    if (!aligned(q, 16) || !aligned(kc, 16) || !aligned(ks, 16) || !aligned(vc, 16) ||
+        !aligned(vs, 16) || !aligned(out, 4))
+        return fail(TQ_ERR_ALIGN, "q and cache must be 16-byte aligned, out 4-byte");
+    return TQ_OK;
+}
+}  // namespace
+}  // namespace tq
+
+extern "C" {
+
 int32_t tq_attn_decode(const uint16_t *q, const uint8_t *kc, const uint16_t *ks, const uint8_t *vc,
                        const uint16_t *vs, int64_t T, int64_t n_q, int64_t n_kv, int64_t t_cap,
                        float *out, void *workspace, size_t workspace_bytes, void *stream) {
     tq::clear_error();
-    if (int32_t rc = tq::check_kv(n_kv, t_cap)) return rc;
-    if (n_q < n_kv || n_q % n_kv || n_q / n_kv > 16)
-        return tq::fail(TQ_ERR_SHAPE, "n_q=%lld must be a multiple of n_kv=%lld, at most 16 times it",
-                        (long long)n_q, (long long)n_kv);
-    if (T < 1 || T > t_cap)
-        return tq::fail(TQ_ERR_SHAPE, "T=%lld outside [1, t_cap=%lld]", (long long)T, (long long)t_cap);
-    if (!q || !kc || !ks || !vc || !vs || !out || !workspace)
-        return tq::fail(TQ_ERR_NULL, "NULL pointer argument");
-    if (!tq::aligned(q, 16) || !tq::aligned(kc, 16) || !tq::aligned(ks, 16) || !tq::aligned(vc, 16) ||
-        !tq::aligned(vs, 16) || !tq::aligned(workspace, 16) || !tq::aligned(out, 4))
-        return tq::fail(TQ_ERR_ALIGN, "q, cache and workspace must be 16-byte aligned, out 4-byte");
+    if (int32_t rc = tq::check_attn(q, kc, ks, vc, vs, T, n_q, n_kv, t_cap, out)) return rc;
+    if (!workspace) return tq::fail(TQ_ERR_NULL, "NULL pointer argument");
+    if (!tq::aligned(workspace, 16)) return tq::fail(TQ_ERR_ALIGN, "workspace must be 16-byte aligned");
     const size_t need = tq::attn_ws_bytes(T, n_q, n_kv);
     if (workspace_bytes < need)
         return tq::fail(TQ_ERR_SHAPE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
     return tq::attn_decode_enqueue(q, kc, ks, vc, vs, T, t_cap, n_q, n_kv, out,
                                    static_cast<float *>(workspace), static_cast<hipStream_t>(stream));
+}
+
+int32_t tq_attn_decode_noalloc(const uint16_t *q, const uint8_t *kc, const uint16_t *ks,
+                               const uint8_t *vc, const uint16_t *vs, int64_t T, int64_t n_q,
+                               int64_t n_kv, int64_t t_cap, float *out, void *stream) {
+    tq::clear_error();
+    if (int32_t rc = tq::check_attn(q, kc, ks, vc, vs, T, n_q, n_kv, t_cap, out)) return rc;
+    const size_t need = tq::attn_ws_bytes(T, n_q, n_kv);
+    if (need > tq::attn_scratch_bytes())
+        return tq::fail(TQ_ERR_SHAPE,
+                        "T=%lld n_q=%lld n_kv=%lld needs %zu bytes of scratch, above the %zu this "
+                        "entry point holds; use tq_attn_decode with a workspace",
+                        (long long)T, (long long)n_q, (long long)n_kv, need, tq::attn_scratch_bytes());
+    float *ws = nullptr;
+    if (int32_t rc = tq::attn_scratch(&ws)) return rc;
+    return tq::attn_decode_enqueue(q, kc, ks, vc, vs, T, t_cap, n_q, n_kv, out, ws,
+                                   static_cast<hipStream_t>(stream));
 }
 
 int32_t tq_gemv_affine(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,

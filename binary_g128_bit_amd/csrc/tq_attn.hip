@@ -36,6 +36,8 @@
 // a second kernel merges the chunks.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -477,6 +479,46 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restri
 
 // Tokens per attention chunk: a multiple of 32 * kWaves giving about two
 // workgroups per CU over the KV heads, and never more than kMaxChunks chunks.
+// ---------------------------------------------------------- no-allocation
+// Scratch for the entry point that allocates nothing (tq_attn_decode_noalloc):
+// the per-chunk (max, sum, output) rows of attn_partial_kernel, which the
+// caller otherwise passes as a workspace.  8 MiB per GPU, held until the
+// process ends; the model's shape (24 query heads over 4 KV heads) needs at
+// most about 3 MiB at any context length.  Nothing in it has to start at
+// zero: the partial kernel writes every row the merge reads in the same call.
+// All calls on one GPU share it, so calls that overlap on a GPU (different
+// streams, no ordering between them) race.
+constexpr size_t kScratchBytes = size_t(8) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t attn_scratch_bytes() { return kScratchBytes; }
+
+// The current device's copy of `scratch`: looked up once per device (with
+// that device current) and kept.  In host code the array's name is only a
+// stand-in for the device symbol, so kernels get this address, never the name.
+int32_t attn_scratch(float **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(TQ_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(TQ_ERR_HIP, "device %d above the %d supported", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(TQ_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+        g_scratch_ptr[dev] = static_cast<float *>(p);
+    }
+    *out = g_scratch_ptr[dev];
+    return TQ_OK;
+}
+
 int64_t attn_chunk(int64_t T, int64_t n_kv) {
     const int64_t step = 32 * kWaves;
     int64_t want = (T * n_kv + 511) / 512;

@@ -242,6 +242,22 @@ int32_t tq_attn_decode(const uint16_t *q, const uint8_t *kc, const uint16_t *ks,
                        int64_t n_kv, int64_t t_cap, float *out, void *workspace,
                        size_t workspace_bytes, void *stream);
 
+/* Device.  For callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): tq_attn_decode
+ * with the same arguments minus the workspace, running the same kernels on a
+ * scratch array the library holds in device memory (8 MiB per GPU, kept until
+ * the process ends; the model's 24 query heads over 4 KV heads need about
+ * 3 MiB at any T).  A call whose workspace would exceed it (see
+ * tq_attn_workspace_bytes) returns TQ_ERR_SHAPE before any HIP call.  The
+ * first call on a device looks the array up (one hipGetSymbolAddress; a
+ * failure returns TQ_ERR_HIP); no call allocates.  Every call on a GPU shares
+ * that GPU's array: calls that overlap on one GPU (streams with no ordering
+ * between them) race and must be serialised by the caller.  Results are
+ * identical to tq_attn_decode's. */
+int32_t tq_attn_decode_noalloc(const uint16_t *q, const uint8_t *kc, const uint16_t *ks,
+                               const uint8_t *vc, const uint16_t *vs, int64_t T, int64_t n_q,
+                               int64_t n_kv, int64_t t_cap, float *out, void *stream);
+
 /* Measurement aid, not part of the matmul: a plain streaming read of `bytes`
  * (a positive multiple of 16) of the device buffer `buf` (16-byte aligned),
  * each 16-byte unit loaded once, on `blocks_per_cu` (1..8) workgroups of 512

@@ -249,3 +249,26 @@ def test_binding_checks_attention_shapes():
         tq.tq_attn_decode(q, kc, ks, vc, vs[:-8], 10, n_kv, t_cap, ws)
     with pytest.raises(ValueError, match="device tensor"):
         tq.tq_attn_decode(q, kc, ks, vc, vs, 10, n_kv, t_cap, ws)
+
+
+def test_attn_noalloc_validates_on_host():
+    """The no-allocation attention entry point checks shapes, pointers and its
+    scratch limit before any HIP call (so this runs without a GPU)."""
+    L = tq.lib()
+    F = FAKE
+    call = lambda T, n_q, n_kv, t_cap, q=F, out=F: L.tq_attn_decode_noalloc(
+        q, F, F, F, F, T, n_q, n_kv, t_cap, out, None)
+    assert call(10, 24, 4, 64, q=0) == 1
+    assert call(10, 24, 4, 64, out=0) == 1
+    assert call(65, 24, 4, 64) == 2          # T above the capacity
+    assert call(10, 25, 4, 64) == 2          # n_q not a multiple of n_kv
+    assert call(10, 24, 4, 64, q=F + 8) == 7
+    # one KV head with 16 query heads at T = 65536: 8.06 MiB of partial rows,
+    # above the 8 MiB scratch
+    need = tq.tq_attn_workspace_bytes(65536, 16, 1)
+    assert need > 8 << 20
+    assert call(65536, 16, 1, 65536) == 2
+    assert "scratch" in L.tq_last_error().decode()
+    # the model's shape fits at every context length tried
+    for T in (1, 4096, 32768, 102400, 262144, 1 << 20):
+        assert tq.tq_attn_workspace_bytes(T, 24, 4) <= 8 << 20, T
