@@ -34,6 +34,16 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, vendor figure
 PEAK_F16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA, vendor figure
 STACK_BYTES = 6_595_543_040  # packed bytes of the 64-layer 24.83B-weight stack
 COPY_BYTES = 1 << 30         # bytes read (and written) by the calibration copy
+GEMV_KERNEL_NAME = ("gemv_xreg_kernel<0,16,5,8,false,true> (ternary, pipelined) "
+                    "on [gate;up] 34816x5120")
+
+
+def log(msg):
+    """Progress on stderr (the JSON line alone goes to stdout)."""
+    print("[bench %.1fs] %s" % (time.perf_counter() - _T0, msg), file=sys.stderr, flush=True)
+
+
+_T0 = time.perf_counter()
 
 
 def packed_bytes(N, K, variant=0):
@@ -44,8 +54,10 @@ def parse():
     p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=300)
-    p.add_argument("--warmup", type=int, default=1000,
-                   help="untimed steps first; the clocks take about 20 ms of load to settle")
+    p.add_argument("--warmup", type=int, default=100,
+                   help="untimed steps first (see --warmup-ms)")
+    p.add_argument("--warmup-ms", type=float, default=300.0,
+                   help="the warm-up runs at least this long (wall clock) even past --warmup steps")
     p.add_argument("--rotate-gib", type=float, default=1.0)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target duration of the oracle's CPU-baseline sample")
@@ -80,11 +92,41 @@ def read_traffic(kernel_tag, src_hash):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(mats, seconds):
-    """The oracle, as it stands, on the step's matrices on all the host cores
-    this process may use: whole passes over gate, up and down, repeated until
-    about `seconds` have elapsed (or the first rows of each matrix if a single
-    pass would take longer).  Returns the cpu_baseline object."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(oracle, codes, s, X, K, threads, seconds, min_rows=16):
+    """Packed-weight GB/s of the oracle on leading rows of one matrix: a short
+    probe sizes the sample to about `seconds`, then the sample is timed.
+    Returns (gbs, rows, elapsed_s)."""
+    n = min(codes.shape[0], min_rows)
+    t0 = time.perf_counter()
+    oracle.gemm(codes[:n], s[:n], X, n, K, threads=threads)
+    per_row = max((time.perf_counter() - t0) / n, 1e-9)
+    n = int(min(codes.shape[0], max(min_rows, seconds / per_row)))
+    t0 = time.perf_counter()
+    oracle.gemm(codes[:n], s[:n], X, n, K, threads=threads)
+    dt = time.perf_counter() - t0
+    return packed_bytes(n, K) / dt / 1e9, n, dt
+
+
+def cpu_baseline(mats, seconds, c1):
+    """The oracle, as it stands, on the GPU machine's host cores.  `value`: whole
+    passes over the step's gate, up and down (all the cores this process may
+    use), repeated for about `seconds`.  Beside it: a single-thread run of the
+    same matrices and per-config rates on bounded row samples (each config's
+    own activation width M; the LM head's rows have the gate's K = 5120, so
+    its per-row cost is sampled on gate rows).  Rates are packed-weight GB/s
+    over the rows processed, comparable with the GPU figures."""
+    import numpy as np
     import oracle
     threads = oracle.default_threads()
     codes, s, x, N, K = mats[0]
@@ -106,9 +148,42 @@ def cpu_baseline(mats, seconds):
             break
     what = ("%d whole passes over gate, up and down (%d weights each pass)" % (passes, total_weights)
             if frac >= 1.0 else "the first %.1f%% of the rows of gate, up and down" % (100 * frac))
-    return {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": "fp64 oracle GEMV, batch 1: %s, %.1f s" % (what, dt)}
+    out = {"value": round(done_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+           "kind": "oracle", "cpu_model": cpu_model(),
+           "sample": "fp64 oracle GEMV, batch 1: %s, %.1f s" % (what, dt)}
+    # single thread, same matrices, bounded sample
+    st = [_oracle_rate(oracle, c, sc, xx, KK, 1, seconds / 6.0) for c, sc, xx, NN, KK in mats]
+    out["single_thread"] = {"value": round(sum(r[0] * r[2] for r in st) / sum(r[2] for r in st), 4),
+                            "unit": "GB/s", "cores": 1,
+                            "sample": "rows %s of gate, up, down" % [r[1] for r in st]}
+    # per config: (name, codes, scales, K, M); activations N(0, 1) fp16 of width M
+    g = np.random.default_rng(2024)
+    (cg, sg, _, _, Kg), _, (cd, sd, _, _, Kd) = mats
+    c1_codes, c1_s, c1_K = c1
+    confs = [("C1_1024x1024_M1", c1_codes, c1_s, c1_K, 1),
+             ("C2a_gate_17408x5120_M1", cg, sg, Kg, 1),
+             ("C2b_down_5120x17408_M1", cd, sd, Kd, 1),
+             ("C5_lm_head_248320x5120_M1_rows_of_gate", cg, sg, Kg, 1),
+             ("C5_lm_head_248320x5120_M8_rows_of_gate", cg, sg, Kg, 8)]
+    for M in (4, 16, 64, 512):
+        confs.append(("C4_gate_17408x5120_M%d" % M, cg, sg, Kg, M))
+        confs.append(("C4_down_5120x17408_M%d" % M, cd, sd, Kd, M))
+    full_rows = {"C5_lm_head_248320x5120_M1_rows_of_gate": 248320,
+                 "C5_lm_head_248320x5120_M8_rows_of_gate": 248320}
+    per = {}
+    budget = seconds / (2.0 * len(confs))
+    for name, c, sc, KK, M in confs:
+        X = g.standard_normal((M, KK), dtype=np.float32).astype(np.float16)
+        rows_full = full_rows.get(name, c.shape[0])
+        entry = {}
+        for label, th in (("all_cores", threads), ("single_thread", 1)):
+            gbs, n, dt = _oracle_rate(oracle, c, sc, X, KK, th, budget, min_rows=4)
+            entry[label + "_gbs"] = round(gbs, 4)
+            entry[label + "_full_matrix_ms"] = round(dt / n * rows_full * 1e3, 2)
+            entry[label + "_rows_timed"] = n
+        per[name] = entry
+    out["per_config"] = per
+    return out
 
 
 class Dev:
@@ -169,18 +244,26 @@ def per_launch_ms(torch, stream, launch, n, warm=10):
     return sum(a.elapsed_time(b) for a, b in ev) / n
 
 
-def back_to_back_ms(torch, stream, launch, n, warm=10):
-    """Average time per call of n back-to-back calls between two events."""
+def back_to_back_ms(torch, stream, launch, n, warm=10, batches=20):
+    """Time per call of back-to-back calls: `batches` batches of n calls, each
+    batch between two events on `stream`; returns the median batch's average.
+    The call index keeps counting across batches (rotating buffers keep
+    rotating)."""
     for i in range(warm):
         launch(i)
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for i in range(n):
-        launch(i)
-    b.record(stream)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(batches)]
+    i = 0
+    for a, b in ev:
+        a.record(stream)
+        for _ in range(n):
+            launch(i)
+            i += 1
+        b.record(stream)
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / n
+    per = sorted(a.elapsed_time(b) / n for a, b in ev)
+    return per[len(per) // 2]
 
 
 def graph_ms(torch, launch, n, replays=5):
@@ -266,10 +349,20 @@ def stack_sweep(torch, tq, gen, stream):
         graph.replay()
     b.record(stream)
     torch.cuda.synchronize()
-    graph_ms = a.elapsed_time(b) / T
+    replay_ms = a.elapsed_time(b) / T
     graph_ok = graph_ok and bool(torch.equal(launches[-1][3], ref))
-    kernel_ms = sum(per_launch_ms(torch, stream, lambda i, L=L: tq.tq_gemv(*L), 5, warm=2)
-                    for L in launches)
+    # per shape: that shape's launches of the token replayed from their own graph
+    shapes = {}
+    for L in launches:
+        shapes.setdefault((L[3].shape[0], L[2].shape[0]), []).append(L)
+    per_shape = {}
+    for (N, K), Ls in shapes.items():
+        us = graph_ms(torch, lambda i, Ls=Ls: tq.tq_gemv(*Ls[i % len(Ls)]), len(Ls)) * 1e3
+        nb = packed_bytes(N, K)
+        per_shape["%dx%d" % (N, K)] = {"launches_per_token": len(Ls), "us_graph": round(us, 3),
+                                       "gbs": round(nb / us / 1e3, 1),
+                                       "frac_hbm": round(nb / us / 1e3 / PEAK_HBM_GBS, 4)}
+    kernel_ms = sum(v["launches_per_token"] * v["us_graph"] for v in per_shape.values()) / 1e3
     del graph
     return {
         "workload": "64-layer batch-1 ternary decode sweep, 24.83B weights, each read once "
@@ -277,12 +370,13 @@ def stack_sweep(torch, tq, gen, stream):
         "bytes_per_token": total,
         "launches_per_token": len(launches),
         "ms_per_token_eager": round(eager_ms, 4),
-        "ms_per_token_graph": round(graph_ms, 4),
-        "ms_per_token_kernels_only": round(kernel_ms, 4),
+        "ms_per_token_graph": round(replay_ms, 4),
+        "ms_per_token_sum_of_shapes": round(kernel_ms, 4),
+        "per_shape": per_shape,
         "tok_s_eager": round(1e3 / eager_ms, 1),
-        "tok_s_graph": round(1e3 / graph_ms, 1),
-        "gbs_graph": round(total / graph_ms / 1e6, 1),
-        "pct_of_hbm_peak_graph": round(100 * total / graph_ms / 1e6 / PEAK_HBM_GBS, 2),
+        "tok_s_graph": round(1e3 / replay_ms, 1),
+        "gbs_graph": round(total / replay_ms / 1e6, 1),
+        "pct_of_hbm_peak_graph": round(100 * total / replay_ms / 1e6 / PEAK_HBM_GBS, 2),
         "graph_replay_matches_eager": graph_ok,
     }
 
@@ -336,6 +430,18 @@ def binary_and_lm_head(torch, tq, gen, stream):
     Y = torch.empty(8, N, dtype=torch.float32, device=gen.dev)
     ms1 = back_to_back_ms(torch, stream, lambda i: tq.tq_gemv(pool[i % 3][0], pool[i % 3][1], X[0], Y[0]), 30)
     ms8 = back_to_back_ms(torch, stream, lambda i: tq.tq_gemm(pool[i % 3][0], pool[i % 3][1], X, Y), 30)
+    del pool
+    torch.cuda.empty_cache()
+    # the 1-bit head, three copies
+    nbb = packed_bytes(N, K, 1)
+    bpool = [(gen.codes(N, K, 1), gen.scales(N, K)) for _ in range(3)]
+    msb = back_to_back_ms(torch, stream, lambda i: tq.tq_gemv(bpool[i % 3][0], bpool[i % 3][1], X[0], Y[0],
+                                                              variant=tq.TQ_BINARY), 30)
+    out["bin_lm_head_248320x5120_M1"] = {"us": round(msb * 1e3, 2), "gbs": round(nbb / msb / 1e6, 1),
+                                         "frac_hbm": round(nbb / msb / 1e6 / PEAK_HBM_GBS, 4)}
+    del bpool
+    torch.cuda.empty_cache()
+    pool = [(gen.codes(N, K, 0), gen.scales(N, K)) for _ in range(3)]
     out["lm_head_248320x5120_M1"] = {"us": round(ms1 * 1e3, 2), "gbs": round(nb / ms1 / 1e6, 1),
                                      "frac_hbm": round(nb / ms1 / 1e6 / PEAK_HBM_GBS, 4)}
     out["lm_head_248320x5120_M8"] = {"us": round(ms8 * 1e3, 2), "gbs": round(nb / ms8 / 1e6, 1),
@@ -478,6 +584,66 @@ def kv_attention(torch, tq, gen, stream):
     return out
 
 
+def stream_ceiling(torch, tq, dev, stream):
+    """A plain streaming read (tq_stream_read) of the dominant launches' byte
+    counts, over windows rotating through 1.25 GiB, at 1, 2 and 4 workgroups
+    per CU; the best of the three per size.  The ceiling a bandwidth-bound
+    launch of that size is measured against."""
+    total = 5 << 28
+    buf = torch.empty(total, dtype=torch.uint8, device=dev)
+    buf.fill_(0x5A)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    out = {}
+    for nbytes in (47349760, 23674880, 337715200):
+        copies = total // nbytes
+        views = [buf[i * nbytes:(i + 1) * nbytes] for i in range(copies)]
+        best = None
+        for bpc in (1, 2, 4):
+            ms = back_to_back_ms(torch, stream,
+                                 lambda i: tq.tq_stream_read(views[i % copies], sink, bpc),
+                                 50 if nbytes < 100_000_000 else 20)
+            if best is None or ms < best[0]:
+                best = (ms, bpc)
+        ms, bpc = best
+        out["bytes_%d" % nbytes] = {"us": round(ms * 1e3, 3), "gbs": round(nbytes / ms / 1e6, 1),
+                                    "frac_hbm": round(nbytes / ms / 1e6 / PEAK_HBM_GBS, 4),
+                                    "blocks_per_cu": bpc}
+    del buf
+    torch.cuda.empty_cache()
+    return out
+
+
+def c1_problems():
+    """The 1024 x 1024 GEMV inputs, ternary and binary, packed on the host."""
+    import binary_g128_bit_amd as tq
+    from binary_g128_bit_amd import synth
+    out = {}
+    for name, variant, cfg in (("ternary", tq.TQ_TERNARY, 1), ("binary", tq.TQ_BINARY, 5)):
+        N, K = synth.C1
+        t, s, X = synth.problem(synth.seed_for(cfg, 0), N, K, 1, variant)
+        out[name] = (tq.tq_pack(t, variant), s, X, variant)
+    return out
+
+
+def c1_latency(torch, tq, dev, stream, probs):
+    """Microseconds per 1024 x 1024 GEMV call (the whole matrix fits in L2):
+    back-to-back calls through Python, and graph-replayed (kernel only)."""
+    out = {}
+    N, K = 1024, 1024
+    for name, (codes, s, X, variant) in probs.items():
+        cd, sd = torch.from_numpy(codes).to(dev), torch.from_numpy(s).to(dev)
+        x = torch.from_numpy(X[0]).to(dev)
+        y = torch.empty(N, dtype=torch.float32, device=dev)
+
+        def launch(i):
+            return tq.tq_gemv(cd, sd, x, y, variant=variant)
+
+        out[name] = {"us_per_call": round(back_to_back_ms(torch, stream, launch, 50) * 1e3, 3),
+                     "us_graph": round(graph_ms(torch, launch, 60) * 1e3, 3),
+                     "bytes": packed_bytes(N, K, variant)}
+    return out
+
+
 def copy_calibration():
     import torch
     dev = torch.device("cuda:0")
@@ -539,10 +705,22 @@ def main():
             c, s = bufs[slot][m]
             tq.tq_gemv(c, s, xs[m], ys[m])
 
-    # ---- timed region: K steps over rotating buffers
-    for w in range(args.warmup):
+    log("inputs ready; warm-up")
+    # ---- untimed warm-up: the W steps asked for, continued until at least
+    # --warmup-ms of wall time has passed (the clocks settle only after some
+    # tens of milliseconds of load, whatever W is)
+    w = 0
+    t0 = time.perf_counter()
+    while w < args.warmup or (time.perf_counter() - t0) * 1e3 < args.warmup_ms:
         step(w % slots)
+        w += 1
+        if w % 256 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    warmup_ms = (time.perf_counter() - t0) * 1e3
+    warmup_steps = w
+
+    # ---- timed region: K steps over rotating buffers
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
     for k in range(args.steps):
@@ -552,31 +730,38 @@ def main():
     ms_per_step = e0.elapsed_time(e1) / args.steps
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # ---- dominant kernel: the fused 34816x5120 GEMV, each launch timed alone
-    launches = max(200, args.steps)
+    log("timed step done: %.3f us/step" % (ms_per_step * 1e3))
+    # ---- dominant kernel: the fused 34816x5120 GEMV
+    launches = 100
 
     def gemv_launch(m, pool):
         return lambda i: tq.tq_gemv(pool[i % len(pool)][0], pool[i % len(pool)][1], xs[m],
                                     ys[m][:pool[0][1].shape[0]])
 
     gu_pool = [bufs[r][0] for r in range(slots)]
-    gu_ms = per_launch_ms(torch, stream, gemv_launch(0, gu_pool), launches)
-    down_ms = back_to_back_ms(torch, stream, gemv_launch(1, [bufs[r][1] for r in range(slots)]), launches)
-    # context: gate alone (17408 x 5120, the unfused per-matrix launch)
+    down_pool = [bufs[r][1] for r in range(slots)]
     half = [(c[: c.shape[0] // 2], s[: s.shape[0] // 2]) for c, s in gu_pool]
-    gate_ms = back_to_back_ms(torch, stream, gemv_launch(0, half), launches)
+    # average launch duration: back-to-back launches between two events on the
+    # kernel's stream, median of 20 batches (per-launch event pairs add the
+    # events' own cost and are printed for reference only)
     gu_b2b_ms = back_to_back_ms(torch, stream, gemv_launch(0, gu_pool), launches)
+    down_ms = back_to_back_ms(torch, stream, gemv_launch(1, down_pool), launches)
+    gate_ms = back_to_back_ms(torch, stream, gemv_launch(0, half), launches)
+    gu_ms = per_launch_ms(torch, stream, gemv_launch(0, gu_pool), launches)
     # the same launches replayed from a HIP graph (no Python cost per launch)
     graph_us = {"gate_up_34816x5120": graph_ms(torch, gemv_launch(0, gu_pool), 4 * slots) * 1e3,
-                "down_5120x17408": graph_ms(torch, gemv_launch(1, [bufs[r][1] for r in range(slots)]),
-                                            4 * slots) * 1e3,
+                "down_5120x17408": graph_ms(torch, gemv_launch(1, down_pool), 4 * slots) * 1e3,
                 "gate_17408x5120_unfused": graph_ms(torch, gemv_launch(0, half), 4 * slots) * 1e3}
     gu_bytes = packed_bytes(Ng + Nu, Kg)
-    # average launch duration: back-to-back launches between two events on the
-    # kernel's stream (per-launch event pairs add the events' own cost)
     achieved = gu_bytes / (gu_b2b_ms * 1e-3) / 1e9
     src = os.path.join(ROOT, "binary_g128_bit_amd", "csrc", "tq_gemv.hip")
     traffic = read_traffic("gemv_tern_34816x5120", source_hash(src))
+    log("per-launch timings done")
+    ceiling = stream_ceiling(torch, tq, dev, stream)
+    log("stream ceiling done")
+    c1_probs = c1_problems()
+    c1 = c1_latency(torch, tq, dev, stream, c1_probs)
+    c1_host = (c1_probs["ternary"][0], c1_probs["ternary"][1], 1024)
 
     line = {
         "metric": "packed-weight GB/s and % of HBM peak, batch-1 ternary GEMV; equiv tokens/s",
@@ -585,6 +770,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_run": {"steps": warmup_steps, "ms": round(warmup_ms, 1)},
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
@@ -601,6 +787,7 @@ def main():
         },
         "pct_of_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
         "equiv_tok_s": round(gbs * 1e9 / STACK_BYTES, 1),
+        "timing": "per-launch figures: median of 20 event-timed batches of back-to-back launches",
         "per_launch_us": {"gate_up_34816x5120": round(gu_b2b_ms * 1e3, 3),
                           "gate_up_34816x5120_event_pairs": round(gu_ms * 1e3, 3),
                           "down_5120x17408": round(down_ms * 1e3, 3),
@@ -609,9 +796,14 @@ def main():
         "per_launch_gbs": {"gate_up_34816x5120": round(achieved, 1),
                            "down_5120x17408": round(packed_bytes(Nd, Kd) / down_ms / 1e6, 1),
                            "gate_17408x5120_unfused": round(packed_bytes(Ng, Kg) / gate_ms / 1e6, 1)},
+        "stream_read_ceiling": ceiling,
+        "frac_of_stream_ceiling": {
+            "gate_up_34816x5120": round(ceiling["bytes_47349760"]["us"] / (gu_b2b_ms * 1e3), 4),
+            "down_5120x17408": round(ceiling["bytes_23674880"]["us"] / (down_ms * 1e3), 4)},
+        "c1_latency": c1,
         "roofline": {
             "bound": "hbm",
-            "kernel": "gemv_xreg_kernel<0,16,5,8,false,true> (ternary, pipelined) on [gate;up] 34816x5120",
+            "kernel": GEMV_KERNEL_NAME,
             "achieved": round(achieved, 2),
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
@@ -619,18 +811,31 @@ def main():
             "traffic": traffic,
             "algorithmic_bytes_per_launch": gu_bytes,
         },
-        "cpu_baseline": None if args.no_cpu else cpu_baseline(host, args.cpu_seconds),
+        "context": {
+            "what": "the pages' whole-model single-batch decode through llama.cpp on other "
+                    "machines (context only, not a target)",
+            "source": "blog.devnsb.com, 'Ternary quantization: 27B in 7 GB', deploy size and "
+                      "hardware section",
+            "tok_s": {"H100": 98.0, "M5 Max": 44.0, "M5 Pro": 26.2},
+        },
+        "cpu_baseline": None if args.no_cpu else cpu_baseline(host, args.cpu_seconds, c1_host),
     }
+    log("cpu baseline done" if not args.no_cpu else "cpu baseline skipped")
     if not args.no_extras:
         gen = Dev(torch, tq, dev, 12345)
         line["gemm"] = gemm_widths(torch, tq, gen, stream, bufs, slots)
+        log("gemm widths done")
         line["binary_and_lm_head"] = binary_and_lm_head(torch, tq, gen, stream)
+        log("binary and lm head done")
         line["ternary5"] = ternary5(torch, tq, gen, stream)
         line["affine2"] = affine2(torch, tq, gen, stream)
+        log("ternary5 and affine2 done")
         line["kv4_attention"] = kv_attention(torch, tq, gen, stream)
+        log("attention done")
         del bufs
         torch.cuda.empty_cache()
         line["stack_sweep"] = stack_sweep(torch, tq, gen, stream)
+        log("stack sweep done")
         line["stack_sweep"]["equiv_tok_s_note"] = (
             "tok_s_graph is the whole stack's GEMVs per second; equiv_tok_s above "
             "scales the MLP step's GB/s to the stack's bytes")
