@@ -5,6 +5,9 @@
 // "How the compression works"), evaluated from the packed slots.
 #include <hip/hip_runtime_api.h>
 
+#include <cstdlib>
+#include <cstring>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -12,6 +15,8 @@ int32_t gemv_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_
                      int64_t N, int64_t K, int32_t variant, hipStream_t stream);
 int32_t gemm_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
                      int64_t M, int64_t N, int64_t K, int32_t variant, hipStream_t stream);
+int32_t gemm_quad_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
+                          int64_t M, int64_t N, int64_t K, int32_t variant, hipStream_t stream, bool *handled);
 int32_t gemm_mcol_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
                           int64_t M, int64_t N, int64_t K, int32_t variant, hipStream_t stream,
                           bool *handled);
@@ -33,6 +38,24 @@ int32_t embed_enqueue(const uint8_t *codes, const uint16_t *scales, const int32_
                       hipStream_t stream);
 
 namespace {
+// Kernel choice for small batches, read once per process from TQ_GEMM_QUAD:
+// "off" never takes the 4-row MFMA kernel (tq_gemm_quad.hip), "all" sends it
+// every M <= 4 (M = 1 included), and the default sends it M = 3 and 4, and
+// M = 2 for 1-bit weights.  Measured on the MLP shapes (same box): ternary
+// M = 2 is a tie on 17408 x 5120 and 8 % slower on 5120 x 17408 than the
+// two-row VALU kernel; M = 4 is 15 % faster on 17408 x 5120 and 3 % on
+// 5120 x 17408 than the MFMA stage kernel, 1.5x on the 248320-row head; 1-bit
+// M = 2 and 4 are 5-25 % faster.
+int quad_mode() {
+    static const int mode = [] {
+        const char *v = getenv("TQ_GEMM_QUAD");
+        if (v && strcmp(v, "off") == 0) return 0;
+        if (v && strcmp(v, "all") == 0) return 2;
+        return 1;
+    }();
+    return mode;
+}
+
 int32_t check_device_args(const void *codes, const void *scales, const void *x, const void *y,
                           int64_t M, int64_t N, int64_t K, int32_t group, int32_t variant) {
     if (!codes || !scales || !x || !y) return fail(TQ_ERR_NULL, "NULL pointer argument");
@@ -86,10 +109,15 @@ int32_t tq_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
                             (long long)M);
         return tq::gemv5_enqueue(codes, scales, X, Y, N, K, static_cast<hipStream_t>(stream));
     }
+    bool handled = false;
+    if (tq::quad_mode() == 2 || (tq::quad_mode() == 1 && (M >= 3 || (M == 2 && variant == TQ_BINARY)))) {
+        const int32_t rq = tq::gemm_quad_enqueue(codes, scales, X, Y, M, N, K, variant,
+                                                 static_cast<hipStream_t>(stream), &handled);
+        if (handled || rq != TQ_OK) return rq;
+    }
     if (M == 1)
         return tq::gemv_enqueue(codes, scales, X, Y, N, K, variant,
                                 static_cast<hipStream_t>(stream));
-    bool handled = false;
     const int32_t rc = tq::gemm_mcol_enqueue(codes, scales, X, Y, M, N, K, variant,
                                              static_cast<hipStream_t>(stream), &handled);
     if (handled || rc != TQ_OK) return rc;

@@ -320,16 +320,35 @@ def test_gemm_zero_rows_and_special_scales(M):
     assert np.all(Y[:, 40] == 0)
 
 
+@pytest.mark.parametrize("variant", [TERN, BIN])
+@pytest.mark.parametrize("M,N,K", [(3, 1, 128), (4, 5, 640), (4, 4097, 5120), (3, 33, 19456),
+                                   (4, 7, 19584), (2, 1030, 1152), (4, 248, 17408)])
+def test_gemm_four_row_mfma_kernel(M, N, K, variant):
+    """Batches of 3 and 4 rows (and two-row 1-bit batches) take the 4-row MFMA
+    kernel: one weight row, a ragged chunk-group tail (K = 640), many blocks
+    per workgroup, the largest K whose activations fit LDS (19456) and the
+    first that does not (19584, another kernel)."""
+    codes, s, X = case(9870 + M + N + K, N, K, M, variant, exact=True)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, _ = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert np.array_equal(Y.astype(np.float64), Yref)
+    codes, s, X = case(9880 + M + N + K, N, K, M, variant, exact=False)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, A = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert_tol(Y, Yref, A, "four-row gemm M=%d N=%d K=%d" % (M, N, K))
+
+
 def test_gemm_deterministic():
     """The K-split partial sums are added in a fixed order: repeated calls
     give identical bits."""
-    N, K, M = 2048, 5120, 16
-    codes, s, X = case(9950, N, K, M, TERN, exact=False)
-    cd, sd, Xd = up(codes), up(s), up(X)
-    Y0 = tq.tq_gemm(cd, sd, Xd, variant=TERN)
-    for _ in range(3):
-        Y1 = tq.tq_gemm(cd, sd, Xd, variant=TERN)
-        assert torch.equal(Y0, Y1)
+    N, K = 2048, 5120
+    for M in (16, 4):
+        codes, s, X = case(9950 + M, N, K, M, TERN, exact=False)
+        cd, sd, Xd = up(codes), up(s), up(X)
+        Y0 = tq.tq_gemm(cd, sd, Xd, variant=TERN)
+        for _ in range(3):
+            Y1 = tq.tq_gemm(cd, sd, Xd, variant=TERN)
+            assert torch.equal(Y0, Y1), M
 
 
 def test_graph_replay_matches_eager():
@@ -340,27 +359,32 @@ def test_graph_replay_matches_eager():
     cd, sd, Xd = up(codes), up(s), up(X)
     y = torch.empty(N, dtype=torch.float32, device="cuda")
     Y = torch.empty(16, N, dtype=torch.float32, device="cuda")
-    tq.tq_gemv(cd, sd, Xd[0], y)
-    tq.tq_gemm(cd, sd, Xd, Y)
+    Y4 = torch.empty(4, N, dtype=torch.float32, device="cuda")
+
+    def calls():
+        tq.tq_gemv(cd, sd, Xd[0], y)
+        tq.tq_gemm(cd, sd, Xd, Y)
+        tq.tq_gemm(cd, sd, Xd[:4], Y4)
+
+    calls()
     torch.cuda.synchronize()
-    y_ref, Y_ref = y.clone(), Y.clone()
+    y_ref, Y_ref, Y4_ref = y.clone(), Y.clone(), Y4.clone()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        tq.tq_gemv(cd, sd, Xd[0], y)
-        tq.tq_gemm(cd, sd, Xd, Y)
+        calls()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        tq.tq_gemv(cd, sd, Xd[0], y)
-        tq.tq_gemm(cd, sd, Xd, Y)
+        calls()
     for r in range(4):
-        y.fill_(float("nan"))
-        Y.fill_(float("nan"))
+        for t in (y, Y, Y4):
+            t.fill_(float("nan"))
         tq.tq_gemv(cd, sd, Xd[1], torch.empty_like(y))   # unrelated eager work
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref), "GEMV replay %d" % r
         assert torch.equal(Y, Y_ref), "GEMM replay %d" % r
+        assert torch.equal(Y4, Y4_ref), "four-row GEMM replay %d" % r
