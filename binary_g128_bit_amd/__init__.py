@@ -29,8 +29,9 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtq.so")
 
 # every symbol include/tq.h declares
 EXPORTS = ("tq_codes_bytes", "tq_scales_count", "tq_pack", "tq_unpack", "tq_gemv", "tq_gemm",
-           "tq_embed", "tq_gemv_affine", "tq_kv_bytes", "tq_kv_append", "tq_attn_workspace_bytes",
-           "tq_attn_decode", "tq_attn_decode_noalloc", "tq_stream_read", "tq_last_error", "tq_last_error_index", "tq_version")
+           "tq_gemm_workspace_bytes", "tq_gemm_ws", "tq_embed", "tq_gemv_affine", "tq_kv_bytes",
+           "tq_kv_append", "tq_attn_workspace_bytes", "tq_attn_decode", "tq_attn_decode_noalloc",
+           "tq_stream_read", "tq_last_error", "tq_last_error_index", "tq_version")
 
 
 class TQError(RuntimeError):
@@ -68,6 +69,10 @@ def lib():
     L.tq_gemv.restype = i32
     L.tq_gemm.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
     L.tq_gemm.restype = i32
+    L.tq_gemm_workspace_bytes.argtypes = [i64, i64, i64, i32, i32]
+    L.tq_gemm_workspace_bytes.restype = ctypes.c_size_t
+    L.tq_gemm_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, ctypes.c_size_t, vp]
+    L.tq_gemm_ws.restype = i32
     L.tq_embed.argtypes = [vp, vp, vp, vp, i64, i64, i64, i32, i32, vp]
     L.tq_embed.restype = i32
     L.tq_gemv_affine.argtypes = [vp, vp, vp, vp, vp, i64, i64, i32, vp]
@@ -194,8 +199,16 @@ def tq_gemv(codes, scales, x, y=None, variant=TQ_TERNARY, group=GROUP, stream=No
     return y
 
 
-def tq_gemm(codes, scales, X, Y=None, variant=TQ_TERNARY, group=GROUP, stream=None):
-    """Y[M][N] = X W^T on the current stream.  X float16 [M][K]."""
+def tq_gemm_workspace_bytes(M, N, K, variant=TQ_TERNARY, group=GROUP):
+    """Device workspace bytes tq_gemm can use for this shape (0: none)."""
+    return lib().tq_gemm_workspace_bytes(M, N, K, group, variant)
+
+
+def tq_gemm(codes, scales, X, Y=None, variant=TQ_TERNARY, group=GROUP, stream=None, workspace=None):
+    """Y[M][N] = X W^T on the current stream (or `stream`).  X float16
+    [M][K].  Shapes that can use a workspace (tq_gemm_workspace_bytes > 0)
+    get `workspace` (a device tensor of at least that many bytes) or, when it
+    is None, one from torch's allocator on the launch stream."""
     import torch
     M, K = X.shape
     N = _shape_checks(codes, scales, K, variant)
@@ -204,9 +217,23 @@ def tq_gemm(codes, scales, X, Y=None, variant=TQ_TERNARY, group=GROUP, stream=No
     if tuple(Y.shape) != (M, N):
         raise ValueError("Y has shape %s, (%d, %d) needed" % (tuple(Y.shape), M, N))
     half = (torch.float16, torch.int16)
-    _check(lib().tq_gemm(_dev(codes, "codes", (torch.uint8,)), _dev(scales, "scales", half),
-                         _dev(X, "X", half), _dev(Y, "Y", (torch.float32,)), M, N, K, group,
-                         variant, _stream(stream, X)))
+    args = (_dev(codes, "codes", (torch.uint8,)), _dev(scales, "scales", half), _dev(X, "X", half),
+            _dev(Y, "Y", (torch.float32,)), M, N, K, group, variant)
+    need = lib().tq_gemm_workspace_bytes(M, N, K, group, variant)
+    if need == 0:
+        _check(lib().tq_gemm(*args, _stream(stream, X)))
+        return Y
+    if workspace is None:
+        # allocated on the launch stream, so that torch reuses it only after
+        # this launch's work on that stream
+        if stream is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+        else:
+            with torch.cuda.stream(stream):
+                workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    _check(lib().tq_gemm_ws(*args, _dev(workspace, "workspace", (torch.uint8, torch.float32)), wbytes,
+                            _stream(stream, X)))
     return Y
 
 

@@ -17,6 +17,10 @@ int32_t gemm_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_
                      int64_t M, int64_t N, int64_t K, int32_t variant, hipStream_t stream);
 int32_t gemm_quad_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
                           int64_t M, int64_t N, int64_t K, int32_t variant, hipStream_t stream, bool *handled);
+int32_t gemm_split_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
+                           int64_t M, int64_t N, int64_t K, int32_t variant, float *ws, size_t ws_bytes,
+                           hipStream_t stream, bool *handled);
+size_t gemm_split_ws_bytes(int64_t M, int64_t N, int64_t K, int32_t variant);
 int32_t gemm_mcol_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
                           int64_t M, int64_t N, int64_t K, int32_t variant, hipStream_t stream,
                           bool *handled);
@@ -99,8 +103,25 @@ int32_t tq_gemv(const uint8_t *codes, const uint16_t *scales, const uint16_t *x,
 
 int32_t tq_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
                 int64_t M, int64_t N, int64_t K, int32_t group, int32_t variant, void *stream) {
+    return tq_gemm_ws(codes, scales, X, Y, M, N, K, group, variant, nullptr, 0, stream);
+}
+
+size_t tq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group, int32_t variant) {
+    if (tq::check_shape(M, N, K, group, variant) != TQ_OK) {
+        tq::clear_error();
+        return 0;
+    }
+    return tq::gemm_split_ws_bytes(M, N, K, variant);
+}
+
+int32_t tq_gemm_ws(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
+                   int64_t M, int64_t N, int64_t K, int32_t group, int32_t variant, void *workspace,
+                   size_t workspace_bytes, void *stream) {
     tq::clear_error();
     if (int32_t rc = tq::check_device_args(codes, scales, X, Y, M, N, K, group, variant)) return rc;
+    if (workspace && !tq::aligned(workspace, 16))
+        return tq::fail(TQ_ERR_ALIGN, "workspace must be 16-byte aligned");
+    if (!workspace) workspace_bytes = 0;
     if (variant == TQ_AFFINE2)
         return tq::fail(TQ_ERR_VARIANT, "TQ_AFFINE2 weights need biases: use tq_gemv_affine");
     if (variant == TQ_TERNARY5) {
@@ -114,6 +135,12 @@ int32_t tq_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
         const int32_t rq = tq::gemm_quad_enqueue(codes, scales, X, Y, M, N, K, variant,
                                                  static_cast<hipStream_t>(stream), &handled);
         if (handled || rq != TQ_OK) return rq;
+    }
+    if (M >= 5 && M <= 16) {
+        const int32_t rs = tq::gemm_split_enqueue(codes, scales, X, Y, M, N, K, variant,
+                                                  static_cast<float *>(workspace), workspace_bytes,
+                                                  static_cast<hipStream_t>(stream), &handled);
+        if (handled || rs != TQ_OK) return rs;
     }
     if (M == 1)
         return tq::gemv_enqueue(codes, scales, X, Y, N, K, variant,

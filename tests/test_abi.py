@@ -272,3 +272,20 @@ def test_attn_noalloc_validates_on_host():
     # the model's shape fits at every context length tried
     for T in (1, 4096, 32768, 102400, 262144, 1 << 20):
         assert tq.tq_attn_workspace_bytes(T, 24, 4) <= 8 << 20, T
+
+
+def test_gemm_workspace_bytes_and_alignment():
+    """The K-split workspace size (host only), and a misaligned workspace
+    rejected before any launch."""
+    assert tq.tq_gemm_workspace_bytes(4, 1000, 5120) == 0
+    assert tq.tq_gemm_workspace_bytes(16, 1000, 384) == 0          # odd group count
+    assert tq.tq_gemm_workspace_bytes(16, 1000, 2048) == 0         # one slice
+    assert tq.tq_gemm_workspace_bytes(16, 1000, 5120) == 3 * 16 * 1000 * 4
+    assert tq.tq_gemm_workspace_bytes(8, 5120, 17408) == 9 * 8 * 5120 * 4
+    assert tq.tq_gemm_workspace_bytes(16, 1000, 5120, variant=tq.TQ_BINARY) == 0
+    assert tq.tq_gemm_workspace_bytes(16, 1000, 100) == 0          # invalid K: no error
+    assert tq.tq_gemm_workspace_bytes(16, 200000, 5120) == 0       # very tall: batched kernel
+    L = tq.lib()
+    fake = 1 << 20
+    rc = L.tq_gemm_ws(fake, fake, fake, fake, 16, 1000, 5120, 128, 0, fake + 8, 1 << 20, None)
+    assert rc == 7 and b"workspace" in L.tq_last_error()

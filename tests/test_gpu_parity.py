@@ -388,3 +388,45 @@ def test_graph_replay_matches_eager():
         assert torch.equal(y, y_ref), "GEMV replay %d" % r
         assert torch.equal(Y, Y_ref), "GEMM replay %d" % r
         assert torch.equal(Y4, Y4_ref), "four-row GEMM replay %d" % r
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 1, 256), (16, 33, 256), (8, 257, 2048), (13, 300, 2304),
+                                   (16, 1000, 5120), (11, 129, 6144), (16, 65, 17408), (9, 4097, 5120),
+                                   (16, 17, 19456), (6, 2049, 4608), (16, 40, 65536)])
+def test_gemm_split_kernel(M, N, K):
+    """5..16 rows of ternary weights on the K-split kernel: one slice (K of
+    one or eight windows, Y written directly), two to thirty-two slices added
+    by the reduction kernel, ragged tiles and workgroup blocks, the largest K;
+    bit-exact on the integer set, within tolerance elsewhere."""
+    assert tq.tq_gemm_workspace_bytes(M, N, K) == (0 if K <= 2048 else
+                                                   4 * M * N * -(-(K // 256) // 8))
+    codes, s, X = case(10100 + M + N + K, N, K, M, TERN, exact=True)
+    Y = gpu_gemm(codes, s, X, TERN, N, K)
+    Yref, _ = oracle.gemm(codes, s, X, N, K, TERN, threads=THREADS)
+    assert np.array_equal(Y.astype(np.float64), Yref)
+    codes, s, X = case(10200 + M + N + K, N, K, M, TERN, exact=False)
+    Y = gpu_gemm(codes, s, X, TERN, N, K)
+    Yref, A = oracle.gemm(codes, s, X, N, K, TERN, threads=THREADS)
+    assert_tol(Y, Yref, A, "split gemm M=%d N=%d K=%d" % (M, N, K))
+
+
+def test_gemm_ws_workspace_sizes():
+    """tq_gemm_ws with the workspace it asks for, a larger one, and none (the
+    call then takes the batched kernel): the same results within the bar, and
+    bit-identical whenever the split kernel runs."""
+    M, N, K = 16, 3000, 5120
+    codes, s, X = case(10300, N, K, M, TERN, exact=False)
+    cd, sd, Xd = up(codes), up(s), up(X)
+    need = tq.tq_gemm_workspace_bytes(M, N, K)
+    assert need == 3 * M * N * 4
+    Yref, A = oracle.gemm(codes, s, X, N, K, TERN, threads=THREADS)
+    ws_exact = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws_big = torch.full((need + 4096,), 255, dtype=torch.uint8, device="cuda")
+    Y1 = tq.tq_gemm(cd, sd, Xd, workspace=ws_exact)
+    Y2 = tq.tq_gemm(cd, sd, Xd, workspace=ws_big)
+    Y3 = tq.tq_gemm(cd, sd, Xd, workspace=ws_exact[: need - 4])  # too small: batched kernel
+    Y4 = tq.tq_gemm(cd, sd, Xd)
+    torch.cuda.synchronize()
+    assert torch.equal(Y1, Y2) and torch.equal(Y1, Y4)
+    for Y in (Y1, Y3):
+        assert_tol(Y.cpu().numpy(), Yref, A, "tq_gemm_ws")
