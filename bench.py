@@ -68,6 +68,14 @@ def parse():
                    help="run only the timed step (counter runs); implies --no-cpu --no-extras")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a 1 GiB device-to-device copy, 5 times")
+    p.add_argument("--only-gemm", action="store_true",
+                   help="run only the GEMM widths 4, 16 and 64 on both MLP shapes, 20 launches each "
+                        "(counter runs)")
+    p.add_argument("--trace-summary", metavar="CSV",
+                   help="summarise a rocprofv3 kernel_trace.csv of this script's default run and exit")
+    p.add_argument("--pmc-summary", metavar="CSV", nargs="+",
+                   help="summarise rocprofv3 counter_collection.csv files (median per kernel and grid) "
+                        "and exit")
     return p.parse_args()
 
 
@@ -381,22 +389,27 @@ def stack_sweep(torch, tq, gen, stream):
     }
 
 
-def gemm_widths(torch, tq, gen, stream, bufs, slots):
+def gemm_widths(torch, tq, gen, stream, bufs, slots, widths=None, launches=50):
     """Small-batch GEMM (speculative verify / prefill widths) on gate
     (17408 x 5120, the first half of the fused buffers) and down, rotating;
-    back-to-back launches between two events."""
+    back-to-back launches between two events.  Widths that take a K-split
+    workspace get one allocated once, outside the timed launches."""
     from binary_g128_bit_amd import synth
+    if widths is None:
+        widths = (2,) + tuple(synth.GEMM_WIDTHS)
     out = {}
     for name, m, (N, K) in (("gate_17408x5120", 0, synth.GATE_UP), ("down_5120x17408", 1, synth.DOWN)):
         pool = [(c[:N], s[:N]) for c, s in (bufs[r][m] for r in range(slots))]
         X = gen.act(512, K)
         Y = torch.empty(512, N, dtype=torch.float32, device=gen.dev)
         # the configured widths and a two-row batch (the VALU kernel's width)
-        for M in (2,) + tuple(synth.GEMM_WIDTHS):
+        for M in widths:
             Xm, Ym = X[:M], Y[:M]
+            need = tq.tq_gemm_workspace_bytes(M, N, K)
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=gen.dev)
             ms = back_to_back_ms(torch, stream,
                                  lambda i: tq.tq_gemm(pool[i % len(pool)][0], pool[i % len(pool)][1],
-                                                    Xm, Ym), 50)
+                                                    Xm, Ym, workspace=ws), launches)
             tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
             gbs = packed_bytes(N, K) / (ms * 1e-3) / 1e9
             out["%s_M%d" % (name, M)] = {
@@ -657,6 +670,63 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": 5}), flush=True)
 
 
+def _csv_rows(path):
+    import csv
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def _col(row, *names):
+    for n in names:
+        if n in row:
+            return row[n]
+    raise KeyError("none of %s in %s" % (names, sorted(row)))
+
+
+def trace_summary(path):
+    """Runs of consecutive dispatches of one kernel (>= 500 long) in a
+    rocprofv3 kernel trace of the default run, in dispatch order: the first
+    long run of the fused GEMV is the back-to-back [gate;up] phase that
+    `roofline.achieved` times (its first 10 dispatches are the warm-up)."""
+    rows = _csv_rows(path)
+    rows.sort(key=lambda r: int(_col(r, "Start_Timestamp")))
+    runs = []
+    for r in rows:
+        name = _col(r, "Kernel_Name")
+        dur = int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))
+        if runs and runs[-1][0] == name:
+            runs[-1][1].append(dur)
+        else:
+            runs.append((name, [dur]))
+    print("| # | kernel | dispatches | avg us (after 10) | median us | min us |")
+    print("|---|---|---|---|---|---|")
+    for i, (name, d) in enumerate(runs):
+        if len(d) < 500:
+            continue
+        body = sorted(d[10:])
+        short = name.replace("(anonymous namespace)::", "").split("(")[0]
+        print("| %d | `%s` | %d | %.3f | %.3f | %.3f |" % (i, short, len(d), sum(body) / len(body) / 1e3,
+                                                       body[len(body) // 2] / 1e3, body[0] / 1e3))
+
+
+def pmc_summary(paths):
+    """Median counter value per (kernel, grid size) over the dispatches of
+    rocprofv3 counter_collection.csv files."""
+    import collections
+    agg = collections.OrderedDict()
+    for path in paths:
+        for r in _csv_rows(path):
+            name = _col(r, "Kernel_Name").replace("(anonymous namespace)::", "").split("(")[0]
+            key = (name, _col(r, "Grid_Size", "Grid_Size_X"))
+            agg.setdefault(key, collections.defaultdict(list))[_col(r, "Counter_Name")].append(
+                float(_col(r, "Counter_Value")))
+    for (name, grid), cs in agg.items():
+        print("%s grid=%s" % (name, grid))
+        for cn, vs in sorted(cs.items()):
+            vs.sort()
+            print("    %-28s median %.6g  (n=%d)" % (cn, vs[len(vs) // 2], len(vs)))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -665,6 +735,12 @@ def main():
         sys.exit(2)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary)
         return
     if args.only_step:
         args.no_cpu = args.no_extras = True
@@ -704,6 +780,11 @@ def main():
         for m in range(2):
             c, s = bufs[slot][m]
             tq.tq_gemv(c, s, xs[m], ys[m])
+
+    if args.only_gemm:
+        gen = Dev(torch, tq, dev, 12345)
+        print(json.dumps(gemm_widths(torch, tq, gen, stream, bufs, slots, widths=(4, 16, 64), launches=20)))
+        return
 
     log("inputs ready; warm-up")
     # ---- untimed warm-up: the W steps asked for, continued until at least

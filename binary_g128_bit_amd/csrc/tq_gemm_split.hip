@@ -127,15 +127,17 @@ __global__ __launch_bounds__(kSThreads, 2) void gemm_split_kernel(const uint8_t 
 
     // ---- 1. this thread's activation units of the slice (L2), then the
     // first PF windows' codes and scales (HBM): the staging below waits for
-    // the activations only.  Unit e = (row m, window wl, unit u16 of 16
-    // values); consecutive threads read consecutive 32-byte units of a row.
+    // the activations only.  Unit e = (unit r = 16 window + u16 of 16 values,
+    // row m = e % 16): the 16 lanes of a row group write 16 distinct LDS
+    // slots (row-major order put all 16 units of a window on one bank group),
+    // and every row's 128-byte line is read whole by 4 such groups.
     constexpr int kUnitsPerThread = 16 * kSMaxWin * 16 / kSThreads;
     const int nunits = 16 * SW * 16;
     u32x4 xlo[kUnitsPerThread], xhi[kUnitsPerThread];
 #pragma unroll
     for (int j = 0; j < kUnitsPerThread; ++j) {
         const int e = (int)threadIdx.x + j * kSThreads;
-        const int m = e / (SW * 16), r = e - m * (SW * 16);
+        const int m = e & 15, r = e >> 4;
         xlo[j] = xhi[j] = u32x4{0u, 0u, 0u, 0u};
         if (e < nunits && m < M) {
             const u32x4 *src = reinterpret_cast<const u32x4 *>(X + (size_t)m * K + (size_t)wb * 256 + 16 * r);
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(kSThreads, 2) void gemm_split_kernel(const uint8_t 
     for (int j = 0; j < kUnitsPerThread; ++j) {
         const int e = (int)threadIdx.x + j * kSThreads;
         if (e >= nunits) break;
-        const int m = e / (SW * 16), r = e - m * (SW * 16);
+        const int m = e & 15, r = e >> 4;
         const int wl = r >> 4, u16 = r & 15, g = u16 >> 3, u8 = u16 & 7;
         uint32_t pr[8];
 #pragma unroll
