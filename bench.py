@@ -684,29 +684,46 @@ def _col(row, *names):
 
 
 def trace_summary(path):
-    """Runs of consecutive dispatches of one kernel (>= 500 long) in a
-    rocprofv3 kernel trace of the default run, in dispatch order: the first
-    long run of the fused GEMV is the back-to-back [gate;up] phase that
-    `roofline.achieved` times (its first 10 dispatches are the warm-up)."""
+    """Runs of consecutive dispatches in a rocprofv3 kernel trace of the
+    default run, in dispatch order: one kernel repeated, or two kernels
+    alternating (a K-split GEMM and its reduction), at least 500 times.  The
+    first long run of the fused GEMV is the back-to-back [gate;up] phase that
+    `roofline.achieved` times.  The first 10 dispatches of a run (its
+    warm-up) are left out of the averages."""
     rows = _csv_rows(path)
     rows.sort(key=lambda r: int(_col(r, "Start_Timestamp")))
-    runs = []
-    for r in rows:
-        name = _col(r, "Kernel_Name")
-        dur = int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))
-        if runs and runs[-1][0] == name:
-            runs[-1][1].append(dur)
-        else:
-            runs.append((name, [dur]))
-    print("| # | kernel | dispatches | avg us (after 10) | median us | min us |")
-    print("|---|---|---|---|---|---|")
-    for i, (name, d) in enumerate(runs):
-        if len(d) < 500:
-            continue
+    names = [_col(r, "Kernel_Name") for r in rows]
+    durs = [int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp")) for r in rows]
+    n = len(rows)
+
+    def short(name):
+        return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+
+    def line(tag, name, d):
         body = sorted(d[10:])
-        short = name.replace("(anonymous namespace)::", "").split("(")[0]
-        print("| %d | `%s` | %d | %.3f | %.3f | %.3f |" % (i, short, len(d), sum(body) / len(body) / 1e3,
-                                                       body[len(body) // 2] / 1e3, body[0] / 1e3))
+        print("| %s | `%s` | %d | %.3f | %.3f | %.3f |" % (tag, short(name), len(d), sum(body) / len(body) / 1e3,
+                                                          body[len(body) // 2] / 1e3, body[0] / 1e3))
+
+    print("| first dispatch | kernel | dispatches | avg us | median us | min us |")
+    print("|---|---|---|---|---|---|")
+    i = 0
+    while i < n:
+        j = i
+        while j < n and names[j] == names[i]:
+            j += 1
+        if j - i >= 500:
+            line(str(i), names[i], durs[i:j])
+            i = j
+            continue
+        j = i
+        while j + 1 < n and names[j] == names[i] and names[j + 1] == names[i + 1] and names[i] != names[i + 1]:
+            j += 2
+        if (j - i) // 2 >= 500:
+            line(str(i), names[i], durs[i:j:2])
+            line("%d (alternating)" % (i + 1), names[i + 1], durs[i + 1:j:2])
+            i = j
+            continue
+        i += 1
 
 
 def pmc_summary(paths):
