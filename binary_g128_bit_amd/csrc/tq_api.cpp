@@ -136,7 +136,7 @@ int32_t tq_gemm_ws(const uint8_t *codes, const uint16_t *scales, const uint16_t 
                                                  static_cast<hipStream_t>(stream), &handled);
         if (handled || rq != TQ_OK) return rq;
     }
-    if (M >= 5 && M <= 16) {
+    if (M >= 5 && M <= 64) {
         const int32_t rs = tq::gemm_split_enqueue(codes, scales, X, Y, M, N, K, variant,
                                                   static_cast<float *>(workspace), workspace_bytes,
                                                   static_cast<hipStream_t>(stream), &handled);

@@ -1,4 +1,4 @@
-// Small-batch GEMM for 5..16 activation rows over packed ternary g128
+// Small-batch GEMM for 5..64 activation rows over packed ternary g128
 // weights on v_mfma_f32_16x16x32_f16, gfx950: K split over workgroups, each
 // workgroup's activation slice staged once in LDS.
 //
@@ -13,9 +13,9 @@
 //
 // Matrix cores.  In v_mfma_f32_16x16x32_f16 lane l supplies row l % 16 of A
 // and column l % 16 of B, eight K values each from the slice 8 (l / 16), and
-// receives D[4 (l / 16) + i][l % 16].  A is the 16 activation rows (rows past
-// M are zero), B a tile of 16 weight rows, so a decoded weight serves every
-// row of the batch.  A window is 256 weights (two scale groups, 64 code bytes
+// receives D[4 (l / 16) + i][l % 16].  A is a tile of 16 activation rows
+// (rows past M are zero; MT = 1, 2 or 4 tiles), B a tile of 16 weight rows,
+// decoded once per window and used by every activation tile.  A window is 256 weights (two scale groups, 64 code bytes
 // per row).  Lane group q loads bytes [16q, 16q + 16) of its row's window;
 // one v_permlane32_swap per dword pair then leaves lane group q 8 bytes (32
 // weights) of each group, weights [32 s, 32 s + 32) with s = (0, 2, 1, 3)[q],
@@ -32,7 +32,7 @@
 // FP32, and results by 2^14 at the end.
 //
 // Work split.  A workgroup of 8 waves owns 8 NT consecutive 16-row tiles and
-// one K slice of at most kSMaxWin windows.  It stages the slice's activations
+// one K slice of at most split_max_win(MT) windows.  It stages the slice's activations
 // (paired, in the MFMA lane order) and offset sums in LDS once; then each
 // wave runs its NT tiles over the slice's windows, the code loads running PF
 // window pairs ahead in registers (a pair is 128 code bytes of a row, both
@@ -43,9 +43,10 @@
 // device-scope release per workgroup, an L2 write-back that measured 5-9x
 // slower in total.)
 //
-// Measured (MI355X, 16 rows, back to back): 17408 x 5120 in 14.5 us,
-// 5120 x 17408 in 16.5 us, 34816 x 5120 in 25 us, against 22, 24.5 and 29 us
-// for the 16-row kernel of tq_gemm.hip.  Wave timestamps: about 3 us of each
+// Measured (MI355X, back to back): 16 rows on 17408 x 5120 in 16.5 us,
+// 5120 x 17408 in 19 us, 34816 x 5120 in 28 us, against 22, 24.5 and 29 us
+// for the per-group kernel of tq_gemm.hip; 32 rows 26.6 / 28.1 us against
+// 35.8 / 46.5; 64 rows 41 / 41 us against 48 / 45.  Wave timestamps: about 3 us of each
 // launch go to the activation slice (fetched at every launch), 1 us more to
 // the first code pairs; the window loop then streams codes at about 5 TB/s.
 #include <hip/hip_runtime.h>
@@ -66,8 +67,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kSWaves = 8;
 constexpr int kSThreads = 64 * kSWaves;
-constexpr int kSMaxWin = 8;                 // windows per K slice
-constexpr int kSWinLds = 8192 + 1024 + 128;  // LDS bytes per staged window
+constexpr int kSWinLds = 8192 + 1024 + 128;  // LDS bytes per staged window and 16-row activation tile
+// Windows per K slice by activation tiles: 74 KB of LDS for one tile (two
+// workgroups per CU), 75 KB for two, 150 KB for four (one workgroup per CU).
+__host__ __device__ constexpr int split_max_win(int mt) { return mt == 1 ? 8 : 4; }
+__host__ __device__ constexpr int split_min_wg(int mt) { return mt == 4 ? 1 : 2; }
 constexpr float kSInvUnit = 16384.0f;
 
 __device__ __forceinline__ uint32_t svreg(uint32_t v) {
@@ -100,25 +104,25 @@ __device__ __forceinline__ constexpr uint32_t sslot_w(int p) {
     return (p == 0 || p == 3) ? 0x14401440u : (p == 1 || p == 4 || p == 6) ? 0x0D000D00u : 0x04000400u;
 }
 
-// LDS layout of a slice of SW windows (u32x4 units):
-//   xf   [SW][2 groups][4 chunks][64 lanes]  A fragments: chunk c of lane
+// LDS layout of a slice of SW windows and MT activation tiles of 16 rows
+// (u32x4 units):
+//   xf   [SW][2 groups][MT][4 chunks][64 lanes]  A fragments: chunk c of lane
 //        (m, q) holds pair dwords 4c..4c+3 of its 32 weights of the group
-//        (unit 2 s + c / 2, pairs 4 (c % 2) .. 4 (c % 2) + 3);
-//   cpart [SW][2][8 units][16 rows] float   per-unit offset sums;
-//   cneg  [SW][2][16 rows] float            -C per group and row.
-template <int NT, int PF>
-__global__ __launch_bounds__(kSThreads, 2) void gemm_split_kernel(const uint8_t *__restrict__ codes,
-                                                                  const uint16_t *__restrict__ scales,
-                                                                  const uint16_t *__restrict__ X,
-                                                                  float *__restrict__ Y, float *__restrict__ ws,
-                                                                  int M, int N, int K, int KS) {
+//        (unit 2 s + c / 2, pairs 4 (c % 2) .. 4 (c % 2) + 3) for row 16u + m;
+//   cpart [SW][2][8 units][16 MT rows] float   per-unit offset sums;
+//   cneg  [SW][2][16 MT rows] float            -C per group and row.
+template <int NT, int PF, int MT>
+__global__ __launch_bounds__(kSThreads, split_min_wg(MT)) void gemm_split_kernel(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, const uint16_t *__restrict__ X,
+    float *__restrict__ Y, float *__restrict__ ws, int M, int N, int K, int KS) {
+    constexpr int MR = 16 * MT;  // staged activation rows
     extern __shared__ u32x4 slds[];
     const int G = K >> 7, W = G >> 1;
     const int ks = blockIdx.y;
-    const int wb = ks * W / KS, SW = (ks + 1) * W / KS - wb;  // this slice's windows (1..kSMaxWin)
+    const int wb = ks * W / KS, SW = (ks + 1) * W / KS - wb;  // this slice's windows
     u32x4 *xf = slds;
-    float *cpart = reinterpret_cast<float *>(slds + SW * 512);
-    float *cneg = cpart + SW * 256;
+    float *cpart = reinterpret_cast<float *>(slds + SW * MT * 512);
+    float *cneg = cpart + SW * MT * 256;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -128,16 +132,16 @@ __global__ __launch_bounds__(kSThreads, 2) void gemm_split_kernel(const uint8_t 
     // ---- 1. this thread's activation units of the slice (L2), then the
     // first PF windows' codes and scales (HBM): the staging below waits for
     // the activations only.  Unit e = (unit r = 16 window + u16 of 16 values,
-    // row m = e % 16): the 16 lanes of a row group write 16 distinct LDS
+    // row m = e % MR): the 16 lanes of a row group write 16 distinct LDS
     // slots (row-major order put all 16 units of a window on one bank group),
     // and every row's 128-byte line is read whole by 4 such groups.
-    constexpr int kUnitsPerThread = 16 * kSMaxWin * 16 / kSThreads;
-    const int nunits = 16 * SW * 16;
+    constexpr int kUnitsPerThread = MR * split_max_win(MT) * 16 / kSThreads;
+    const int nunits = MR * SW * 16;
     u32x4 xlo[kUnitsPerThread], xhi[kUnitsPerThread];
 #pragma unroll
     for (int j = 0; j < kUnitsPerThread; ++j) {
         const int e = (int)threadIdx.x + j * kSThreads;
-        const int m = e & 15, r = e >> 4;
+        const int m = e % MR, r = e / MR;
         xlo[j] = xhi[j] = u32x4{0u, 0u, 0u, 0u};
         if (e < nunits && m < M) {
             const u32x4 *src = reinterpret_cast<const u32x4 *>(X + (size_t)m * K + (size_t)wb * 256 + 16 * r);
@@ -183,8 +187,9 @@ __global__ __launch_bounds__(kSThreads, 2) void gemm_split_kernel(const uint8_t 
     for (int j = 0; j < kUnitsPerThread; ++j) {
         const int e = (int)threadIdx.x + j * kSThreads;
         if (e >= nunits) break;
-        const int m = e & 15, r = e >> 4;
+        const int m = e % MR, r = e / MR;
         const int wl = r >> 4, u16 = r & 15, g = u16 >> 3, u8 = u16 & 7;
+        const int ut = m >> 4, mm = m & 15;  // activation tile, row in it
         uint32_t pr[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -193,7 +198,7 @@ __global__ __launch_bounds__(kSThreads, 2) void gemm_split_kernel(const uint8_t 
             pr[2 * i + 1] = __builtin_amdgcn_perm(xhi[j][i], xlo[j][i], 0x07060302u);  // (x_2i+1, x_2i+9)
         }
         const int sg = u8 >> 1, qq = ((sg & 1) << 1) | (sg >> 1), c0 = 2 * (u8 & 1);
-        u32x4 *dst = xf + ((wl * 2 + g) * 4 + c0) * 64 + 16 * qq + m;
+        u32x4 *dst = xf + (((wl * 2 + g) * MT + ut) * 4 + c0) * 64 + 16 * qq + mm;
         dst[0] = u32x4{pr[0], pr[1], pr[2], pr[3]};
         dst[64] = u32x4{pr[4], pr[5], pr[6], pr[7]};
         float c = 0.0f;
@@ -201,14 +206,14 @@ __global__ __launch_bounds__(kSThreads, 2) void gemm_split_kernel(const uint8_t 
         for (int p = 0; p < 8; ++p)
             c = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, pr[p]), __builtin_bit_cast(half2_t, sslot_w(p)),
                                        c, false);
-        cpart[((wl * 2 + g) * 8 + u8) * 16 + m] = c;
+        cpart[((wl * 2 + g) * 8 + u8) * MR + m] = c;
     }
     __syncthreads();
-    for (int e = (int)threadIdx.x; e < SW * 32; e += kSThreads) {
-        const float *src = cpart + (e >> 4) * 128 + (e & 15);
+    for (int e = (int)threadIdx.x; e < SW * 2 * MR; e += kSThreads) {
+        const float *src = cpart + (e / MR) * 8 * MR + e % MR;
         float c = 0.0f;
 #pragma unroll
-        for (int u = 0; u < 8; ++u) c += src[16 * u];
+        for (int u = 0; u < 8; ++u) c += src[MR * u];
         cneg[e] = -c;
     }
     __syncthreads();
@@ -217,9 +222,11 @@ __global__ __launch_bounds__(kSThreads, 2) void gemm_split_kernel(const uint8_t 
     // only reload its last pair (the loads stay unconditional, so the
     // compiler's waits are exact)
     const uint32_t m8 = svreg(0x03000300u), m6 = svreg(0x00C000C0u);
-    f32x4 acc[NT];
+    f32x4 acc[NT][MT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int u = 0; u < MT; ++u) acc[t][u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int w0 = 0; w0 < NPR; w0 += PF) {
 #pragma unroll
         for (int p = 0; p < PF; ++p) {
@@ -254,22 +261,37 @@ __global__ __launch_bounds__(kSThreads, 2) void gemm_split_kernel(const uint8_t 
                 }
 #pragma unroll
                 for (int g = 0; g < 2; ++g) {
-                    const u32x4 *af = xf + (wl * 2 + g) * 256 + lane;
-                    const u32x4 a0 = af[0], a1 = af[64], a2 = af[128], a3 = af[192];
-                    const f32x4 cn = *reinterpret_cast<const f32x4 *>(cneg + (wl * 2 + g) * 16 + 4 * q);
+                    // each tile's weights decoded once, used by every activation tile
+                    uint32_t wd[NT][16];
+                    float sc[NT];
 #pragma unroll
                     for (int t = 0; t < NT; ++t) {
                         uint32_t wa[8], wq[8];
                         sdecode(gd[t][g][0], m8, m6, wa);
                         sdecode(gd[t][g][1], m8, m6, wq);
-                        f32x4 D = cn;
-                        D = mfma16(a0, u32x4{wa[0], wa[1], wa[2], wa[3]}, D);
-                        D = mfma16(a1, u32x4{wa[4], wa[5], wa[6], wa[7]}, D);
-                        D = mfma16(a2, u32x4{wq[0], wq[1], wq[2], wq[3]}, D);
-                        D = mfma16(a3, u32x4{wq[4], wq[5], wq[6], wq[7]}, D);
-                        const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)(g ? svp[t][h] >> 16 : svp[t][h]));
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[t][i] = __builtin_fmaf(s, D[i], acc[t][i]);
+                        for (int i = 0; i < 8; ++i) {
+                            wd[t][i] = wa[i];
+                            wd[t][8 + i] = wq[i];
+                        }
+                        sc[t] = (float)__builtin_bit_cast(_Float16, (uint16_t)(g ? svp[t][h] >> 16 : svp[t][h]));
+                    }
+#pragma unroll
+                    for (int u = 0; u < MT; ++u) {
+                        const u32x4 *af = xf + ((wl * 2 + g) * MT + u) * 256 + lane;
+                        const u32x4 a0 = af[0], a1 = af[64], a2 = af[128], a3 = af[192];
+                        const f32x4 cn =
+                            *reinterpret_cast<const f32x4 *>(cneg + (wl * 2 + g) * MR + 16 * u + 4 * q);
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) {
+                            f32x4 D = cn;
+                            D = mfma16(a0, u32x4{wd[t][0], wd[t][1], wd[t][2], wd[t][3]}, D);
+                            D = mfma16(a1, u32x4{wd[t][4], wd[t][5], wd[t][6], wd[t][7]}, D);
+                            D = mfma16(a2, u32x4{wd[t][8], wd[t][9], wd[t][10], wd[t][11]}, D);
+                            D = mfma16(a3, u32x4{wd[t][12], wd[t][13], wd[t][14], wd[t][15]}, D);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) acc[t][u][i] = __builtin_fmaf(sc[t], D[i], acc[t][u][i]);
+                        }
                     }
                 }
             }
@@ -283,10 +305,12 @@ __global__ __launch_bounds__(kSThreads, 2) void gemm_split_kernel(const uint8_t 
     for (int t = 0; t < NT; ++t) {
         const int row = 16 * (tile0 + t) + n;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int m = 4 * q + i;
-            if (m < M && row < N) dst[(size_t)m * N + row] = acc[t][i] * kSInvUnit;
-        }
+        for (int u = 0; u < MT; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * u + 4 * q + i;
+                if (m < M && row < N) dst[(size_t)m * N + row] = acc[t][u][i] * kSInvUnit;
+            }
     }
 }
 
@@ -302,16 +326,17 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float *__restri
 
 struct SplitPlan {
     bool ok = false;
-    int nt = 0;
+    int nt = 0, mt = 0;
     int64_t nblk = 0, kslices = 0;
     size_t ws_bytes = 0;
 };
 
-// 5 <= M <= 16 ternary with an even group count, N <= 131072 and 32-bit
-// buffer offsets.  Shape: two tiles per wave, and the fewest K slices of at most kSMaxWin
-// windows (more slices measured slower: every workgroup pays the activation
-// staging).  TQ_GEMM_SPLIT = "off" disables the kernel, "NT,KS" fixes the
-// shape (for measurements).
+// 5 <= M <= 64 ternary with an even group count, N <= 131072 and 32-bit
+// buffer offsets; MT = 1, 2 or 4 activation tiles of 16 rows.  Shape: two
+// weight tiles per wave, and the fewest K slices that fit LDS (more slices
+// measured slower: every workgroup pays the activation staging).
+// TQ_GEMM_SPLIT = "off" disables the kernel, "NT,KS" fixes the shape (for
+// measurements).
 SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int32_t variant) {
     static const int forced_nt = [] {
         const char *v = getenv("TQ_GEMM_SPLIT");
@@ -324,15 +349,17 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int32_t variant) {
         return c ? atoi(c + 1) : 0;
     }();
     SplitPlan pl;
-    if (forced_nt < 0 || variant != TQ_TERNARY || M < 5 || M > 16 || K < 256 || (K / 128) % 2) return pl;
+    if (forced_nt < 0 || variant != TQ_TERNARY || M < 5 || M > 64 || K < 256 || (K / 128) % 2) return pl;
     const int64_t W = K / 256, ntiles = (N + 15) / 16;
     // very tall matrices keep the batched kernel of tq_gemm.hip: on the
     // 248320-row head with 8 rows it ran 113 us against 127 us here, the
     // staging and the K-split partials growing with N
     if (forced_nt == 0 && N > 131072) return pl;
+    pl.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
     pl.nt = forced_nt == 1 ? 1 : 2;
     pl.nblk = (ntiles + kSWaves * pl.nt - 1) / (kSWaves * pl.nt);
-    const int64_t ks_min = (W + kSMaxWin - 1) / kSMaxWin;
+    const int64_t maxw = split_max_win(pl.mt);
+    const int64_t ks_min = (W + maxw - 1) / maxw;
     pl.kslices = std::min<int64_t>(W, std::max<int64_t>(ks_min, forced_ks));
     if (pl.nblk * kSWaves * pl.nt * 16 * (K / 4) >= (int64_t(1) << 31)) return pl;
     if (pl.kslices * M * N >= (int64_t(1) << 31)) return pl;
@@ -361,13 +388,22 @@ int32_t gemm_split_enqueue(const uint8_t *codes, const uint16_t *scales, const u
     *handled = true;
     const int64_t W = K / 256;
     const int64_t sw_max = (W + pl.kslices - 1) / pl.kslices;
-    const size_t lds = (size_t)sw_max * kSWinLds;
+    const size_t lds = (size_t)sw_max * pl.mt * kSWinLds;
     const dim3 grid((unsigned)pl.nblk, (unsigned)pl.kslices), block(kSThreads);
     const int m = (int)M, n = (int)N, k = (int)K, kk = (int)pl.kslices;
-    if (pl.nt == 2)
-        hipLaunchKernelGGL((gemm_split_kernel<2, 2>), grid, block, lds, stream, codes, scales, X, Y, ws, m, n, k, kk);
-    else
-        hipLaunchKernelGGL((gemm_split_kernel<1, 2>), grid, block, lds, stream, codes, scales, X, Y, ws, m, n, k, kk);
+#define TQ_SPLIT(NT_, MT_)                                                                                   \
+    hipLaunchKernelGGL((gemm_split_kernel<NT_, 2, MT_>), grid, block, lds, stream, codes, scales, X, Y, ws, m, \
+                       n, k, kk)
+    if (pl.nt == 2) {
+        if (pl.mt == 1) TQ_SPLIT(2, 1);
+        else if (pl.mt == 2) TQ_SPLIT(2, 2);
+        else TQ_SPLIT(2, 4);
+    } else {
+        if (pl.mt == 1) TQ_SPLIT(1, 1);
+        else if (pl.mt == 2) TQ_SPLIT(1, 2);
+        else TQ_SPLIT(1, 4);
+    }
+#undef TQ_SPLIT
     hipError_t e = hipGetLastError();
     if (e == hipSuccess && kk > 1) {
         const int mn = m * n;

@@ -285,6 +285,8 @@ def test_gemm_workspace_bytes_and_alignment():
     assert tq.tq_gemm_workspace_bytes(16, 1000, 5120, variant=tq.TQ_BINARY) == 0
     assert tq.tq_gemm_workspace_bytes(16, 1000, 100) == 0          # invalid K: no error
     assert tq.tq_gemm_workspace_bytes(16, 200000, 5120) == 0       # very tall: batched kernel
+    assert tq.tq_gemm_workspace_bytes(64, 1000, 5120) == 5 * 64 * 1000 * 4
+    assert tq.tq_gemm_workspace_bytes(65, 1000, 5120) == 0
     L = tq.lib()
     fake = 1 << 20
     rc = L.tq_gemm_ws(fake, fake, fake, fake, 16, 1000, 5120, 128, 0, fake + 8, 1 << 20, None)

@@ -392,14 +392,18 @@ def test_graph_replay_matches_eager():
 
 @pytest.mark.parametrize("M,N,K", [(5, 1, 256), (16, 33, 256), (8, 257, 2048), (13, 300, 2304),
                                    (16, 1000, 5120), (11, 129, 6144), (16, 65, 17408), (9, 4097, 5120),
-                                   (16, 17, 19456), (6, 2049, 4608), (16, 40, 65536)])
+                                   (16, 17, 19456), (6, 2049, 4608), (16, 40, 65536),
+                                   (17, 33, 1024), (32, 1000, 5120), (29, 257, 2304), (33, 300, 5120),
+                                   (64, 65, 17408), (48, 4097, 5120), (64, 17, 65536), (61, 129, 1280)])
 def test_gemm_split_kernel(M, N, K):
-    """5..16 rows of ternary weights on the K-split kernel: one slice (K of
-    one or eight windows, Y written directly), two to thirty-two slices added
-    by the reduction kernel, ragged tiles and workgroup blocks, the largest K;
-    bit-exact on the integer set, within tolerance elsewhere."""
-    assert tq.tq_gemm_workspace_bytes(M, N, K) == (0 if K <= 2048 else
-                                                   4 * M * N * -(-(K // 256) // 8))
+    """5..64 rows of ternary weights on the K-split kernel (one, two or four
+    16-row activation tiles): one slice (Y written directly), two to sixty-four
+    slices added by the reduction kernel, ragged tiles, activation tiles and
+    workgroup blocks, the largest K; bit-exact on the integer set, within
+    tolerance elsewhere."""
+    win = 8 if M <= 16 else 4
+    slices = -(-(K // 256) // win)
+    assert tq.tq_gemm_workspace_bytes(M, N, K) == (0 if slices == 1 else 4 * M * N * slices)
     codes, s, X = case(10100 + M + N + K, N, K, M, TERN, exact=True)
     Y = gpu_gemm(codes, s, X, TERN, N, K)
     Yref, _ = oracle.gemm(codes, s, X, N, K, TERN, threads=THREADS)
