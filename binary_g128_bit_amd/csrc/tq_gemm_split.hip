@@ -45,8 +45,8 @@
 //
 // Measured (MI355X, back to back): 16 rows on 17408 x 5120 in 16.5 us,
 // 5120 x 17408 in 19 us, 34816 x 5120 in 28 us, against 22, 24.5 and 29 us
-// for the per-group kernel of tq_gemm.hip; 32 rows 26.6 / 28.1 us against
-// 35.8 / 46.5; 64 rows 41 / 41 us against 48 / 45.  Wave timestamps: about 3 us of each
+// for the per-group kernel of tq_gemm.hip; 32 rows 22.4 / 24.0 us against
+// 35.8 / 46.5; 64 rows 32.5 / 32.3 us against 48 / 45.  Wave timestamps: about 3 us of each
 // launch go to the activation slice (fetched at every launch), 1 us more to
 // the first code pairs; the window loop then streams codes at about 5 TB/s.
 #include <hip/hip_runtime.h>
@@ -332,9 +332,9 @@ struct SplitPlan {
 };
 
 // 5 <= M <= 64 ternary with an even group count, N <= 131072 and 32-bit
-// buffer offsets; MT = 1, 2 or 4 activation tiles of 16 rows.  Shape: two
-// weight tiles per wave, and the fewest K slices that fit LDS (more slices
-// measured slower: every workgroup pays the activation staging).
+// buffer offsets; MT = 1, 2 or 4 activation tiles of 16 rows.  Shape: the
+// fewest K slices that fit LDS (more slices measured slower: every
+// workgroup pays the activation staging).
 // TQ_GEMM_SPLIT = "off" disables the kernel, "NT,KS" fixes the shape (for
 // measurements).
 SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int32_t variant) {
@@ -356,7 +356,11 @@ SplitPlan split_plan(int64_t M, int64_t N, int64_t K, int32_t variant) {
     // staging and the K-split partials growing with N
     if (forced_nt == 0 && N > 131072) return pl;
     pl.mt = M <= 16 ? 1 : M <= 32 ? 2 : 4;
-    pl.nt = forced_nt == 1 ? 1 : 2;
+    // two weight tiles per wave for one activation tile, three for two or
+    // four: with the VGPRs these take, one workgroup runs per CU, and three
+    // tiles keep the MLP shapes to one round of workgroups (32 / 64 rows on
+    // 17408 x 5120: 22.4 / 32.5 us against 26.5 / 41.2 with two tiles)
+    pl.nt = forced_nt >= 1 && forced_nt <= 4 ? forced_nt : pl.mt == 1 ? 2 : 3;
     pl.nblk = (ntiles + kSWaves * pl.nt - 1) / (kSWaves * pl.nt);
     const int64_t maxw = split_max_win(pl.mt);
     const int64_t ks_min = (W + maxw - 1) / maxw;
@@ -398,6 +402,14 @@ int32_t gemm_split_enqueue(const uint8_t *codes, const uint16_t *scales, const u
         if (pl.mt == 1) TQ_SPLIT(2, 1);
         else if (pl.mt == 2) TQ_SPLIT(2, 2);
         else TQ_SPLIT(2, 4);
+    } else if (pl.nt == 3) {
+        if (pl.mt == 1) TQ_SPLIT(3, 1);
+        else if (pl.mt == 2) TQ_SPLIT(3, 2);
+        else TQ_SPLIT(3, 4);
+    } else if (pl.nt == 4) {
+        if (pl.mt == 1) TQ_SPLIT(4, 1);
+        else if (pl.mt == 2) TQ_SPLIT(4, 2);
+        else TQ_SPLIT(4, 4);
     } else {
         if (pl.mt == 1) TQ_SPLIT(1, 1);
         else if (pl.mt == 2) TQ_SPLIT(1, 2);
