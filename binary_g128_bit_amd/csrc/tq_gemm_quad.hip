@@ -73,6 +73,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kQWaves = 16;            // waves per workgroup
 constexpr int kQThreads = 64 * kQWaves;
 constexpr int kQPrefetch = 4;          // chunk items in flight per wave
+constexpr int kQRing = kQPrefetch + 1;  // ring slots: one spare, see the item loop
 constexpr int kQMaxLds = 163840;       // bytes of LDS a gfx950 workgroup may use
 constexpr int kQRows = 4;              // activation rows staged (M <= 4)
 constexpr float kUnit = 6.103515625e-05f;  // 2^-14
@@ -81,6 +82,12 @@ constexpr float kInvUnit = 16384.0f;
 __device__ __forceinline__ uint32_t vreg(uint32_t v) {
     asm volatile("" : "+v"(v));
     return v;
+}
+
+// Pins four values in registers at this point (no contraction or sinking
+// across it).
+__device__ __forceinline__ void fbar4(float (&v)[4]) {
+    asm volatile("" : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]));
 }
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -256,14 +263,12 @@ struct StageX {
 template <int VARIANT, typename Code>
 __device__ __forceinline__ f32x4 item_mma(const Code &cw, const u32x4 (&xa)[8], f32x4 sd, uint32_t m8,
                                           uint32_t m6, const BinMasks &bk) {
-    f32x4 D0 = sd;
-    f32x4 D1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 D = sd;
     if constexpr (VARIANT == TQ_TERNARY) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             uint32_t w[8];
             tern_decode(cw[u], m8, m6, w);
-            f32x4 &D = (u & 1) ? D1 : D0;
             D = mfma4(xa[2 * u][0], xa[2 * u][1], w[0], w[1], D);
             D = mfma4(xa[2 * u][2], xa[2 * u][3], w[2], w[3], D);
             D = mfma4(xa[2 * u + 1][0], xa[2 * u + 1][1], w[4], w[5], D);
@@ -276,13 +281,12 @@ __device__ __forceinline__ f32x4 item_mma(const Code &cw, const u32x4 (&xa)[8], 
             bin_decode(cw[u], bk, w);
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
-                f32x4 &D = (h & 1) ? D1 : D0;
                 D = mfma4(xa[4 * u + h][0], xa[4 * u + h][1], w[4 * h], w[4 * h + 1], D);
                 D = mfma4(xa[4 * u + h][2], xa[4 * u + h][3], w[4 * h + 2], w[4 * h + 3], D);
             }
         }
     }
-    return D0 + D1;
+    return D;
 }
 
 // Kernel.  CPR: 64-weight chunks per row; capc: CPR rounded up to 16 (chunk
@@ -336,8 +340,8 @@ __global__ __launch_bounds__(kQThreads) void gemm_quad_kernel(const uint8_t *__r
         __builtin_amdgcn_make_buffer_rsrc((void *)codes, 0, N * row_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t srs =
         __builtin_amdgcn_make_buffer_rsrc((void *)scales, 0, N * G * 2, 0x00020000);
-    Code ring[kQPrefetch];
-    uint32_t sring[kQPrefetch];
+    Code ring[kQRing];
+    uint32_t sring[kQRing];
     // issue pointer: (group i, block lb) of the next item to load, advanced
     // in i-major order and held at the last item once the range is spent
     int ii = nb > 0 ? it0 / nb : 0, il = nb > 0 ? it0 - ii * nb : 0, left = nit;
@@ -372,22 +376,26 @@ __global__ __launch_bounds__(kQThreads) void gemm_quad_kernel(const uint8_t *__r
     __syncthreads();
 
     // ---- items: lane 4b+j decodes weight row 4 blk + j at chunk b + 16 i and
-    // supplies activation row j of that chunk.  The body is unconditional
-    // (items past the range recompute the last one and store nothing): with
-    // loads under a branch the compiler merges the ring registers with moves
-    // at the loop latch, which wait for every load in flight.
+    // supplies activation row j of that chunk.  The loads are unconditional
+    // (loads under a branch made the compiler merge the ring registers with
+    // moves at the loop latch, which wait for every load in flight); only
+    // the compute of the last round's items past the range is skipped.
     const uint32_t m8 = vreg(0x03000300u), m6 = vreg(0x00C000C0u);
     const BinMasks bk;
     int cur_i = -1;
     u32x4 xa[8];
     f32x4 sd = {0.0f, 0.0f, 0.0f, 0.0f};
-    const int nit_pad = (nit + kQPrefetch - 1) / kQPrefetch * kQPrefetch;
     int i = nb > 0 ? it0 / nb : 0, lb = nb > 0 ? it0 - i * nb : 0;  // compute pointer
-    for (int t0 = 0; t0 < nit_pad; t0 += kQPrefetch) {
+    // Item p of an unrolled round reads slot p and refills slot p - 1, read
+    // by the item before: the load never targets a register still in use, so
+    // the slots keep their registers across the loop latch.  (With the
+    // refill in the slot being read, the scheduler hoists the load above the
+    // decode, and the ring rotates through register moves at the latch that
+    // wait for every load in flight.)
+    for (int t0 = 0; t0 < nit; t0 += kQRing) {
 #pragma unroll
-        for (int p = 0; p < kQPrefetch; ++p) {
+        for (int p = 0; p < kQRing; ++p) {
             const int t = t0 + p;
-            const bool live = t < nit;
             if (i != cur_i) {  // wave-uniform: a new chunk group's activations and seeds
                 const int c = b + 16 * i;
 #pragma unroll
@@ -397,24 +405,34 @@ __global__ __launch_bounds__(kQThreads) void gemm_quad_kernel(const uint8_t *__r
             }
             const Code cw = ring[p];
             const float s = half_bits(sring[p]);
-            issue(p);
-            const f32x4 D = item_mma<VARIANT>(cw, xa, sd, m8, m6, bk);
-            float v[4];
+            issue((p + kQRing - 1) % kQRing);
+            if (t < nit) {  // wave-uniform: the last round's items past the range only load
+                const f32x4 D = item_mma<VARIANT>(cw, xa, sd, m8, m6, bk);
+                // the scaled partial stays a separate product (no contraction
+                // into the adds) and the sum is formed before the store branch,
+                // so that each add takes its cross-lane operand as a DPP source
+                float v[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                v[r] = s * D[r];
-                v[r] += dpp_f<0x124>(v[r]);  // row_ror:4
-                v[r] += dpp_f<0x128>(v[r]);  // row_ror:8
-                if (RP <= 2) v[r] += __shfl_xor(v[r], 16);
-                if (RP == 1) v[r] += __shfl_xor(v[r], 32);
-            }
-            // lanes 0-3 of each (RP = 4) or every other (RP = 2) 16-lane row
-            // hold their rows' sums for weight row j
-            const int grp = lane >> 4;
-            if (live && (lane & 15) < 4 && (RP == 4 || (RP == 2 && (grp & 1) == 0) || grp == 0)) {
-                float *dst = part + ((size_t)(i * nb + lb) * RP + (RP == 4 ? grp : grp >> 1)) * 16;
+                for (int r = 0; r < 4; ++r) v[r] = s * D[r];
+                fbar4(v);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) dst[r * 4 + q4] = v[r];
+                for (int r = 0; r < 4; ++r) v[r] += dpp_f<0x124>(v[r]);  // row_ror:4
+#pragma unroll
+                for (int r = 0; r < 4; ++r) v[r] += dpp_f<0x128>(v[r]);  // row_ror:8
+                fbar4(v);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    if (RP <= 2) v[r] += __shfl_xor(v[r], 16);
+                    if (RP == 1) v[r] += __shfl_xor(v[r], 32);
+                }
+                // lanes 0-3 of each (RP = 4) or every other (RP = 2) 16-lane
+                // row hold their rows' sums for weight row j
+                const int grp = lane >> 4;
+                if ((lane & 15) < 4 && (RP == 4 || (RP == 2 && (grp & 1) == 0) || grp == 0)) {
+                    float *dst = part + ((size_t)(i * nb + lb) * RP + (RP == 4 ? grp : grp >> 1)) * 16;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) dst[r * 4 + q4] = v[r];
+                }
             }
             if (t + 1 < nit && ++lb == nb) {  // next item (held at the last one)
                 lb = 0;
