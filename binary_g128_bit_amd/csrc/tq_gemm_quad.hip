@@ -192,6 +192,19 @@ __device__ __forceinline__ float dpp_f(float v) {
                                                                  true));
 }
 
+// v + (v of the lane W = 16 or 32 away, within 2W-lane groups), as
+// v_permlane16/32_swap of v with itself: the swap leaves the lane's own value
+// in one result and its partner's in the other (even 16-lane rows or the
+// lower half: own value first), so the sum is the one a lane-xor shuffle
+// gives, without the LDS crossbar.
+template <int W>
+__device__ __forceinline__ float swap_sum(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto e = W == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                           : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)e[0]) + __builtin_bit_cast(float, (uint32_t)e[1]);
+}
+
 // Stage X into LDS: one 16- or 32-weight unit per work item, the units of a
 // chunk on consecutive threads, activation row m, chunk c; pairs as the
 // decode produces them and each (row, chunk) seed.  Every thread of the
@@ -422,8 +435,8 @@ __global__ __launch_bounds__(kQThreads) void gemm_quad_kernel(const uint8_t *__r
                 fbar4(v);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    if (RP <= 2) v[r] += __shfl_xor(v[r], 16);
-                    if (RP == 1) v[r] += __shfl_xor(v[r], 32);
+                    if (RP <= 2) v[r] = swap_sum<16>(v[r]);
+                    if (RP == 1) v[r] = swap_sum<32>(v[r]);
                 }
                 // lanes 0-3 of each (RP = 4) or every other (RP = 2) 16-lane
                 // row hold their rows' sums for weight row j

@@ -322,12 +322,14 @@ def test_gemm_zero_rows_and_special_scales(M):
 
 @pytest.mark.parametrize("variant", [TERN, BIN])
 @pytest.mark.parametrize("M,N,K", [(3, 1, 128), (4, 5, 640), (4, 4097, 5120), (3, 33, 19456),
-                                   (4, 7, 19584), (2, 1030, 1152), (4, 248, 17408)])
+                                   (4, 7, 19584), (2, 1030, 1152), (4, 248, 17408), (4, 2000, 19456)])
 def test_gemm_four_row_mfma_kernel(M, N, K, variant):
     """Batches of 3 and 4 rows (and two-row 1-bit batches) take the 4-row MFMA
     kernel: one weight row, a ragged chunk-group tail (K = 640), many blocks
     per workgroup, the largest K whose activations fit LDS (19456) and the
-    first that does not (19584, another kernel)."""
+    first that does not (19584, another kernel).  Item partials are summed
+    over 4, 2 (N = 33 at K = 19456) or 1 (N = 2000 at K = 19456) row groups
+    before they go to LDS, by the LDS space left beside the activations."""
     codes, s, X = case(9870 + M + N + K, N, K, M, variant, exact=True)
     Y = gpu_gemm(codes, s, X, variant, N, K)
     Yref, _ = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
