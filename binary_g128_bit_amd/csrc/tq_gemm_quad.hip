@@ -49,11 +49,15 @@
 // stored to LDS per row group; at the end the partials of each block are
 // added in a fixed order (deterministic) and stored.
 //
-// Measured on the MLP shapes (MI355X, same box): M = 4 on 17408 x 5120 takes
-// 11.5 us against 13.6 us for the MFMA stage kernel, 1.5x less on the
-// 248320-row head; per item the VALU (decode, 40 ops) and the 16 MFMA issues
-// cost about 460 cycles per SIMD, and about 4 us of each launch go before the
-// first item (the first code loads' latency, behind which X is staged).
+// Measured on the MLP shapes (MI355X, same box, back to back): M = 4 on
+// 17408 x 5120 takes 10.2 us and on 5120 x 17408 12.2 us, against 8.1 /
+// 8.2 us for the batch-1 GEMV.  Wave timestamps (17408 x 5120 / 5120 x
+// 17408): the items start 3.3 / 4.5 us into the launch, after the staging
+// and its barrier; a wave's item takes about 0.6 us of its time with 4 waves
+// per SIMD, the decode (40 VALU ops), the sums (13) and the 16 MFMA issues.
+// Loading each lane's own fragment instead of staging (no barrier) measured
+// 35 % slower: every 16-byte load then touches 64 cache lines, and the
+// fragments shared by two waves are read twice.
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
@@ -382,11 +386,16 @@ __global__ __launch_bounds__(kQThreads) void gemm_quad_kernel(const uint8_t *__r
             }
         }
     };
+    // half the ring before the staging, half after its barrier: with the
+    // whole ring in flight the code stream (most of a short range) competes
+    // with the activation reads that every item waits for
 #pragma unroll
-    for (int p = 0; p < kQPrefetch; ++p) issue(p);
+    for (int p = 0; p < kQPrefetch / 2; ++p) issue(p);
 
     sx.store(xs, seeds, capc);
     __syncthreads();
+#pragma unroll
+    for (int p = kQPrefetch / 2; p < kQPrefetch; ++p) issue(p);
 
     // ---- items: lane 4b+j decodes weight row 4 blk + j at chunk b + 16 i and
     // supplies activation row j of that chunk.  The loads are unconditional
