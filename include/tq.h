@@ -159,8 +159,9 @@ int32_t tq_gemm(const uint8_t *codes, const uint16_t *scales, const uint16_t *X,
 
 /* Host.  Bytes of device workspace tq_gemm_ws can use for this shape: the
  * partial products of a K split (the product of tq_gemm, same passages), for
- * 5 <= M <= 16 ternary weights with an even group count; 0 when the shape
- * takes no workspace or the arguments are invalid (no error is recorded). */
+ * 5 <= M <= 64 ternary weights with an even group count and N <= 131072
+ * rows; 0 when the shape takes no workspace (or a K split into one slice) or
+ * the arguments are invalid (no error is recorded). */
 size_t tq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group,
                                int32_t variant);
 
@@ -169,7 +170,7 @@ size_t tq_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t group,
  * "Throughput and speculative decoding") with a caller-owned workspace:
  * workspace is device memory, 16-byte aligned, of workspace_bytes bytes
  * (NULL / 0 allowed).  With at least tq_gemm_workspace_bytes(...) bytes,
- * 5..16-row ternary batches take a K-split kernel whose slices are added in a
+ * 5..64-row ternary batches take a K-split kernel whose slices are added in a
  * fixed order; with less, the call behaves as tq_gemm.  The workspace is
  * overwritten and in use until the work enqueued on `stream` completes:
  * calls that share one workspace must be ordered (the same stream).
