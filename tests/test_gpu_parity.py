@@ -436,3 +436,28 @@ def test_gemm_ws_workspace_sizes():
     assert torch.equal(Y1, Y2) and torch.equal(Y1, Y4)
     for Y in (Y1, Y3):
         assert_tol(Y.cpu().numpy(), Yref, A, "tq_gemm_ws")
+
+
+@pytest.mark.parametrize("M,N,K", [(32, 300, 5120), (64, 257, 17408), (16, 3000, 5120), (13, 129, 6144)])
+def test_gemm_split_reduce_paths(M, N, K):
+    """The slice reduction reads and writes four outputs per thread from five
+    slices up when M * N is a multiple of 4 and Y is 16-byte aligned (5 slices
+    at 32 x 5120, 17 = two batches of eight and one at 64 x 17408), else one
+    (3 slices, or M * N odd): an output view one float into a buffer (4-byte
+    aligned) takes the one-output path, with the same sums in the same order,
+    so the bits are equal."""
+    codes, s, X = case(10400 + M + N, N, K, M, TERN, exact=False)
+    cd, sd, Xd = up(codes), up(s), up(X)
+    need = tq.tq_gemm_workspace_bytes(M, N, K)
+    assert need > 0
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    Ya = torch.empty(M, N, dtype=torch.float32, device="cuda")
+    buf = torch.empty(M * N + 1, dtype=torch.float32, device="cuda")
+    Yb = buf[1:].view(M, N)
+    assert Yb.data_ptr() % 16 == 4
+    tq.tq_gemm(cd, sd, Xd, Ya, workspace=ws)
+    tq.tq_gemm(cd, sd, Xd, Yb, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Ya, Yb)
+    Yref, A = oracle.gemm(codes, s, X, N, K, TERN, threads=THREADS)
+    assert_tol(Ya.cpu().numpy(), Yref, A, "split reduce paths")
