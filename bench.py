@@ -7,7 +7,9 @@ same activation, so they are stored as one 34816 x 5120 matrix (rows of gate,
 then rows of up) and run as one GEMV launch; down is a second launch.  Both go
 through the C ABI.  Weights rotate over >= 1 GiB of distinct device buffers so
 that no step reads from the 256 MB last-level cache what the previous one left
-there.  Inputs are resident in HBM before the timed region starts.
+there.  Inputs are resident in HBM before the timed region starts, and the K
+timed steps are enqueued behind a spin kernel, so that the events around them
+time their GPU work back to back rather than the host's launch latency.
 
 Prints ONE JSON line: packed-weight GB/s (value), % of the 8 TB/s HBM peak,
 the roofline object of the dominant kernel (its launches timed one by one with
@@ -272,6 +274,18 @@ def back_to_back_ms(torch, stream, launch, n, warm=10, batches=20):
     torch.cuda.synchronize()
     per = sorted(a.elapsed_time(b) / n for a, b in ev)
     return per[len(per) // 2]
+
+
+def spin_cycles_per_ms(torch, stream, cycles=200000):
+    """Cycles of torch.cuda._sleep per millisecond on this GPU, timed with
+    events (the spin counts the shader clock, whose rate the events measure)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(cycles)
+    e0.record(stream)
+    torch.cuda._sleep(cycles)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return cycles / max(e0.elapsed_time(e1), 1e-3)
 
 
 def graph_ms(torch, launch, n, replays=5):
@@ -818,12 +832,24 @@ def main():
     warmup_ms = (time.perf_counter() - t0) * 1e3
     warmup_steps = w
 
-    # ---- timed region: K steps over rotating buffers
+    # ---- timed region: K steps over rotating buffers.  A short spin kernel
+    # holds the stream while the host starts enqueueing the K steps (two
+    # launches each from Python), so that the events time the GPU's work on
+    # the steps back to back, not the host's first launches.  The host
+    # enqueues a step faster than the GPU runs one, so a head start keeps it
+    # ahead; the JSON reports both rates.  (A spin as long as the whole
+    # enqueue, milliseconds on one CU with the rest idle, let the clocks
+    # drop: 21.0 against 18.5 us per step over 300 steps.)
+    cycles_per_ms = spin_cycles_per_ms(torch, stream)
+    prime_ms = 0.6
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(int(prime_ms * cycles_per_ms))
+    t_enq = time.perf_counter()
     e0.record(stream)
     for k in range(args.steps):
         step(k % slots)
     e1.record(stream)
+    enqueue_ms = (time.perf_counter() - t_enq) * 1e3
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
@@ -869,6 +895,12 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "warmup_run": {"steps": warmup_steps, "ms": round(warmup_ms, 1)},
+        "timed_region": {"steps": args.steps, "events": "on the launch stream around the K steps",
+                         "queue_primed_ms": round(prime_ms, 3),
+                         "host_us_per_step": round(enqueue_ms * 1e3 / args.steps, 3),
+                         "gpu_us_per_step": round(ms_per_step * 1e3, 3),
+                         "host_ahead": bool(enqueue_ms < prime_ms + ms_per_step * args.steps and
+                                            enqueue_ms / args.steps < ms_per_step)},
         "ms_per_step": round(ms_per_step, 6),
         "higher_is_better": True,
         "scaling": "weak",
