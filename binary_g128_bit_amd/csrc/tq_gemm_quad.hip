@@ -1,4 +1,4 @@
-// Small-batch GEMM for M <= 4 activation rows over packed ternary / binary
+// Small-batch GEMM for M <= 8 activation rows over packed ternary / binary
 // g128 weights, gfx950.
 //
 // Y[m][n] = sum_g s[n][g] * sum_{j<128} t[n][128g+j] * X[m][128g+j]
@@ -19,7 +19,9 @@
 // Lane 4b+j therefore reads activation row j & 3 and decodes weight row j & 3
 // of its block; the 16 products of one instruction are 16 different 16-byte
 // code chunks (columns) of the same 4 weight rows, so one 16-byte load per
-// lane reads 4 rows x 256 contiguous bytes.
+// lane reads 4 rows x 256 contiguous bytes.  For 5..8 rows a second row set
+// (activation rows 4..7) takes a second chain of products on the same
+// decoded weights, so the decode is paid once for 8 rows.
 //
 // Decode (exact).  As in the batch-1 GEMV: ternary codes placed in FP16
 // exponent / mantissa bits are linear in the code (E: c 2^-14; M4: 2^-12 +
@@ -76,10 +78,11 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kQWaves = 16;            // waves per workgroup
 constexpr int kQThreads = 64 * kQWaves;
-constexpr int kQPrefetch = 4;          // chunk items in flight per wave
-constexpr int kQRing = kQPrefetch + 1;  // ring slots: one spare, see the item loop
+// chunk items in flight per wave: four with one row set, three with two
+// (whose second set of activation registers leaves no room for a fourth)
+constexpr int q_prefetch(int MR) { return MR == 1 ? 4 : 3; }
 constexpr int kQMaxLds = 163840;       // bytes of LDS a gfx950 workgroup may use
-constexpr int kQRows = 4;              // activation rows staged (M <= 4)
+constexpr int kQRows = 4;              // activation rows per MFMA operand (a row set)
 constexpr float kUnit = 6.103515625e-05f;  // 2^-14
 constexpr float kInvUnit = 16384.0f;
 
@@ -138,10 +141,11 @@ struct QFmt<TQ_BINARY> {
 
 // LDS position (in 16-byte pieces) of piece q of chunk slot (m, c).  A slot
 // is 8 pieces, half the 64 banks.  The 16 lanes served together read chunks
-// c0..c0+3 of activation rows 0..3: (c & 1) picks the half and the XOR key
-// m + 4 ((c >> 1) & 1) spreads the 8 lanes that share it.
+// c0..c0+3 of the 4 activation rows of one row set: (c & 1) picks the half
+// and the XOR key (m & 3) + 4 ((c >> 1) & 1) spreads the 8 lanes that share
+// it.
 __device__ __forceinline__ int piece_at(int m, int c, int q, int capc) {
-    return (m * capc + c) * 8 + (q ^ (m + 4 * ((c >> 1) & 1)));
+    return (m * capc + c) * 8 + (q ^ ((m & 3) + 4 * ((c >> 1) & 1)));
 }
 
 // The 16 ternary weights of code dword d as 8 pair dwords w[p], p = 0..7.
@@ -216,8 +220,9 @@ __device__ __forceinline__ float swap_sum(float v) {
 // Staged activation units of one thread: UMAX units of 16 (ternary) or 32
 // (binary) weights, activation row m, chunk c; the units of a chunk sit on
 // consecutive threads.
-template <int VARIANT, int UMAX>
+template <int VARIANT, int UMAX, int MR>
 struct StageX {
+    static constexpr int ROWS = kQRows * MR;              // staged activation rows
     using F = QFmt<VARIANT>;
     static constexpr int UPC = F::kWeights / F::kUnit;  // units per chunk: 4 or 2
     static constexpr int V4 = F::kUnit / 8;             // 16-byte loads per unit
@@ -227,11 +232,11 @@ struct StageX {
     // every load first: they are issued before the code prologue, so the
     // wait for them does not cover the code stream
     __device__ __forceinline__ void load(const uint16_t *__restrict__ X, int M, int K, int CPR, int capc) {
-        const int units = kQRows * capc * UPC;
+        const int units = ROWS * capc * UPC;
 #pragma unroll
         for (int k = 0; k < UMAX; ++k) {
             const int uu = k * kQThreads + (int)threadIdx.x;
-            const int u = uu % UPC, mc = min(uu / UPC, kQRows * capc - 1);
+            const int u = uu % UPC, mc = min(uu / UPC, ROWS * capc - 1);
             const int m = mc / capc, c = mc % capc;
             const bool real = uu < units && m < M && c < CPR;
             const u32x4 *src = reinterpret_cast<const u32x4 *>(X + (size_t)min(m, M - 1) * K +
@@ -241,14 +246,15 @@ struct StageX {
         }
     }
 
-    // pairs as the decode produces them and each (row, chunk) seed into LDS;
-    // every thread runs it (the seed sum is a cross-lane op)
+    // pairs as the decode produces them and each (row, chunk) seed into LDS
+    // (seeds[set][chunk], one f32x4 for the set's 4 rows); every thread runs
+    // it (the seed sum is a cross-lane op)
     __device__ __forceinline__ void store(u32x4 *xs, f32x4 *seeds, int capc) const {
-        const int units = kQRows * capc * UPC;
+        const int units = ROWS * capc * UPC;
 #pragma unroll
         for (int k = 0; k < UMAX; ++k) {
             const int uu = k * kQThreads + (int)threadIdx.x;
-            const int u = uu % UPC, mc = min(uu / UPC, kQRows * capc - 1);
+            const int u = uu % UPC, mc = min(uu / UPC, ROWS * capc - 1);
             const int m = mc / capc, c = mc % capc;
             uint32_t xp[HP];
 #pragma unroll
@@ -267,29 +273,33 @@ struct StageX {
                 for (int i = 0; i < HP / 4; ++i)
                     xs[piece_at(m, c, u * (HP / 4) + i, capc)] =
                         u32x4{xp[4 * i], xp[4 * i + 1], xp[4 * i + 2], xp[4 * i + 3]};
-                if (u == 0) reinterpret_cast<float *>(seeds)[c * 4 + m] = -z * kUnit;
+                if (u == 0) reinterpret_cast<float *>(seeds)[((m >> 2) * capc + c) * 4 + (m & 3)] = -z * kUnit;
             }
         }
     }
 };
 
-// One item's 16 MFMAs: the chunk's 64 decoded weights of this lane's row
-// against its activation pairs xa, the chain started from the seeds sd.
-// Returns D = 2^-14 sum t x for the 4 activation rows (register i) of this
-// lane's weight row.
-template <int VARIANT, typename Code>
-__device__ __forceinline__ f32x4 item_mma(const Code &cw, const u32x4 (&xa)[8], f32x4 sd, uint32_t m8,
-                                          uint32_t m6, const BinMasks &bk) {
-    f32x4 D = sd;
+// One item's 16 MFMAs per row set: the chunk's 64 decoded weights of this
+// lane's row against each set's activation pairs xa[set], each chain started
+// from its set's seeds.  D[set] = 2^-14 sum t x for the set's 4 activation
+// rows (register i) of this lane's weight row; the decode is paid once for
+// all sets.
+template <int VARIANT, int MR, typename Code>
+__device__ __forceinline__ void item_mma(const Code &cw, const u32x4 (&xa)[MR][8], const f32x4 (&sd)[MR],
+                                         uint32_t m8, uint32_t m6, const BinMasks &bk, f32x4 (&D)[MR]) {
+#pragma unroll
+    for (int s = 0; s < MR; ++s) D[s] = sd[s];
     if constexpr (VARIANT == TQ_TERNARY) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             uint32_t w[8];
             tern_decode(cw[u], m8, m6, w);
-            D = mfma4(xa[2 * u][0], xa[2 * u][1], w[0], w[1], D);
-            D = mfma4(xa[2 * u][2], xa[2 * u][3], w[2], w[3], D);
-            D = mfma4(xa[2 * u + 1][0], xa[2 * u + 1][1], w[4], w[5], D);
-            D = mfma4(xa[2 * u + 1][2], xa[2 * u + 1][3], w[6], w[7], D);
+#pragma unroll
+            for (int h = 0; h < 4; ++h)
+#pragma unroll
+                for (int s = 0; s < MR; ++s)
+                    D[s] = mfma4(xa[s][2 * u + h / 2][2 * (h % 2)], xa[s][2 * u + h / 2][2 * (h % 2) + 1], w[2 * h],
+                                 w[2 * h + 1], D[s]);
         }
     } else {
 #pragma unroll
@@ -297,13 +307,13 @@ __device__ __forceinline__ f32x4 item_mma(const Code &cw, const u32x4 (&xa)[8], 
             uint32_t w[16];
             bin_decode(cw[u], bk, w);
 #pragma unroll
-            for (int h = 0; h < 4; ++h) {
-                D = mfma4(xa[4 * u + h][0], xa[4 * u + h][1], w[4 * h], w[4 * h + 1], D);
-                D = mfma4(xa[4 * u + h][2], xa[4 * u + h][3], w[4 * h + 2], w[4 * h + 3], D);
-            }
+            for (int h = 0; h < 8; ++h)
+#pragma unroll
+                for (int s = 0; s < MR; ++s)
+                    D[s] = mfma4(xa[s][4 * u + h / 2][2 * (h % 2)], xa[s][4 * u + h / 2][2 * (h % 2) + 1], w[2 * h],
+                                 w[2 * h + 1], D[s]);
         }
     }
-    return D;
 }
 
 // Kernel.  CPR: 64-weight chunks per row; capc: CPR rounded up to 16 (chunk
@@ -319,7 +329,7 @@ __device__ __forceinline__ f32x4 item_mma(const Code &cw, const u32x4 (&xa)[8], 
 // Codes and scales are read through buffer descriptors: an offset past the
 // matrix returns zeros, so rows past N (the last block) need no clamp, and
 // chunk slots past a ragged row read bytes that meet zero activations.
-template <int VARIANT, int UMAX, int RP>
+template <int VARIANT, int UMAX, int RP, int MR>
 __global__ __launch_bounds__(kQThreads) void gemm_quad_kernel(const uint8_t *__restrict__ codes,
                                                               const uint16_t *__restrict__ scales,
                                                               const uint16_t *__restrict__ X,
@@ -331,9 +341,10 @@ __global__ __launch_bounds__(kQThreads) void gemm_quad_kernel(const uint8_t *__r
     const int CPR = K >> 6;
     const int capc = (CPR + 15) & ~15;
     const int NI = capc >> 4;
-    u32x4 *xs = lds;                                                   // [4][capc][8 pieces]
-    f32x4 *seeds = reinterpret_cast<f32x4 *>(lds + kQRows * capc * 8);  // [capc]
-    float *part = reinterpret_cast<float *>(seeds + capc);            // [NI][blocks][RP][16]
+    constexpr int PW = 16 * MR;  // partial floats per item and row group
+    u32x4 *xs = lds;                                                         // [4 MR][capc][8 pieces]
+    f32x4 *seeds = reinterpret_cast<f32x4 *>(lds + kQRows * MR * capc * 8);  // [MR][capc]
+    float *part = reinterpret_cast<float *>(seeds + MR * capc);             // [NI][blocks][RP][PW]
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -348,7 +359,7 @@ __global__ __launch_bounds__(kQThreads) void gemm_quad_kernel(const uint8_t *__r
 
     // ---- activation loads first (L2), then this wave's first code chunks
     // (HBM), so that the staging below waits for the activations only
-    StageX<VARIANT, UMAX> sx;
+    StageX<VARIANT, UMAX, MR> sx;
     sx.load(X, M, K, CPR, capc);
 
     constexpr int CB = sizeof(Code);  // code bytes per chunk
@@ -357,6 +368,8 @@ __global__ __launch_bounds__(kQThreads) void gemm_quad_kernel(const uint8_t *__r
         __builtin_amdgcn_make_buffer_rsrc((void *)codes, 0, N * row_bytes, 0x00020000);
     const __amdgpu_buffer_rsrc_t srs =
         __builtin_amdgcn_make_buffer_rsrc((void *)scales, 0, N * G * 2, 0x00020000);
+    constexpr int kQPrefetch = q_prefetch(MR);
+    constexpr int kQRing = kQPrefetch + 1;  // ring slots: one spare, see the item loop
     Code ring[kQRing];
     uint32_t sring[kQRing];
     // issue pointer: (group i, block lb) of the next item to load, advanced
@@ -405,8 +418,8 @@ __global__ __launch_bounds__(kQThreads) void gemm_quad_kernel(const uint8_t *__r
     const uint32_t m8 = vreg(0x03000300u), m6 = vreg(0x00C000C0u);
     const BinMasks bk;
     int cur_i = -1;
-    u32x4 xa[8];
-    f32x4 sd = {0.0f, 0.0f, 0.0f, 0.0f};
+    u32x4 xa[MR][8];
+    f32x4 sd[MR];
     int i = nb > 0 ? it0 / nb : 0, lb = nb > 0 ? it0 - i * nb : 0;  // compute pointer
     // Item p of an unrolled round reads slot p and refills slot p - 1, read
     // by the item before: the load never targets a register still in use, so
@@ -421,39 +434,48 @@ __global__ __launch_bounds__(kQThreads) void gemm_quad_kernel(const uint8_t *__r
             if (i != cur_i) {  // wave-uniform: a new chunk group's activations and seeds
                 const int c = b + 16 * i;
 #pragma unroll
-                for (int q = 0; q < 8; ++q) xa[q] = xs[piece_at(q4, c, q, capc)];
-                sd = seeds[c];
+                for (int rs = 0; rs < MR; ++rs) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) xa[rs][q] = xs[piece_at(4 * rs + q4, c, q, capc)];
+                    sd[rs] = seeds[rs * capc + c];
+                }
                 cur_i = i;
             }
             const Code cw = ring[p];
             const float s = half_bits(sring[p]);
             issue((p + kQRing - 1) % kQRing);
             if (t < nit) {  // wave-uniform: the last round's items past the range only load
-                const f32x4 D = item_mma<VARIANT>(cw, xa, sd, m8, m6, bk);
+                f32x4 D[MR];
+                item_mma<VARIANT, MR>(cw, xa, sd, m8, m6, bk, D);
                 // the scaled partial stays a separate product (no contraction
                 // into the adds) and the sum is formed before the store branch,
                 // so that each add takes its cross-lane operand as a DPP source
-                float v[4];
+                float v[MR][4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] = s * D[r];
-                fbar4(v);
+                for (int rs = 0; rs < MR; ++rs) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] += dpp_f<0x124>(v[r]);  // row_ror:4
+                    for (int r = 0; r < 4; ++r) v[rs][r] = s * D[rs][r];
+                    fbar4(v[rs]);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) v[r] += dpp_f<0x128>(v[r]);  // row_ror:8
-                fbar4(v);
+                    for (int r = 0; r < 4; ++r) v[rs][r] += dpp_f<0x124>(v[rs][r]);  // row_ror:4
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (RP <= 2) v[r] = swap_sum<16>(v[r]);
-                    if (RP == 1) v[r] = swap_sum<32>(v[r]);
+                    for (int r = 0; r < 4; ++r) v[rs][r] += dpp_f<0x128>(v[rs][r]);  // row_ror:8
+                    fbar4(v[rs]);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (RP <= 2) v[rs][r] = swap_sum<16>(v[rs][r]);
+                        if (RP == 1) v[rs][r] = swap_sum<32>(v[rs][r]);
+                    }
                 }
                 // lanes 0-3 of each (RP = 4) or every other (RP = 2) 16-lane
                 // row hold their rows' sums for weight row j
                 const int grp = lane >> 4;
                 if ((lane & 15) < 4 && (RP == 4 || (RP == 2 && (grp & 1) == 0) || grp == 0)) {
-                    float *dst = part + ((size_t)(i * nb + lb) * RP + (RP == 4 ? grp : grp >> 1)) * 16;
+                    float *dst = part + ((size_t)(i * nb + lb) * RP + (RP == 4 ? grp : grp >> 1)) * PW;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) dst[r * 4 + q4] = v[r];
+                    for (int rs = 0; rs < MR; ++rs)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) dst[rs * 16 + r * 4 + q4] = v[rs][r];
                 }
             }
             if (t + 1 < nit && ++lb == nb) {  // next item (held at the last one)
@@ -465,14 +487,15 @@ __global__ __launch_bounds__(kQThreads) void gemm_quad_kernel(const uint8_t *__r
     __syncthreads();
 
     // ---- per (block, activation row, weight row): the partials in a fixed order
-    for (int e = (int)threadIdx.x; e < nb * 16; e += kQThreads) {
-        const int lb = e >> 4, m = (e >> 2) & 3, j = e & 3;
+    for (int e = (int)threadIdx.x; e < nb * PW; e += kQThreads) {
+        const int lb = e / PW, w = e % PW;  // w = 16 set + 4 (row in set) + weight row
+        const int m = 4 * (w >> 4) + ((w >> 2) & 3), j = w & 3;
         const int row = 4 * (blk0 + lb) + j;
         float y = 0.0f;
         for (int i = 0; i < NI; ++i) {
-            const float *src = part + (size_t)(i * nb + lb) * RP * 16;
+            const float *src = part + (size_t)(i * nb + lb) * RP * PW;
 #pragma unroll
-            for (int g = 0; g < RP; ++g) y += src[g * 16 + m * 4 + j];
+            for (int g = 0; g < RP; ++g) y += src[g * PW + w];
         }
         if (m < M && row < N) Y[(size_t)m * N + row] = y * kInvUnit;
     }
@@ -480,10 +503,10 @@ __global__ __launch_bounds__(kQThreads) void gemm_quad_kernel(const uint8_t *__r
 
 }  // namespace
 
-// LDS bytes of the staged activations and seeds for K.
-size_t gemm_quad_stage_lds(int64_t K) {
+// LDS bytes of the staged activations and seeds of MR row sets for K.
+size_t gemm_quad_stage_lds(int64_t K, int MR) {
     const int64_t capc = (K / 64 + 15) / 16 * 16;
-    return (size_t)(kQRows * capc * 8 * 16 + capc * 16);
+    return (size_t)(MR * (kQRows * capc * 8 * 16 + capc * 16));
 }
 
 int device_cu_count() {
@@ -498,23 +521,24 @@ int device_cu_count() {
     return cache[dev];
 }
 
-// M <= 4 on the quad kernel when the staged activations and at least one
-// block's partials fit LDS and the packed matrix is below 2^31 bytes (32-bit
-// buffer offsets); *handled is false otherwise.  Blocks are dealt to
-// workgroups evenly, as many per workgroup as their partials fit beside the
-// activations, in whole rounds of one workgroup per CU.  Four row-group
-// partials per item when they fit at one round, else two.
-template <int VARIANT, int UMAX>
+// M <= 8 on the quad kernel (one row set for M <= 4, two for 5..8) when the
+// staged activations and at least one block's partials fit LDS (two sets:
+// in one round of workgroups) and the packed matrix is below 2^31 bytes
+// (32-bit buffer offsets); *handled is false otherwise.  Blocks are dealt to workgroups evenly, as many per
+// workgroup as their partials fit beside the activations, in whole rounds of
+// one workgroup per CU.  Four row-group partials per item when they fit at
+// one round, else two, else one.
+template <int VARIANT, int UMAX, int MR>
 hipError_t launch_quad(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y, int M, int N,
                        int K, int rp, int grid, int bpw, size_t lds, hipStream_t stream) {
     if (rp == 4)
-        hipLaunchKernelGGL((gemm_quad_kernel<VARIANT, UMAX, 4>), dim3(grid), dim3(kQThreads), lds, stream, codes,
+        hipLaunchKernelGGL((gemm_quad_kernel<VARIANT, UMAX, 4, MR>), dim3(grid), dim3(kQThreads), lds, stream, codes,
                            scales, X, Y, M, N, K, bpw);
     else if (rp == 2)
-        hipLaunchKernelGGL((gemm_quad_kernel<VARIANT, UMAX, 2>), dim3(grid), dim3(kQThreads), lds, stream, codes,
+        hipLaunchKernelGGL((gemm_quad_kernel<VARIANT, UMAX, 2, MR>), dim3(grid), dim3(kQThreads), lds, stream, codes,
                            scales, X, Y, M, N, K, bpw);
     else
-        hipLaunchKernelGGL((gemm_quad_kernel<VARIANT, UMAX, 1>), dim3(grid), dim3(kQThreads), lds, stream, codes,
+        hipLaunchKernelGGL((gemm_quad_kernel<VARIANT, UMAX, 1, MR>), dim3(grid), dim3(kQThreads), lds, stream, codes,
                            scales, X, Y, M, N, K, bpw);
     return hipGetLastError();
 }
@@ -522,16 +546,17 @@ hipError_t launch_quad(const uint8_t *codes, const uint16_t *scales, const uint1
 int32_t gemm_quad_enqueue(const uint8_t *codes, const uint16_t *scales, const uint16_t *X, float *Y,
                           int64_t M, int64_t N, int64_t K, int32_t variant, hipStream_t stream, bool *handled) {
     *handled = false;
-    if (M < 1 || M > kQRows || (variant != TQ_TERNARY && variant != TQ_BINARY)) return TQ_OK;
+    if (M < 1 || M > 2 * kQRows || (variant != TQ_TERNARY && variant != TQ_BINARY)) return TQ_OK;
+    const int MR = M <= kQRows ? 1 : 2;
     const int64_t cpr = K / 64, capc = (cpr + 15) / 16 * 16, NI = capc / 16;
     if (N * cpr * (variant == TQ_TERNARY ? 16 : 8) >= (int64_t(1) << 31)) return TQ_OK;
-    const int64_t stage = (int64_t)gemm_quad_stage_lds(K);
+    const int64_t stage = (int64_t)gemm_quad_stage_lds(K, MR);
     const int64_t nblocks = (N + 3) / 4;
     const int64_t cus = device_cu_count();
     int rp = 0;
     int64_t grid = 0, bpw = 0;
     for (int try_rp : {4, 2, 1}) {
-        const int64_t per_block = NI * try_rp * 64;
+        const int64_t per_block = NI * try_rp * 64 * MR;
         if (stage + per_block > kQMaxLds) continue;
         const int64_t max_b = (kQMaxLds - stage) / per_block;
         int64_t g = cus;
@@ -542,28 +567,42 @@ int32_t gemm_quad_enqueue(const uint8_t *codes, const uint16_t *scales, const ui
         break;
     }
     if (!rp) return TQ_OK;
+    // Two row sets only in one round of workgroups: on the 248320-row head
+    // (two rounds, re-staging the activations) they measured 112 / 112 us at
+    // M = 5 / 8 against 101 / 108 us for the per-group MFMA kernel
+    if (MR == 2 && grid > cus) return TQ_OK;
     *handled = true;
     if (grid > nblocks) grid = nblocks;
     bpw = (nblocks + grid - 1) / grid;
     grid = (nblocks + bpw - 1) / bpw;
-    const size_t lds = (size_t)(stage + bpw * NI * rp * 64);
+    const size_t lds = (size_t)(stage + bpw * NI * rp * 64 * MR);
     const int64_t upc = variant == TQ_TERNARY ? 4 : 2;
-    const int64_t umax = (kQRows * capc * upc + kQThreads - 1) / kQThreads;
+    const int64_t umax = (kQRows * MR * capc * upc + kQThreads - 1) / kQThreads;
     if (umax > (variant == TQ_TERNARY ? 5 : 3)) {  // unreachable while the stage fits LDS
         *handled = false;
         return TQ_OK;
     }
     hipError_t e = hipErrorInvalidValue;
     const int m = (int)M, n = (int)N, k = (int)K, g = (int)grid, bb = (int)bpw;
-#define TQ_QL(V, U) e = launch_quad<V, U>(codes, scales, X, Y, m, n, k, rp, g, bb, lds, stream)
+#define TQ_QL(V, U, R) e = launch_quad<V, U, R>(codes, scales, X, Y, m, n, k, rp, g, bb, lds, stream)
     // the staged activations fit LDS, so a thread stages at most 5 ternary
     // (16-weight) or 3 binary (32-weight) units
     if (variant == TQ_TERNARY) {
-        if (umax <= 2) TQ_QL(TQ_TERNARY, 2);
-        else TQ_QL(TQ_TERNARY, 5);
+        if (MR == 1) {
+            if (umax <= 2) TQ_QL(TQ_TERNARY, 2, 1);
+            else TQ_QL(TQ_TERNARY, 5, 1);
+        } else {
+            if (umax <= 3) TQ_QL(TQ_TERNARY, 3, 2);
+            else TQ_QL(TQ_TERNARY, 5, 2);
+        }
     } else {
-        if (umax <= 1) TQ_QL(TQ_BINARY, 1);
-        else TQ_QL(TQ_BINARY, 3);
+        if (MR == 1) {
+            if (umax <= 1) TQ_QL(TQ_BINARY, 1, 1);
+            else TQ_QL(TQ_BINARY, 3, 1);
+        } else {
+            if (umax <= 2) TQ_QL(TQ_BINARY, 2, 2);
+            else TQ_QL(TQ_BINARY, 3, 2);
+        }
     }
 #undef TQ_QL
     if (e != hipSuccess) return fail(TQ_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));

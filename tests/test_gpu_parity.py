@@ -211,7 +211,7 @@ def _sampled_rows(N, n, seed):
     return rows
 
 
-@pytest.mark.parametrize("M", [2, 4, 16, 64, 512])
+@pytest.mark.parametrize("M", [2, 4, 8, 16, 64, 512])
 @pytest.mark.parametrize("N,K", [synth.GATE_UP, synth.DOWN])
 def test_gemm_full_size_sampled(M, N, K):
     """Speculative-verify / prefill widths on the MLP shapes: the full GEMM on
@@ -338,6 +338,26 @@ def test_gemm_four_row_mfma_kernel(M, N, K, variant):
     Y = gpu_gemm(codes, s, X, variant, N, K)
     Yref, A = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
     assert_tol(Y, Yref, A, "four-row gemm M=%d N=%d K=%d" % (M, N, K))
+
+
+@pytest.mark.parametrize("variant", [TERN, BIN])
+@pytest.mark.parametrize("M,N,K", [(5, 1, 128), (8, 5, 640), (6, 4097, 5120), (8, 33, 9216),
+                                   (7, 7, 9728), (8, 32000, 5120), (8, 70000, 5120)])
+def test_gemm_four_row_kernel_two_sets(M, N, K, variant):
+    """Batches of 5 to 8 rows take the 4-row MFMA kernel with two row sets
+    (one decode per weight for both) while both sets' activations fit LDS:
+    one weight row, a ragged chunk-group tail, many blocks per workgroup, the
+    largest K that fits (9216), the first that does not (9728: the K-split
+    kernel), and two (N = 32000) or one (N = 70000) row-group partials per
+    item."""
+    codes, s, X = case(9890 + M + N + K, N, K, M, variant, exact=True)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, _ = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert np.array_equal(Y.astype(np.float64), Yref)
+    codes, s, X = case(9900 + M + N + K, N, K, M, variant, exact=False)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, A = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert_tol(Y, Yref, A, "two-set four-row gemm M=%d N=%d K=%d" % (M, N, K))
 
 
 def test_gemm_deterministic():
