@@ -410,13 +410,14 @@ def gemm_widths(torch, tq, gen, stream, bufs, slots, widths=None, launches=50):
     workspace get one allocated once, outside the timed launches."""
     from binary_g128_bit_amd import synth
     if widths is None:
-        widths = (2,) + tuple(synth.GEMM_WIDTHS)
+        # the configured widths, a two-row batch (the VALU kernel's width) and
+        # eight rows (the four-row kernel's two row sets)
+        widths = tuple(sorted({2, 8} | set(synth.GEMM_WIDTHS)))
     out = {}
     for name, m, (N, K) in (("gate_17408x5120", 0, synth.GATE_UP), ("down_5120x17408", 1, synth.DOWN)):
         pool = [(c[:N], s[:N]) for c, s in (bufs[r][m] for r in range(slots))]
         X = gen.act(512, K)
         Y = torch.empty(512, N, dtype=torch.float32, device=gen.dev)
-        # the configured widths and a two-row batch (the VALU kernel's width)
         for M in widths:
             Xm, Ym = X[:M], Y[:M]
             need = tq.tq_gemm_workspace_bytes(M, N, K)
