@@ -71,7 +71,7 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a 1 GiB device-to-device copy, 5 times")
     p.add_argument("--only-gemm", action="store_true",
-                   help="run only the GEMM widths 4, 16 and 64 on both MLP shapes, 20 launches each "
+                   help="run only the GEMM widths 4, 8, 16 and 64 on both MLP shapes, 20 launches each "
                         "(counter runs)")
     p.add_argument("--trace-summary", metavar="CSV",
                    help="summarise a rocprofv3 kernel_trace.csv of this script's default run and exit")
@@ -698,42 +698,52 @@ def _col(row, *names):
     raise KeyError("none of %s in %s" % (names, sorted(row)))
 
 
-def trace_summary(path):
+def trace_summary(path, min_run=90):
     """Runs of consecutive dispatches in a rocprofv3 kernel trace of the
     default run, in dispatch order: one kernel repeated, or two kernels
-    alternating (a K-split GEMM and its reduction), at least 500 times.  The
+    alternating (a K-split GEMM and its reduction, or decode attention's two
+    launches), at least min_run times.  The
     first long run of the fused GEMV is the back-to-back [gate;up] phase that
     `roofline.achieved` times.  The first 10 dispatches of a run (its
     warm-up) are left out of the averages."""
     rows = _csv_rows(path)
     rows.sort(key=lambda r: int(_col(r, "Start_Timestamp")))
-    names = [_col(r, "Kernel_Name") for r in rows]
+
+    def grid_of(r):
+        for c in ("Grid_Size_X", "Grid_Size"):
+            if c in r:
+                return r[c]
+        return ""
+
+    # a run is keyed by kernel and grid: launches of one kernel at different
+    # sizes (batch widths, context lengths) are separate runs
+    names = [(_col(r, "Kernel_Name"), grid_of(r)) for r in rows]
     durs = [int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp")) for r in rows]
     n = len(rows)
 
     def short(name):
         return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
 
-    def line(tag, name, d):
+    def line(tag, key, d):
         body = sorted(d[10:])
-        print("| %s | `%s` | %d | %.3f | %.3f | %.3f |" % (tag, short(name), len(d), sum(body) / len(body) / 1e3,
-                                                          body[len(body) // 2] / 1e3, body[0] / 1e3))
+        print("| %s | `%s` | %d | %.3f | %.3f | %.3f | %s |" % (tag, short(key[0]), len(d), sum(body) / len(body) / 1e3,
+                                                               body[len(body) // 2] / 1e3, body[0] / 1e3, key[1]))
 
-    print("| first dispatch | kernel | dispatches | avg us | median us | min us |")
-    print("|---|---|---|---|---|---|")
+    print("| first dispatch | kernel | dispatches | avg us | median us | min us | grid |")
+    print("|---|---|---|---|---|---|---|")
     i = 0
     while i < n:
         j = i
         while j < n and names[j] == names[i]:
             j += 1
-        if j - i >= 500:
+        if j - i >= min_run:
             line(str(i), names[i], durs[i:j])
             i = j
             continue
         j = i
         while j + 1 < n and names[j] == names[i] and names[j + 1] == names[i + 1] and names[i] != names[i + 1]:
             j += 2
-        if (j - i) // 2 >= 500:
+        if (j - i) // 2 >= min_run:
             line(str(i), names[i], durs[i:j:2])
             line("%d (alternating)" % (i + 1), names[i + 1], durs[i + 1:j:2])
             i = j
@@ -743,17 +753,27 @@ def trace_summary(path):
 
 def pmc_summary(paths):
     """Median counter value per (kernel, grid size) over the dispatches of
-    rocprofv3 counter_collection.csv files."""
+    rocprofv3 counter_collection.csv files.  A dispatch directly followed by
+    a slice reduction is also keyed by that reduction's grid, which tells
+    apart batch widths that share a kernel and grid."""
     import collections
     agg = collections.OrderedDict()
     for path in paths:
-        for r in _csv_rows(path):
+        rows = list(_csv_rows(path))
+        kernels = {}
+        for r in rows:
             name = _col(r, "Kernel_Name").replace("(anonymous namespace)::", "").split("(")[0]
-            key = (name, _col(r, "Grid_Size", "Grid_Size_X"))
+            kernels[int(_col(r, "Dispatch_Id"))] = (name, _col(r, "Grid_Size", "Grid_Size_X"))
+        for r in rows:
+            d = int(_col(r, "Dispatch_Id"))
+            name, grid = kernels[d]
+            nxt = kernels.get(d + 1)
+            then = nxt[1] if nxt and "reduce" in nxt[0] and "reduce" not in name else None
+            key = (name, grid, then)
             agg.setdefault(key, collections.defaultdict(list))[_col(r, "Counter_Name")].append(
                 float(_col(r, "Counter_Value")))
-    for (name, grid), cs in agg.items():
-        print("%s grid=%s" % (name, grid))
+    for (name, grid, then), cs in agg.items():
+        print("%s grid=%s%s" % (name, grid, " then-reduce-grid=%s" % then if then else ""))
         for cn, vs in sorted(cs.items()):
             vs.sort()
             print("    %-28s median %.6g  (n=%d)" % (cn, vs[len(vs) // 2], len(vs)))
@@ -815,7 +835,7 @@ def main():
 
     if args.only_gemm:
         gen = Dev(torch, tq, dev, 12345)
-        print(json.dumps(gemm_widths(torch, tq, gen, stream, bufs, slots, widths=(4, 16, 64), launches=20)))
+        print(json.dumps(gemm_widths(torch, tq, gen, stream, bufs, slots, widths=(4, 8, 16, 64), launches=20)))
         return
 
     log("inputs ready; warm-up")
