@@ -44,12 +44,11 @@ int32_t embed_enqueue(const uint8_t *codes, const uint16_t *scales, const int32_
 namespace {
 // Kernel choice for small batches, read once per process from TQ_GEMM_QUAD:
 // "off" never takes the 4-row MFMA kernel (tq_gemm_quad.hip), "all" sends it
-// every M <= 4 (M = 1 included), and the default sends it M = 3 and 4, and
-// M = 2 for 1-bit weights.  Measured on the MLP shapes (same box): ternary
-// M = 2 is a tie on 17408 x 5120 and 8 % slower on 5120 x 17408 than the
-// two-row VALU kernel; M = 4 is 15 % faster on 17408 x 5120 and 3 % on
-// 5120 x 17408 than the MFMA stage kernel, 1.5x on the 248320-row head; 1-bit
-// M = 2 and 4 are 5-25 % faster.
+// M = 1 as well, and the default sends it M >= 2 (it declines what it does
+// not fit; M = 9 and up).  Measured (same box), ternary M = 2 against the
+// two-row VALU kernel: 9.6 / 15.0 / 11.2 us against 11.4 / 16.4 / 11.7 on
+// 17408 x 5120, 34816 x 5120 and 5120 x 17408, 87 against 100 us on the
+// 248320-row head; M = 1 stays with the GEMV (8.2 against 9.8 us).
 int quad_mode() {
     static const int mode = [] {
         const char *v = getenv("TQ_GEMM_QUAD");
@@ -131,7 +130,7 @@ int32_t tq_gemm_ws(const uint8_t *codes, const uint16_t *scales, const uint16_t 
         return tq::gemv5_enqueue(codes, scales, X, Y, N, K, static_cast<hipStream_t>(stream));
     }
     bool handled = false;
-    if (tq::quad_mode() == 2 || (tq::quad_mode() == 1 && (M >= 3 || (M == 2 && variant == TQ_BINARY)))) {
+    if (tq::quad_mode() == 2 || (tq::quad_mode() == 1 && M >= 2)) {
         const int32_t rq = tq::gemm_quad_enqueue(codes, scales, X, Y, M, N, K, variant,
                                                  static_cast<hipStream_t>(stream), &handled);
         if (handled || rq != TQ_OK) return rq;

@@ -244,7 +244,8 @@ def test_lm_head_sampled(M):
 def test_gemm_ragged(M, N, K, variant):
     """Ragged activation and weight tiles, K of one group (most waves of a
     workgroup idle), the largest K, 5..8 rows (eight staged rows) and two-row
-    batches near the capacity of the two-row VALU kernel's LDS tile."""
+    batches past the four-row kernel's staging (K = 30080: the two-row VALU
+    kernel, near the capacity of its LDS tile)."""
     codes, s, X = case(9700 + M + N + K, N, K, M, variant, exact=True)
     Y = gpu_gemm(codes, s, X, variant, N, K)
     Yref, _ = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
