@@ -376,22 +376,25 @@ def test_gemm_deterministic():
 
 def test_graph_replay_matches_eager():
     """GEMV and GEMM launches captured in a HIP graph: every replay, with eager
-    work and synchronisation between replays, gives the eager result's bits."""
+    work and synchronisation between replays, gives the eager result's bits.
+    The widths cover the four-row kernel with one and two row sets (2, 4, 8),
+    the K-split kernel with the plain (16 rows, three slices) and the
+    four-wide (64 rows, five slices) slice reduction."""
     N, K = 4096, 5120
-    codes, s, X = case(9960, N, K, 16, TERN, exact=False)
+    codes, s, X = case(9960, N, K, 64, TERN, exact=False)
     cd, sd, Xd = up(codes), up(s), up(X)
     y = torch.empty(N, dtype=torch.float32, device="cuda")
-    Y = torch.empty(16, N, dtype=torch.float32, device="cuda")
-    Y4 = torch.empty(4, N, dtype=torch.float32, device="cuda")
+    widths = (2, 4, 8, 16, 64)
+    Ys = [torch.empty(m, N, dtype=torch.float32, device="cuda") for m in widths]
 
     def calls():
         tq.tq_gemv(cd, sd, Xd[0], y)
-        tq.tq_gemm(cd, sd, Xd, Y)
-        tq.tq_gemm(cd, sd, Xd[:4], Y4)
+        for m, Ym in zip(widths, Ys):
+            tq.tq_gemm(cd, sd, Xd[:m], Ym)
 
     calls()
     torch.cuda.synchronize()
-    y_ref, Y_ref, Y4_ref = y.clone(), Y.clone(), Y4.clone()
+    y_ref, Y_refs = y.clone(), [t.clone() for t in Ys]
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -402,15 +405,15 @@ def test_graph_replay_matches_eager():
     with torch.cuda.graph(g):
         calls()
     for r in range(4):
-        for t in (y, Y, Y4):
+        for t in [y] + Ys:
             t.fill_(float("nan"))
         tq.tq_gemv(cd, sd, Xd[1], torch.empty_like(y))   # unrelated eager work
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y_ref), "GEMV replay %d" % r
-        assert torch.equal(Y, Y_ref), "GEMM replay %d" % r
-        assert torch.equal(Y4, Y4_ref), "four-row GEMM replay %d" % r
+        for m, Ym, Yr in zip(widths, Ys, Y_refs):
+            assert torch.equal(Ym, Yr), "GEMM M=%d replay %d" % (m, r)
 
 
 @pytest.mark.parametrize("M,N,K", [(5, 1, 256), (16, 33, 256), (8, 257, 2048), (13, 300, 2304),
