@@ -172,6 +172,17 @@ __device__ __forceinline__ float seg_sum(float v) {
     return v;
 }
 
+// Waits for every vector load issued so far.  The GEMV kernels call it
+// between their x loads and the first block's code loads: issued together,
+// the x loads of later waves queue behind the code burst of every wave (the
+// first block of 2048 waves, 10 MB on the fused MLP launch).  Wave
+// timestamps on that launch: x lands 0.6 us into it and is in registers at
+// 2.2-2.3 us, against 2.9 us when issued together.  Interleaved A/B, back to
+// back: 0.1-0.6 us less per launch (down, o / lin_out, [lin_qkv;lin_z], the
+// LM head, binary and affine [gate;up]), none slower.  The same wait in the
+// MFMA GEMM kernels and the five-trit GEMV measured no gain.
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 // x staging.  Ternary unit: 16 weights -> 8 pairs (p, p+8); binary unit:
 // 32 weights -> 16 pairs (p, p+16).  UPC consecutive units make one chunk:
 // four for a 16-byte code chunk (64 ternary or 128 binary weights), two for
@@ -427,6 +438,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_kernel(const uint8_t *__restr
     for (int k = 0; k < XMAX; ++k)
         xu[k].load(x, min(min((int)threadIdx.x + k * THREADS, CAP * 4 - 1), nunits - 1));
     __builtin_amdgcn_sched_barrier(0);
+    wait_loads();  // x first, then the code burst
     u32x4 ca[NU][RPL], cb[NU][RPL];
     uint32_t sa[NU][RPL], sb[NU][RPL];
     int b = b_begin + wave;
@@ -591,6 +603,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         };
         Code ca[NU];
         uint32_t sa[NU], ba[NU];
+        wait_loads();  // x first, then the code burst
 #pragma unroll
         for (int i = 0; i < NU; ++i) load_chunk(b0, i, ca, sa, ba);
         __builtin_amdgcn_sched_barrier(0);
