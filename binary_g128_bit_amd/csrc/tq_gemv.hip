@@ -172,15 +172,10 @@ __device__ __forceinline__ float seg_sum(float v) {
     return v;
 }
 
-// Waits for every vector load issued so far.  The GEMV kernels call it
-// between their x loads and the first block's code loads: issued together,
-// the x loads of later waves queue behind the code burst of every wave (the
-// first block of 2048 waves, 10 MB on the fused MLP launch).  Wave
-// timestamps on that launch: x lands 0.6 us into it and is in registers at
-// 2.2-2.3 us, against 2.9 us when issued together.  Interleaved A/B, back to
-// back: 0.1-0.6 us less per launch (down, o / lin_out, [lin_qkv;lin_z], the
-// LM head, binary and affine [gate;up]), none slower.  The same wait in the
-// MFMA GEMM kernels and the five-trit GEMV measured no gain.
+// Waits for every vector load issued so far.  The LDS-activation GEMV calls
+// it between its x loads and the first block's code loads, so that the x
+// loads of later waves do not queue behind the code burst of every wave
+// (0.16 us less per launch on 5120 x 24576).
 __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // x staging.  Ternary unit: 16 weights -> 8 pairs (p, p+8); binary unit:
@@ -552,28 +547,33 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         xu[k].load(x, min(min((int)threadIdx.x + k * THREADS, CAP * UPC - 1), nunits - 1));
     __builtin_amdgcn_sched_barrier(0);
 
-    // x staged into LDS, then this lane's chunk slots into registers
-    auto stage_x = [&](uint32_t (&xr)[NU][XN]) __attribute__((always_inline)) {
+    // x staged into LDS (permuted, with the chunk constants) once per
+    // workgroup, then chunk slot i of this lane copied into registers
+    auto stage_lds = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int k = 0; k < XMAX; ++k) {
             const int u = min((int)threadIdx.x + k * THREADS, CAP * UPC - 1);
             xu[k].store(xs, u, u < nunits);
         }
         __syncthreads();
+    };
+    auto fill = [&](uint32_t (&xr)[NU][XN], int i) __attribute__((always_inline)) {
+        const uint32_t *slot = xs + (j + i * LPR) * XU::CHUNK_DW;
 #pragma unroll
-        for (int i = 0; i < NU; ++i) {
-            const uint32_t *slot = xs + (j + i * LPR) * XU::CHUNK_DW;
-#pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const u32x4 v = reinterpret_cast<const u32x4 *>(slot)[q];
-                xr[i][4 * q] = v[0];
-                xr[i][4 * q + 1] = v[1];
-                xr[i][4 * q + 2] = v[2];
-                xr[i][4 * q + 3] = v[3];
-            }
-            xr[i][32] = slot[32];
-            if constexpr (AFF) xr[i][33] = slot[33];
+        for (int q = 0; q < 8; ++q) {
+            const u32x4 v = reinterpret_cast<const u32x4 *>(slot)[q];
+            xr[i][4 * q] = v[0];
+            xr[i][4 * q + 1] = v[1];
+            xr[i][4 * q + 2] = v[2];
+            xr[i][4 * q + 3] = v[3];
         }
+        xr[i][32] = slot[32];
+        if constexpr (AFF) xr[i][33] = slot[33];
+    };
+    auto stage_x = [&](uint32_t (&xr)[NU][XN]) __attribute__((always_inline)) {
+        stage_lds();
+#pragma unroll
+        for (int i = 0; i < NU; ++i) fill(xr, i);
     };
     uint32_t xr[NU][XN];
 
@@ -603,17 +603,28 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         };
         Code ca[NU];
         uint32_t sa[NU], ba[NU];
-        wait_loads();  // x first, then the code burst
+        // Every wave of the workgroup issues its x loads before any wave
+        // issues code loads (a barrier, no wait for data): issued per wave,
+        // the x loads of later waves queued behind earlier waves' first-block
+        // code bursts and x reached the registers about 2.9 us into the fused
+        // MLP launch.  The first block then copies chunk slot i + 1 from LDS
+        // while chunk i computes, instead of all 165 registers before the
+        // loop (about 340 KB of LDS reads per CU, 1.3 us at 128 B per clock).
+        __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int i = 0; i < NU; ++i) load_chunk(b0, i, ca, sa, ba);
         __builtin_amdgcn_sched_barrier(0);
-        stage_x(xr);
+        stage_lds();
+        fill(xr, 0);
 
-        auto block = [&](auto refill, Code (&c)[NU], uint32_t (&sv)[NU], uint32_t (&bv)[NU], int bb,
+        auto block = [&](auto refill, auto first, Code (&c)[NU], uint32_t (&sv)[NU], uint32_t (&bv)[NU], int bb,
                          int bn) __attribute__((always_inline)) {
             float acc = 0.0f;
 #pragma unroll
             for (int i = 0; i < NU; ++i) {
+                if constexpr (decltype(first)::value) {
+                    if (i + 1 < NU) fill(xr, i + 1);
+                }
                 chunk_dot_reg<VARIANT>(c[i], xr[i], sv[i] >> hsh[i], AFF ? bv[i] >> hsh[i] : 0u, acc, km);
                 if constexpr (decltype(refill)::value) load_chunk(bn, i, c, sv, bv);
                 __builtin_amdgcn_sched_barrier(0);
@@ -624,9 +635,18 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         };
         using Refill = std::integral_constant<bool, true>;
         using Last = std::integral_constant<bool, false>;
+        using First = std::integral_constant<bool, true>;
+        using Later = std::integral_constant<bool, false>;
         int k = 0;
-        for (; k + 1 < nb; ++k) block(Refill{}, ca, sa, ba, b0 + k * WAVES, b0 + (k + 1) * WAVES);
-        if (k < nb) block(Last{}, ca, sa, ba, b0 + k * WAVES, 0);
+        if (nb > 1) {
+            block(Refill{}, First{}, ca, sa, ba, b0, b0 + WAVES);
+            k = 1;
+        } else if (nb == 1) {
+            block(Last{}, First{}, ca, sa, ba, b0, 0);
+            k = 1;
+        }
+        for (; k + 1 < nb; ++k) block(Refill{}, Later{}, ca, sa, ba, b0 + k * WAVES, b0 + (k + 1) * WAVES);
+        if (k < nb) block(Last{}, Later{}, ca, sa, ba, b0 + k * WAVES, 0);
     } else if constexpr (VARIANT != TQ_BINARY) {
         u32x4 ca[NU][1], cb[NU][1];
         uint32_t sa[NU][1], sb[NU][1];
