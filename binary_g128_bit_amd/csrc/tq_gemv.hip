@@ -590,14 +590,27 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         }
         const uint32_t *sc32 = reinterpret_cast<const uint32_t *>(scales);
         const uint32_t *bi32 = reinterpret_cast<const uint32_t *>(biases);
-        auto load_chunk = [&](int bb, int i, Code (&c)[NU], uint32_t (&sv)[NU], uint32_t (&bv)[NU])
-                              __attribute__((always_inline)) {
+        // Bases of the row this lane segment loads: the same for all NU
+        // chunks of a block, so they are formed once per block and each chunk
+        // adds its column (this loop runs with an even group count, so every
+        // row's scales start on a dword and chunk col's scale dword is
+        // col / 4 into the row).
+        const Code *crow = nullptr;
+        const uint32_t *srow = nullptr, *brow = nullptr;
+        auto set_row = [&](int bb) __attribute__((always_inline)) {
             const int r = min(min(bb, blast) * RS + seg, N - 1);
-            const size_t h = ((size_t)r * G + (col[i] >> 1)) >> 1;
-            sv[i] = sc32[h];
-            if constexpr (AFF) bv[i] = bi32[h];
-            c[i] = __builtin_nontemporal_load(
-                reinterpret_cast<const Code *>(codes + (size_t)r * CPR * CB) + col[i]);
+            crow = reinterpret_cast<const Code *>(codes + (size_t)r * CPR * CB);
+            srow = sc32 + (size_t)r * (G >> 1);
+            if constexpr (AFF) brow = bi32 + (size_t)r * (G >> 1);
+        };
+        auto load_chunk = [&](int i, Code (&c)[NU], uint32_t (&sv)[NU], uint32_t (&bv)[NU])
+                              __attribute__((always_inline)) {
+            // unclamped columns are j + i LPR: constant offsets from the
+            // lane's first chunk, which the loads take as immediates
+            const int sc = RAGGED ? col[i] >> 2 : (j >> 2) + i * (LPR >> 2);
+            sv[i] = srow[sc];
+            if constexpr (AFF) bv[i] = brow[sc];
+            c[i] = __builtin_nontemporal_load(crow + (RAGGED ? col[i] : j + i * LPR));
         };
         Code ca[NU];
         uint32_t sa[NU], ba[NU];
@@ -609,8 +622,9 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         // while chunk i computes, instead of all 165 registers before the
         // loop (about 340 KB of LDS reads per CU, 1.3 us at 128 B per clock).
         __builtin_amdgcn_s_barrier();
+        set_row(b0);
 #pragma unroll
-        for (int i = 0; i < NU; ++i) load_chunk(b0, i, ca, sa, ba);
+        for (int i = 0; i < NU; ++i) load_chunk(i, ca, sa, ba);
         __builtin_amdgcn_sched_barrier(0);
         stage_lds();
         fill(xr, 0);
@@ -618,13 +632,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         auto block = [&](auto refill, auto first, Code (&c)[NU], uint32_t (&sv)[NU], uint32_t (&bv)[NU], int bb,
                          int bn) __attribute__((always_inline)) {
             float acc = 0.0f;
+            if constexpr (decltype(refill)::value) set_row(bn);
 #pragma unroll
             for (int i = 0; i < NU; ++i) {
                 if constexpr (decltype(first)::value) {
                     if (i + 1 < NU) fill(xr, i + 1);
                 }
                 chunk_dot_reg<VARIANT>(c[i], xr[i], sv[i] >> hsh[i], AFF ? bv[i] >> hsh[i] : 0u, acc, km);
-                if constexpr (decltype(refill)::value) load_chunk(bn, i, c, sv, bv);
+                if constexpr (decltype(refill)::value) load_chunk(i, c, sv, bv);
                 __builtin_amdgcn_sched_barrier(0);
             }
             const float out = seg_sum<LPR>(acc) * XU::kRowScale;
