@@ -16,8 +16,9 @@
 //   M16: a code at bits [6,8) under exponent field 5 is 2^-10 + c * 2^-14.
 // One copy of a code dword serves an E, an M4 and an M16 pair (slot p in the
 // low half, p + 8 in the high half): d gives slots 5, 4, 3, d << 6 gives
-// 2, 1, 0 and d >> 4 gives 7, 6, so two shifts and one mask op per pair
-// decode 16 weights.  Per 16-byte chunk the slot offsets (4 and 16 units) and
+// 2, 1, 0 and d >> 4 gives 7, 6, so one mask op per pair and two shifts
+// decode 16 weights (the shifts taken on two code dwords at once as 64-bit
+// shifts: one per dword and copy kind per pair of dwords).  Per 16-byte chunk the slot offsets (4 and 16 units) and
 // sum x (t = c - 1) are removed by seeding the chunk's accumulator with
 // -(sum x + 4 S_M4 + 16 S_M16) * 2^-14, a constant computed while x is staged
 // (S_M4 and S_M16 sum x over those slots), and the row total is scaled by
@@ -78,8 +79,28 @@ struct Masks {
     }
 };
 
-
 typedef uint64_t u64;
+
+// d << L and d >> R of the code dword pair (d0, d1) taken as one 64-bit value
+// (d0 low): one 64-bit shift yields both dwords' copies, where two 32-bit
+// shifts did.  Bits that cross between the dwords land in bits [0, L) of the
+// high dword of d << L and bits [32 - R, 32) of the low dword of d >> R.  The
+// decodes read only bits [6, 12) and [22, 28) of d << 6, and bits [8, 12) and
+// [24, 28) (ternary, binary: R = 4) or [4, 10) and [20, 26) (affine: R = 6)
+// of d >> R, so the crossed bits are always masked off.
+template <int L, int R>
+__device__ __forceinline__ void shifts64(uint32_t d0, uint32_t d1, uint32_t (&l)[2], uint32_t (&r)[2]) {
+    const u64 w = ((u64)d1 << 32) | d0;
+    u64 wl, wr;
+    // written out: the compiler splits a right shift whose halves are used
+    // apart into an alignbit and a 32-bit shift
+    asm("v_lshlrev_b64 %0, %2, %1" : "=v"(wl) : "v"(w), "i"(L));
+    asm("v_lshrrev_b64 %0, %2, %1" : "=v"(wr) : "v"(w), "i"(R));
+    l[0] = (uint32_t)wl;
+    l[1] = (uint32_t)(wl >> 32);
+    r[0] = (uint32_t)wr;
+    r[1] = (uint32_t)(wr >> 32);
+}
 
 // 32 ternary codes (dwords d0, d1) against pairs xp[p] = (x[p], x[p+8]) of
 // each dword's 16 weights, accumulated into a in units of 2^-14.
@@ -87,10 +108,12 @@ __device__ __forceinline__ void tern_acc32(uint32_t d0, uint32_t d1, const uint3
                                            const uint32_t *xp1, float &a, const Masks &k) {
     const uint32_t dd[2] = {d0, d1};
     const uint32_t *xps[2] = {xp0, xp1};
+    uint32_t l6[2], s4[2];
+    shifts64<6, 4>(d0, d1, l6, s4);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const uint32_t *xp = xps[h];
-        const uint32_t c0 = dd[h], c6 = dd[h] << 6, r4 = dd[h] >> 4;
+        const uint32_t c0 = dd[h], c6 = l6[h], r4 = s4[h];
         a = dot2(c0 & 0x0C000C00u, xp[5], a);              // E   slot 5
         a = dot2((c0 & k.m8) | 0x0C000C00u, xp[4], a);     // M4  slot 4
         a = dot2((c0 & k.m6) | 0x14001400u, xp[3], a);     // M16 slot 3
@@ -112,10 +135,12 @@ __device__ __forceinline__ void aff_acc32(uint32_t d0, uint32_t d1, const uint32
                                           const uint32_t *xp1, float &a, const Masks &k) {
     const uint32_t dd[2] = {d0, d1};
     const uint32_t *xps[2] = {xp0, xp1};
+    uint32_t l6[2], s6[2];
+    shifts64<6, 6>(d0, d1, l6, s6);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const uint32_t *xp = xps[h];
-        const uint32_t c0 = dd[h], c6 = dd[h] << 6, r6 = dd[h] >> 6;
+        const uint32_t c0 = dd[h], c6 = l6[h], r6 = s6[h];
         a = dot2((c0 & k.m8) | 0x0C000C00u, xp[4], a);     // M4  slot 4
         a = dot2((c0 & k.m6) | 0x14001400u, xp[3], a);     // M16 slot 3
         a = dot2((c0 & k.m4) | 0x1C001C00u, xp[2], a);     // M64 slot 2
@@ -146,11 +171,13 @@ __device__ __forceinline__ void bin_acc64(uint32_t d0, uint32_t d1, const uint32
                                           const uint32_t *xp1, float &a, const Masks &k) {
     const uint32_t dd[2] = {d0, d1};
     const uint32_t *xps[2] = {xp0, xp1};
+    uint32_t l6[2], s4[2];
+    shifts64<6, 4>(d0, d1, l6, s4);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         bin_slots(dd[h], xps[h], 11, 6, a, k);
-        bin_slots(dd[h] << 6, xps[h], 5, 6, a, k);
-        bin_slots(dd[h] >> 4, xps[h], 15, 4, a, k);
+        bin_slots(l6[h], xps[h], 5, 6, a, k);
+        bin_slots(s4[h], xps[h], 15, 4, a, k);
     }
 }
 
