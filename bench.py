@@ -78,6 +78,10 @@ def parse():
     p.add_argument("--pmc-summary", metavar="CSV", nargs="+",
                    help="summarise rocprofv3 counter_collection.csv files (median per kernel and grid) "
                         "and exit")
+    p.add_argument("--traffic-json", metavar="CSV", nargs=4,
+                   help="write the fused GEMV's HBM traffic summary from four rocprofv3 counter files: "
+                        "FETCH_SIZE and WRITE_SIZE of `--only-step`, then of `--copy-calibration`; "
+                        "print it as JSON and exit")
     return p.parse_args()
 
 
@@ -779,6 +783,67 @@ def pmc_summary(paths):
             print("    %-28s median %.6g  (n=%d)" % (cn, vs[len(vs) // 2], len(vs)))
 
 
+TRAFFIC_KERNEL = "gemv_xreg_kernel<0, 16, 5, 8, false, true>"   # the fused [gate;up] launch's template
+TRAFFIC_GRID = "131072"
+
+
+def traffic_json(step_fetch, step_write, cal_fetch, cal_write, skip=5):
+    """HBM bytes per fused [gate;up] launch from rocprofv3 FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch): the mean over the `--only-step` run's
+    launches of the fused GEMV (its first `skip` left out), each counter
+    scaled by bytes / KiB read for the 1 GiB calibration copy."""
+    def values(path, pick):
+        rows = [r for r in _csv_rows(path) if pick(r)]
+        rows.sort(key=lambda r: int(_col(r, "Dispatch_Id")))
+        return [float(_col(r, "Counter_Value")) for r in rows]
+
+    def fused(r):
+        return TRAFFIC_KERNEL in _col(r, "Kernel_Name") and _col(r, "Grid_Size", "Grid_Size_X") == TRAFFIC_GRID
+
+    def copy(r):
+        return "copyBuffer" in _col(r, "Kernel_Name")
+
+    out = {"kernel": TRAFFIC_KERNEL + " on [gate;up] 34816x5120 ternary",
+           "source_sha256_16": source_hash(os.path.join(ROOT, "binary_g128_bit_amd", "csrc", "tq_gemv.hip")),
+           "commands": [
+               "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {FETCH_SIZE|WRITE_SIZE} -d /tmp/step_<ctr> -o run "
+               "--output-format csv -- python3 $REPO/bench.py --only-step --steps 20 --warmup 2",
+               "cd /tmp && TMPDIR=/tmp rocprofv3 --pmc {FETCH_SIZE|WRITE_SIZE} -d /tmp/cal_<ctr> -o run "
+               "--output-format csv -- python3 $REPO/bench.py --copy-calibration",
+               "python3 $REPO/bench.py --traffic-json <step FETCH_SIZE csv> <step WRITE_SIZE csv> "
+               "<calibration FETCH_SIZE csv> <calibration WRITE_SIZE csv>"]}
+    cal = {}
+    for name, path in (("fetch", cal_fetch), ("write", cal_write)):
+        v = sorted(values(path, copy))
+        kib = v[len(v) // 2]
+        cal[name] = (COPY_BYTES / 1024.0) / kib
+        out.setdefault("copy_calibration", {"bytes": COPY_BYTES})["%s_size_kib" % name] = kib
+        out["copy_calibration"]["%s_scale" % name] = cal[name]
+    # the unfused 17408-row gate of the per-launch timings runs the same
+    # template and grid on half the rows: its dispatches count about half
+    # the bytes, and are left out by that
+    def fused_only(v):
+        top = max(v)
+        return [x for x in v if x >= 0.75 * top]
+    f = fused_only(values(step_fetch, fused)[skip:])
+    w = fused_only(values(step_write, fused)[skip:])
+    out["dispatches"] = {"fetch": len(f), "write": len(w),
+                         "note": "fused launches only (grid %s, counts within 0.75 of the largest: the unfused "
+                                 "gate on the same template counts about half); the first %d of each pass left "
+                                 "out" % (TRAFFIC_GRID, skip)}
+    fk, wk = sum(f) / len(f), sum(w) / len(w)
+    out["fetch_size_kib_per_launch"] = fk
+    out["write_size_kib_per_launch"] = wk
+    out["hbm_fetch_bytes_per_launch"] = round(fk * 1024 * cal["fetch"])
+    out["hbm_write_bytes_per_launch"] = round(wk * 1024 * cal["write"])
+    out["hbm_bytes_per_launch"] = out["hbm_fetch_bytes_per_launch"] + out["hbm_write_bytes_per_launch"]
+    N, K = 34816, 5120
+    codes, scales = N * K // 4, N * (K // 128) * 2
+    out["algorithmic_bytes_per_launch"] = codes + scales + 2 * K + 4 * N
+    out["note"] = "algorithmic = codes %d + scales %d + x %d + y %d" % (codes, scales, 2 * K, 4 * N)
+    print(json.dumps(out, indent=1))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -793,6 +858,9 @@ def main():
         return
     if args.pmc_summary:
         pmc_summary(args.pmc_summary)
+        return
+    if args.traffic_json:
+        traffic_json(*args.traffic_json)
         return
     if args.only_step:
         args.no_cpu = args.no_extras = True
