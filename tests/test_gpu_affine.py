@@ -51,6 +51,26 @@ def test_affine_integer_exact(N, K):
     assert np.array_equal(gpu(codes, s, b, x), yref[0])
 
 
+@pytest.mark.parametrize("N,K", [(64, 5120), (20, 17408)])
+def test_affine_saturated_neighbour_dwords(N, K):
+    """Code dwords of level 3 (every bit set) next to dwords of level 0 and
+    the reverse, row by row, plus rows of one level-3 weight per dword: bits
+    of one dword leaking into its neighbour's shifted copies would change
+    these rows.  Integer-exact inputs, so the bar is bit-exact."""
+    _, s, b, X = synth.affine_problem(17700 + N + K, N, K, 1, True)
+    q = np.empty((N, K), np.int8)
+    for n in range(N):
+        hi, lo = (3, 0) if n % 2 == 0 else (0, 3)
+        for d in range(K // 16):
+            q[n, d * 16:(d + 1) * 16] = hi if d % 2 == 0 else lo
+        if n % 4 == 3:
+            q[n] = 0
+            q[n, 15::16] = 3
+    codes = oracle.pack(q, oracle.AFFINE2)
+    yref, _ = oracle.affine_gemm(codes, s, b, X[0], N, K, threads=THREADS)
+    assert np.array_equal(gpu(codes, s, b, X[0]), yref[0])
+
+
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_affine_random(N, K):
     codes, s, b, x = case(18000 + N + K, N, K, exact=False)

@@ -63,6 +63,30 @@ def test_gemv_integer_exact(N, K, variant):
 
 
 @pytest.mark.parametrize("variant", [TERN, BIN])
+@pytest.mark.parametrize("N,K", [(64, 5120), (20, 17408), (32, 6144)])
+def test_gemv_saturated_neighbour_dwords(N, K, variant):
+    """Every code dword all t = +1 (every bit of a dword set for binary)
+    next to dwords of t = -1 or 0 and the reverse, row by row: a decode that
+    let bits of one dword leak into its neighbour's shifted copies would
+    change these rows.  Integer-exact inputs, so the bar is bit-exact."""
+    _, s, X = synth.problem(7700 + N + K, N, K, 1, variant, exact=True)
+    per = 16 if variant == TERN else 32              # weights per code dword
+    lo = [-1, 0] if variant == TERN else [-1]
+    t = np.empty((N, K), np.int8)
+    for n in range(N):
+        a, b = (1, lo[n % len(lo)]) if n % 2 == 0 else (lo[n % len(lo)], 1)
+        for d in range(K // per):
+            t[n, d * per:(d + 1) * per] = a if d % 2 == 0 else b
+        if n % 4 == 3:                               # and a row of single set weights
+            t[n] = lo[0]
+            t[n, per - 1::per] = 1
+    codes = oracle.pack(t, variant)
+    Y = gpu_gemm(codes, s, X, variant, N, K)
+    Yref, _ = oracle.gemm(codes, s, X, N, K, variant, threads=THREADS)
+    assert np.array_equal(Y.astype(np.float64), Yref)
+
+
+@pytest.mark.parametrize("variant", [TERN, BIN])
 @pytest.mark.parametrize("N,K", SHAPES)
 def test_gemv_random(N, K, variant):
     codes, s, X = case(8000 + N + K, N, K, 1, variant, exact=False)
