@@ -106,6 +106,20 @@ __device__ __forceinline__ void tern_acc32(uint32_t d0, uint32_t d1, const uint3
     }
 }
 
+// 16 ternary codes (dword d) against its pairs xp[p] = (x[p], x[p+8]),
+// accumulated into a in units of 2^-14 (one dword of tern_acc32).
+__device__ __forceinline__ void tern_acc16(uint32_t d, const uint32_t *xp, float &a, const Masks &k) {
+    const uint32_t c6 = d << 6, r4 = d >> 4;
+    a = dot2(d & 0x0C000C00u, xp[5], a);               // E   slot 5
+    a = dot2((d & k.m8) | 0x0C000C00u, xp[4], a);      // M4  slot 4
+    a = dot2((d & k.m6) | 0x14001400u, xp[3], a);      // M16 slot 3
+    a = dot2(c6 & 0x0C000C00u, xp[2], a);              // E   slot 2
+    a = dot2((c6 & k.m8) | 0x0C000C00u, xp[1], a);     // M4  slot 1
+    a = dot2((c6 & k.m6) | 0x14001400u, xp[0], a);     // M16 slot 0
+    a = dot2(r4 & 0x0C000C00u, xp[7], a);              // E   slot 7
+    a = dot2((r4 & k.m8) | 0x0C000C00u, xp[6], a);     // M4  slot 6
+}
+
 // 32 affine levels q in {0..3} (dwords d0, d1) against pairs xp[p] =
 // (x[p], x[p+8]), accumulated into a in units of 2^-14.  Level 3 rules out the
 // E slot (exponent field 3 is 4 units, not 3), so three mantissa slots serve
@@ -519,7 +533,7 @@ __device__ __forceinline__ void load_bias(const uint16_t *__restrict__ biases, i
 // value: 16-bit registers are packed in pairs, and the packing waits for both
 // loads).  Otherwise a plain ping-pong of two register sets, each loaded whole
 // one block ahead.
-template <int VARIANT, int LPR, int NU, int WAVES, bool RAGGED, bool PIPE>
+template <int VARIANT, int LPR, int NU, int WAVES, bool RAGGED, bool PIPE, bool TAIL = false>
 __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__restrict__ codes,
                                                                const uint16_t *__restrict__ scales,
                                                                const uint16_t *__restrict__ biases,
@@ -530,11 +544,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
     using Code = typename XReg<VARIANT>::Code;
     constexpr bool AFF = VARIANT == TQ_AFFINE2;
     static_assert(PIPE || VARIANT != TQ_BINARY, "binary codes take the pipelined loop only");
+    // TAIL: a row is NU full chunk columns of the LPR lanes plus LPR / 4
+    // chunks more, which the lanes take one 16-weight unit (one code dword)
+    // each in a tail slot, where a clamped fifth chunk column would leave
+    // three quarters of its lanes decoding nothing
+    static_assert(!TAIL || (VARIANT == TQ_TERNARY && PIPE && !RAGGED && (LPR * NU) % 8 == 0),
+                  "the tail slot is a ternary, exact, pipelined layout with an even scale dword start");
     constexpr int XN = XReg<VARIANT>::N;
     constexpr int UPC = XReg<VARIANT>::UPC, CB = XReg<VARIANT>::CB;
     constexpr int THREADS = 64 * WAVES;
     constexpr int RS = 64 / LPR;  // rows per block (one per lane segment)
-    constexpr int CAP = LPR * NU;
+    constexpr int CAP = LPR * NU + (TAIL ? LPR / 4 : 0);  // staged chunk slots
     constexpr int XMAX = (CAP * UPC + THREADS - 1) / THREADS;
     const int G = K >> 7, CPR = 2 * G;  // 64-weight chunks per row
     const int nunits = CPR * UPC;
@@ -622,6 +642,35 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         };
         Code ca[NU];
         uint32_t sa[NU], ba[NU];
+        // tail slot (TAIL): unit j of the row's last LPR / 4 chunks, one code
+        // dword; its group is LPR NU / 2 + j / 8, in scale dword
+        // LPR NU / 4 + j / 16 at half (j / 8) & 1 (LPR NU is a multiple of 8)
+        uint32_t ct = 0, st = 0, xt[9];
+        const uint32_t hsh_t = ((uint32_t)(j >> 3) & 1u) * 16u;
+        auto load_tail = [&]() __attribute__((always_inline)) {
+            if constexpr (TAIL) {
+                st = srow[(LPR * NU) / 4 + j / 16];
+                ct = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(crow) + LPR * NU * 4 + j);
+            }
+        };
+        // the unit's 8 pairs from its chunk slot and its own seed (the chunk
+        // constant covers all four units of a chunk)
+        auto fill_tail = [&]() __attribute__((always_inline)) {
+            if constexpr (TAIL) {
+                const uint32_t *slot = xs + (LPR * NU + j / 4) * XU::CHUNK_DW + (j % 4) * (XU::UNIT / 2);
+                const u32x4 v0 = reinterpret_cast<const u32x4 *>(slot)[0];
+                const u32x4 v1 = reinterpret_cast<const u32x4 *>(slot)[1];
+                float z = 0.0f;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    xt[p] = v0[p];
+                    xt[4 + p] = v1[p];
+                }
+#pragma unroll
+                for (int p = 0; p < 8; ++p) z = dot2(xt[p], XU::zweight(p), z);
+                xt[8] = __builtin_bit_cast(uint32_t, z * -XU::kSeedScale);
+            }
+        };
         // Every wave of the workgroup issues its x loads before any wave
         // issues code loads (a barrier, no wait for data): issued per wave,
         // the x loads of later waves queued behind earlier waves' first-block
@@ -633,6 +682,7 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         set_row(b0);
 #pragma unroll
         for (int i = 0; i < NU; ++i) load_chunk(i, ca, sa, ba);
+        load_tail();
         __builtin_amdgcn_sched_barrier(0);
         stage_lds();
         fill(xr, 0);
@@ -645,9 +695,17 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
             for (int i = 0; i < NU; ++i) {
                 if constexpr (decltype(first)::value) {
                     if (i + 1 < NU) fill(xr, i + 1);
+                    else fill_tail();
                 }
                 chunk_dot_reg<VARIANT>(c[i], xr[i], sv[i] >> hsh[i], AFF ? bv[i] >> hsh[i] : 0u, acc, km);
                 if constexpr (decltype(refill)::value) load_chunk(i, c, sv, bv);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (TAIL) {
+                float a = __builtin_bit_cast(float, xt[8]);
+                tern_acc16(ct, xt, a, km);
+                acc = __builtin_fmaf(half_bits(st >> hsh_t), a, acc);
+                if constexpr (decltype(refill)::value) load_tail();
                 __builtin_amdgcn_sched_barrier(0);
             }
             const float out = seg_sum<LPR>(acc) * XU::kRowScale;
@@ -821,9 +879,25 @@ Config pick_xreg(int cpr) {
     return best;
 }
 
-template <int VARIANT, int LPR, int NU>
+template <int VARIANT, int LPR, int NU, bool TAIL = false>
 constexpr size_t lds_bytes_xreg() {
-    return (size_t)LPR * NU * XReg<VARIANT>::Unit::CHUNK_DW * sizeof(uint32_t);
+    return (size_t)(LPR * NU + (TAIL ? LPR / 4 : 0)) * XReg<VARIANT>::Unit::CHUNK_DW * sizeof(uint32_t);
+}
+
+// A row of exactly LPR NU full chunk columns plus LPR / 4 chunks (one
+// 16-weight unit per lane): 2-bit codes on the pipelined loop take the tail
+// slot instead of a fifth, mostly clamped, chunk column.
+template <int LPR, int NU>
+hipError_t launch_xreg_tail(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y, int N,
+                            hipStream_t stream) {
+    constexpr int RS = 64 / LPR;
+    constexpr int K = (LPR * NU + LPR / 4) * 64;
+    const int nblocks = (N + RS - 1) / RS;
+    const int grid = max(1, min(device_cus(), (nblocks + kXregWaves - 1) / kXregWaves));
+    constexpr size_t lds = lds_bytes_xreg<TQ_TERNARY, LPR, NU, true>();
+    hipLaunchKernelGGL((gemv_xreg_kernel<TQ_TERNARY, LPR, NU, kXregWaves, false, true, true>), dim3(grid),
+                       dim3(64 * kXregWaves), lds, stream, codes, scales, nullptr, x, y, N, K);
+    return hipGetLastError();
 }
 
 template <int VARIANT, int LPR, int NU>
@@ -842,6 +916,10 @@ hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint1
     hipLaunchKernelGGL((gemv_xreg_kernel<VARIANT, LPR, NU, kXregWaves, R, P>), dim3(grid),         \
                        dim3(64 * kXregWaves), lds, stream, codes, scales, biases, x, y, N, K)
     if constexpr (VARIANT == TQ_TERNARY) {
+        if constexpr (NU >= 2) {
+            if (pipe && K == (LPR * (NU - 1) + LPR / 4) * 64)
+                return launch_xreg_tail<LPR, NU - 1>(codes, scales, x, y, N, stream);
+        }
         if (pipe && exact) TQ_XL(false, true);
         else if (pipe) TQ_XL(true, true);
         else TQ_XL(true, false);
