@@ -545,11 +545,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
     constexpr bool AFF = VARIANT == TQ_AFFINE2;
     static_assert(PIPE || VARIANT != TQ_BINARY, "binary codes take the pipelined loop only");
     // TAIL: a row is NU full chunk columns of the LPR lanes plus LPR / 4
-    // chunks more, which the lanes take one 16-weight unit (one code dword)
-    // each in a tail slot, where a clamped fifth chunk column would leave
-    // three quarters of its lanes decoding nothing
-    static_assert(!TAIL || (VARIANT == TQ_TERNARY && PIPE && !RAGGED && (LPR * NU) % 8 == 0),
-                  "the tail slot is a ternary, exact, pipelined layout with an even scale dword start");
+    // chunks more, which the lanes take one unit (one code dword: 16 2-bit or
+    // 32 1-bit weights) each in a tail slot (1-bit: lanes j < LPR / 2), where
+    // a clamped fifth chunk column would leave three quarters of its lanes
+    // decoding nothing
+    static_assert(!TAIL || ((VARIANT == TQ_TERNARY || VARIANT == TQ_BINARY) && PIPE && !RAGGED &&
+                            (LPR * NU) % 8 == 0),
+                  "the tail slot is a 2-bit or 1-bit, exact, pipelined layout with an even scale dword start");
     constexpr int XN = XReg<VARIANT>::N;
     constexpr int UPC = XReg<VARIANT>::UPC, CB = XReg<VARIANT>::CB;
     constexpr int THREADS = 64 * WAVES;
@@ -642,33 +644,38 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         };
         Code ca[NU];
         uint32_t sa[NU], ba[NU];
-        // tail slot (TAIL): unit j of the row's last LPR / 4 chunks, one code
-        // dword; its group is LPR NU / 2 + j / 8, in scale dword
-        // LPR NU / 4 + j / 16 at half (j / 8) & 1 (LPR NU is a multiple of 8)
-        uint32_t ct = 0, st = 0, xt[9];
-        const uint32_t hsh_t = ((uint32_t)(j >> 3) & 1u) * 16u;
+        // tail slot (TAIL): unit j of the row's last LPR / 4 chunks (TU units,
+        // one code dword of UW weights each); its group is LPR NU / 2 +
+        // UW j / 128, in scale dword LPR NU / 4 + UW j / 256 at half
+        // (UW j / 128) & 1 (LPR NU is a multiple of 8).  1-bit lanes
+        // j >= TU load the last unit and hold zero activations.
+        constexpr int UW = XU::UNIT, TP = UW / 2;        // weights and pair dwords per unit
+        constexpr int TU = LPR * 16 / UW;                // tail units per row
+        constexpr int CDW = CB / 4;                      // code dwords per chunk
+        const int jt = min(j, TU - 1);
+        uint32_t ct = 0, st = 0, xt[TP + 1];
+        const uint32_t hsh_t = ((uint32_t)(jt * UW / 128) & 1u) * 16u;
         auto load_tail = [&]() __attribute__((always_inline)) {
             if constexpr (TAIL) {
-                st = srow[(LPR * NU) / 4 + j / 16];
-                ct = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(crow) + LPR * NU * 4 + j);
+                st = srow[(LPR * NU) / 4 + jt * UW / 256];
+                ct = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(crow) + LPR * NU * CDW + jt);
             }
         };
-        // the unit's 8 pairs from its chunk slot and its own seed (the chunk
-        // constant covers all four units of a chunk)
+        // the unit's pairs from its chunk slot and its own seed (the chunk
+        // constant covers all the units of a chunk)
         auto fill_tail = [&]() __attribute__((always_inline)) {
             if constexpr (TAIL) {
-                const uint32_t *slot = xs + (LPR * NU + j / 4) * XU::CHUNK_DW + (j % 4) * (XU::UNIT / 2);
-                const u32x4 v0 = reinterpret_cast<const u32x4 *>(slot)[0];
-                const u32x4 v1 = reinterpret_cast<const u32x4 *>(slot)[1];
+                const uint32_t *slot = xs + (LPR * NU + jt / UPC) * XU::CHUNK_DW + (jt % UPC) * TP;
                 float z = 0.0f;
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    xt[p] = v0[p];
-                    xt[4 + p] = v1[p];
+                for (int q = 0; q < TP / 4; ++q) {
+                    const u32x4 v = reinterpret_cast<const u32x4 *>(slot)[q];
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) xt[4 * q + p] = j < TU ? v[p] : 0u;
                 }
 #pragma unroll
-                for (int p = 0; p < 8; ++p) z = dot2(xt[p], XU::zweight(p), z);
-                xt[8] = __builtin_bit_cast(uint32_t, z * -XU::kSeedScale);
+                for (int p = 0; p < TP; ++p) z = dot2(xt[p], XU::zweight(p), z);
+                xt[TP] = __builtin_bit_cast(uint32_t, z * -XU::kSeedScale);
             }
         };
         // Every wave of the workgroup issues its x loads before any wave
@@ -702,8 +709,14 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (TAIL) {
-                float a = __builtin_bit_cast(float, xt[8]);
-                tern_acc16(ct, xt, a, km);
+                float a = __builtin_bit_cast(float, xt[TP]);
+                if constexpr (VARIANT == TQ_TERNARY) {
+                    tern_acc16(ct, xt, a, km);
+                } else {
+                    bin_slots(ct, xt, 11, 6, a, km);
+                    bin_slots(ct << 6, xt, 5, 6, a, km);
+                    bin_slots(ct >> 4, xt, 15, 4, a, km);
+                }
                 acc = __builtin_fmaf(half_bits(st >> hsh_t), a, acc);
                 if constexpr (decltype(refill)::value) load_tail();
                 __builtin_amdgcn_sched_barrier(0);
@@ -884,18 +897,19 @@ constexpr size_t lds_bytes_xreg() {
     return (size_t)(LPR * NU + (TAIL ? LPR / 4 : 0)) * XReg<VARIANT>::Unit::CHUNK_DW * sizeof(uint32_t);
 }
 
-// A row of exactly LPR NU full chunk columns plus LPR / 4 chunks (one
-// 16-weight unit per lane): 2-bit codes on the pipelined loop take the tail
-// slot instead of a fifth, mostly clamped, chunk column.
-template <int LPR, int NU>
+// A row of exactly LPR NU full chunk columns plus LPR / 4 chunks (one unit
+// per lane: 16 2-bit weights, or 32 1-bit weights on half the lanes): codes
+// on the pipelined loop take the tail slot instead of a fifth, mostly
+// clamped, chunk column.
+template <int VARIANT, int LPR, int NU>
 hipError_t launch_xreg_tail(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y, int N,
                             hipStream_t stream) {
     constexpr int RS = 64 / LPR;
     constexpr int K = (LPR * NU + LPR / 4) * 64;
     const int nblocks = (N + RS - 1) / RS;
     const int grid = max(1, min(device_cus(), (nblocks + kXregWaves - 1) / kXregWaves));
-    constexpr size_t lds = lds_bytes_xreg<TQ_TERNARY, LPR, NU, true>();
-    hipLaunchKernelGGL((gemv_xreg_kernel<TQ_TERNARY, LPR, NU, kXregWaves, false, true, true>), dim3(grid),
+    constexpr size_t lds = lds_bytes_xreg<VARIANT, LPR, NU, true>();
+    hipLaunchKernelGGL((gemv_xreg_kernel<VARIANT, LPR, NU, kXregWaves, false, true, true>), dim3(grid),
                        dim3(64 * kXregWaves), lds, stream, codes, scales, nullptr, x, y, N, K);
     return hipGetLastError();
 }
@@ -915,11 +929,11 @@ hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint1
 #define TQ_XL(R, P)                                                                               \
     hipLaunchKernelGGL((gemv_xreg_kernel<VARIANT, LPR, NU, kXregWaves, R, P>), dim3(grid),         \
                        dim3(64 * kXregWaves), lds, stream, codes, scales, biases, x, y, N, K)
+    if constexpr (VARIANT != TQ_AFFINE2 && NU >= 2) {
+        if (pipe && K == (LPR * (NU - 1) + LPR / 4) * 64)
+            return launch_xreg_tail<VARIANT, LPR, NU - 1>(codes, scales, x, y, N, stream);
+    }
     if constexpr (VARIANT == TQ_TERNARY) {
-        if constexpr (NU >= 2) {
-            if (pipe && K == (LPR * (NU - 1) + LPR / 4) * 64)
-                return launch_xreg_tail<LPR, NU - 1>(codes, scales, x, y, N, stream);
-        }
         if (pipe && exact) TQ_XL(false, true);
         else if (pipe) TQ_XL(true, true);
         else TQ_XL(true, false);
