@@ -147,6 +147,20 @@ __device__ __forceinline__ void aff_acc32(uint32_t d0, uint32_t d1, const uint32
     }
 }
 
+// 16 affine levels (dword d) against its pairs xp[p] = (x[p], x[p+8]),
+// accumulated into a in units of 2^-14 (one dword of aff_acc32).
+__device__ __forceinline__ void aff_acc16(uint32_t d, const uint32_t *xp, float &a, const Masks &k) {
+    const uint32_t c6 = d << 6, r6 = d >> 6;
+    a = dot2((d & k.m8) | 0x0C000C00u, xp[4], a);      // M4  slot 4
+    a = dot2((d & k.m6) | 0x14001400u, xp[3], a);      // M16 slot 3
+    a = dot2((d & k.m4) | 0x1C001C00u, xp[2], a);      // M64 slot 2
+    a = dot2((c6 & k.m8) | 0x0C000C00u, xp[1], a);     // M4  slot 1
+    a = dot2((c6 & k.m6) | 0x14001400u, xp[0], a);     // M16 slot 0
+    a = dot2((r6 & k.m8) | 0x0C000C00u, xp[7], a);     // M4  slot 7
+    a = dot2((r6 & k.m6) | 0x14001400u, xp[6], a);     // M16 slot 6
+    a = dot2((r6 & k.m4) | 0x1C001C00u, xp[5], a);     // M64 slot 5
+}
+
 // 64 binary bits (dwords d0, d1) against pairs xp[p] = (x[p], x[p+16]) of
 // each dword's 32 weights, accumulated into a: bit b at position 11 is
 // b * 2^-13 and at position q <= 10 under exponent field 12 - q it is
@@ -545,13 +559,13 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
     constexpr bool AFF = VARIANT == TQ_AFFINE2;
     static_assert(PIPE || VARIANT != TQ_BINARY, "binary codes take the pipelined loop only");
     // TAIL: a row is NU full chunk columns of the LPR lanes plus LPR / 4
-    // chunks more, which the lanes take one unit (one code dword: 16 2-bit or
-    // 32 1-bit weights) each in a tail slot (1-bit: lanes j < LPR / 2), where
+    // chunks more, which the lanes take one unit (one code dword: 16 2-bit
+    // codes or affine levels, or 32 1-bit weights) each in a tail slot (1-bit:
+    // lanes j < LPR / 2), where
     // a clamped fifth chunk column would leave three quarters of its lanes
     // decoding nothing
-    static_assert(!TAIL || ((VARIANT == TQ_TERNARY || VARIANT == TQ_BINARY) && PIPE && !RAGGED &&
-                            (LPR * NU) % 8 == 0),
-                  "the tail slot is a 2-bit or 1-bit, exact, pipelined layout with an even scale dword start");
+    static_assert(!TAIL || (PIPE && !RAGGED && (LPR * NU) % 8 == 0),
+                  "the tail slot is an exact, pipelined layout with an even scale dword start");
     constexpr int XN = XReg<VARIANT>::N;
     constexpr int UPC = XReg<VARIANT>::UPC, CB = XReg<VARIANT>::CB;
     constexpr int THREADS = 64 * WAVES;
@@ -653,11 +667,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         constexpr int TU = LPR * 16 / UW;                // tail units per row
         constexpr int CDW = CB / 4;                      // code dwords per chunk
         const int jt = min(j, TU - 1);
-        uint32_t ct = 0, st = 0, xt[TP + 1];
+        uint32_t ct = 0, st = 0, bt = 0, xt[TP + 2];
         const uint32_t hsh_t = ((uint32_t)(jt * UW / 128) & 1u) * 16u;
         auto load_tail = [&]() __attribute__((always_inline)) {
             if constexpr (TAIL) {
                 st = srow[(LPR * NU) / 4 + jt * UW / 256];
+                if constexpr (AFF) bt = brow[(LPR * NU) / 4 + jt * UW / 256];
                 ct = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(crow) + LPR * NU * CDW + jt);
             }
         };
@@ -676,6 +691,12 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
 #pragma unroll
                 for (int p = 0; p < TP; ++p) z = dot2(xt[p], XU::zweight(p), z);
                 xt[TP] = __builtin_bit_cast(uint32_t, z * -XU::kSeedScale);
+                if constexpr (AFF) {  // the unit's plain sum of x, in the accumulator unit
+                    float zs = 0.0f;
+#pragma unroll
+                    for (int p = 0; p < TP; ++p) zs = dot2(xt[p], 0x3C003C00u, zs);
+                    xt[TP + 1] = __builtin_bit_cast(uint32_t, zs * XU::kSeedScale);
+                }
             }
         };
         // Every wave of the workgroup issues its x loads before any wave
@@ -712,12 +733,15 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
                 float a = __builtin_bit_cast(float, xt[TP]);
                 if constexpr (VARIANT == TQ_TERNARY) {
                     tern_acc16(ct, xt, a, km);
+                } else if constexpr (AFF) {
+                    aff_acc16(ct, xt, a, km);
                 } else {
                     bin_slots(ct, xt, 11, 6, a, km);
                     bin_slots(ct << 6, xt, 5, 6, a, km);
                     bin_slots(ct >> 4, xt, 15, 4, a, km);
                 }
                 acc = __builtin_fmaf(half_bits(st >> hsh_t), a, acc);
+                if constexpr (AFF) acc = __builtin_fmaf(half_bits(bt >> hsh_t), __builtin_bit_cast(float, xt[TP + 1]), acc);
                 if constexpr (decltype(refill)::value) load_tail();
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -898,19 +922,19 @@ constexpr size_t lds_bytes_xreg() {
 }
 
 // A row of exactly LPR NU full chunk columns plus LPR / 4 chunks (one unit
-// per lane: 16 2-bit weights, or 32 1-bit weights on half the lanes): codes
-// on the pipelined loop take the tail slot instead of a fifth, mostly
-// clamped, chunk column.
+// per lane: 16 2-bit codes or affine levels, or 32 1-bit weights on half the
+// lanes): codes on the pipelined loop take the tail slot instead of a fifth,
+// mostly clamped, chunk column.
 template <int VARIANT, int LPR, int NU>
-hipError_t launch_xreg_tail(const uint8_t *codes, const uint16_t *scales, const uint16_t *x, float *y, int N,
-                            hipStream_t stream) {
+hipError_t launch_xreg_tail(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
+                            const uint16_t *x, float *y, int N, hipStream_t stream) {
     constexpr int RS = 64 / LPR;
     constexpr int K = (LPR * NU + LPR / 4) * 64;
     const int nblocks = (N + RS - 1) / RS;
     const int grid = max(1, min(device_cus(), (nblocks + kXregWaves - 1) / kXregWaves));
     constexpr size_t lds = lds_bytes_xreg<VARIANT, LPR, NU, true>();
     hipLaunchKernelGGL((gemv_xreg_kernel<VARIANT, LPR, NU, kXregWaves, false, true, true>), dim3(grid),
-                       dim3(64 * kXregWaves), lds, stream, codes, scales, nullptr, x, y, N, K);
+                       dim3(64 * kXregWaves), lds, stream, codes, scales, biases, x, y, N, K);
     return hipGetLastError();
 }
 
@@ -929,9 +953,9 @@ hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint1
 #define TQ_XL(R, P)                                                                               \
     hipLaunchKernelGGL((gemv_xreg_kernel<VARIANT, LPR, NU, kXregWaves, R, P>), dim3(grid),         \
                        dim3(64 * kXregWaves), lds, stream, codes, scales, biases, x, y, N, K)
-    if constexpr (VARIANT != TQ_AFFINE2 && NU >= 2) {
+    if constexpr (NU >= 2) {
         if (pipe && K == (LPR * (NU - 1) + LPR / 4) * 64)
-            return launch_xreg_tail<VARIANT, LPR, NU - 1>(codes, scales, x, y, N, stream);
+            return launch_xreg_tail<VARIANT, LPR, NU - 1>(codes, scales, biases, x, y, N, stream);
     }
     if constexpr (VARIANT == TQ_TERNARY) {
         if (pipe && exact) TQ_XL(false, true);
