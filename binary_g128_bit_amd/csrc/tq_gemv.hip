@@ -957,6 +957,22 @@ hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint1
         if (pipe && K == (LPR * (NU - 1) + LPR / 4) * 64)
             return launch_xreg_tail<VARIANT, LPR, NU - 1>(codes, scales, biases, x, y, N, stream);
     }
+    // Few rows: a shape with several rows per wave block leaves at least half
+    // the waves without a block, where one row per block over 64 lanes (full
+    // columns plus the tail slot) gives every wave work: 1024 x 5120
+    // 4.06 -> 2.93 us, 2048 x 5120 4.17 -> 3.12, 4096 x 5120 4.43 -> 3.95,
+    // 2048 x 9216 4.55 -> 3.71.  From 6144 rows (three quarters of the waves
+    // busy) the 64-lane rows, with their longer row sums, measured slower.
+    if constexpr (LPR < 64) {
+        if (pipe && (N + RS - 1) / RS <= kXregWaves / 2 * device_cus()) {
+            switch (K) {
+                case (64 * 1 + 16) * 64: return launch_xreg_tail<VARIANT, 64, 1>(codes, scales, biases, x, y, N, stream);
+                case (64 * 2 + 16) * 64: return launch_xreg_tail<VARIANT, 64, 2>(codes, scales, biases, x, y, N, stream);
+                case (64 * 3 + 16) * 64: return launch_xreg_tail<VARIANT, 64, 3>(codes, scales, biases, x, y, N, stream);
+                default: break;
+            }
+        }
+    }
     if constexpr (VARIANT == TQ_TERNARY) {
         if (pipe && exact) TQ_XL(false, true);
         else if (pipe) TQ_XL(true, true);
