@@ -547,7 +547,7 @@ __device__ __forceinline__ void load_bias(const uint16_t *__restrict__ biases, i
 // value: 16-bit registers are packed in pairs, and the packing waits for both
 // loads).  Otherwise a plain ping-pong of two register sets, each loaded whole
 // one block ahead.
-template <int VARIANT, int LPR, int NU, int WAVES, bool RAGGED, bool PIPE, bool TAIL = false>
+template <int VARIANT, int LPR, int NU, int WAVES, bool RAGGED, bool PIPE, int TW = 0>
 __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__restrict__ codes,
                                                                const uint16_t *__restrict__ scales,
                                                                const uint16_t *__restrict__ biases,
@@ -558,19 +558,20 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
     using Code = typename XReg<VARIANT>::Code;
     constexpr bool AFF = VARIANT == TQ_AFFINE2;
     static_assert(PIPE || VARIANT != TQ_BINARY, "binary codes take the pipelined loop only");
-    // TAIL: a row is NU full chunk columns of the LPR lanes plus LPR / 4
-    // chunks more, which the lanes take one unit (one code dword: 16 2-bit
-    // codes or affine levels, or 32 1-bit weights) each in a tail slot (1-bit:
-    // lanes j < LPR / 2), where
-    // a clamped fifth chunk column would leave three quarters of its lanes
-    // decoding nothing
+    // TW (tail weights per lane, 16 or 32): a row is NU full chunk columns of
+    // the LPR lanes plus LPR TW / 64 chunks more, which the lanes take TW
+    // weights each in a tail slot (one or two code dwords of 2-bit codes or
+    // affine levels; one 1-bit dword, on lanes j < LPR TW / 32), where a
+    // clamped extra chunk column would leave most of its lanes decoding nothing
+    constexpr bool TAIL = TW != 0;
+    static_assert(TW == 0 || TW == 16 || TW == 32, "a tail slot takes 16 or 32 weights per lane");
     static_assert(!TAIL || (PIPE && !RAGGED && (LPR * NU) % 8 == 0),
                   "the tail slot is an exact, pipelined layout with an even scale dword start");
     constexpr int XN = XReg<VARIANT>::N;
     constexpr int UPC = XReg<VARIANT>::UPC, CB = XReg<VARIANT>::CB;
     constexpr int THREADS = 64 * WAVES;
     constexpr int RS = 64 / LPR;  // rows per block (one per lane segment)
-    constexpr int CAP = LPR * NU + (TAIL ? LPR / 4 : 0);  // staged chunk slots
+    constexpr int CAP = LPR * NU + LPR * TW / 64;  // staged chunk slots
     constexpr int XMAX = (CAP * UPC + THREADS - 1) / THREADS;
     const int G = K >> 7, CPR = 2 * G;  // 64-weight chunks per row
     const int nunits = CPR * UPC;
@@ -658,44 +659,49 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
         };
         Code ca[NU];
         uint32_t sa[NU], ba[NU];
-        // tail slot (TAIL): unit j of the row's last LPR / 4 chunks (TU units,
-        // one code dword of UW weights each); its group is LPR NU / 2 +
-        // UW j / 128, in scale dword LPR NU / 4 + UW j / 256 at half
-        // (UW j / 128) & 1 (LPR NU is a multiple of 8).  1-bit lanes
-        // j >= TU load the last unit and hold zero activations.
+        // tail slot (TW): lane j takes UL units (UL code dwords of UW weights)
+        // from unit UL j of the row's last LPR TW / 64 chunks; their group is
+        // LPR NU / 2 + UW UL j / 128, in scale dword LPR NU / 4 + UW UL j / 256
+        // at half (UW UL j / 128) & 1 (LPR NU is a multiple of 8).  1-bit
+        // lanes j >= TU load the last unit and hold zero activations.
         constexpr int UW = XU::UNIT, TP = UW / 2;        // weights and pair dwords per unit
-        constexpr int TU = LPR * 16 / UW;                // tail units per row
+        constexpr int UL = TW > UW ? TW / UW : 1;        // units per lane
+        constexpr int TU = TW ? LPR * TW / UW / UL : 1;  // lanes with tail units
         constexpr int CDW = CB / 4;                      // code dwords per chunk
+        using TCode = typename std::conditional<UL == 2, u32x2, uint32_t>::type;
         const int jt = min(j, TU - 1);
-        uint32_t ct = 0, st = 0, bt = 0, xt[TP + 2];
-        const uint32_t hsh_t = ((uint32_t)(jt * UW / 128) & 1u) * 16u;
+        TCode ct{};
+        uint32_t st = 0, bt = 0, xt[UL * TP + 2];
+        const uint32_t hsh_t = ((uint32_t)(jt * UL * UW / 128) & 1u) * 16u;
         auto load_tail = [&]() __attribute__((always_inline)) {
             if constexpr (TAIL) {
-                st = srow[(LPR * NU) / 4 + jt * UW / 256];
-                if constexpr (AFF) bt = brow[(LPR * NU) / 4 + jt * UW / 256];
-                ct = __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(crow) + LPR * NU * CDW + jt);
+                st = srow[(LPR * NU) / 4 + jt * UL * UW / 256];
+                if constexpr (AFF) bt = brow[(LPR * NU) / 4 + jt * UL * UW / 256];
+                ct = __builtin_nontemporal_load(
+                    reinterpret_cast<const TCode *>(reinterpret_cast<const uint32_t *>(crow) + LPR * NU * CDW) + jt);
             }
         };
-        // the unit's pairs from its chunk slot and its own seed (the chunk
-        // constant covers all the units of a chunk)
+        // the units' pairs from their chunk slot and their own seed (the
+        // chunk constant covers all the units of a chunk)
         auto fill_tail = [&]() __attribute__((always_inline)) {
             if constexpr (TAIL) {
-                const uint32_t *slot = xs + (LPR * NU + jt / UPC) * XU::CHUNK_DW + (jt % UPC) * TP;
+                const int u0 = jt * UL;
+                const uint32_t *slot = xs + (LPR * NU + u0 / UPC) * XU::CHUNK_DW + (u0 % UPC) * TP;
                 float z = 0.0f;
 #pragma unroll
-                for (int q = 0; q < TP / 4; ++q) {
+                for (int q = 0; q < UL * TP / 4; ++q) {
                     const u32x4 v = reinterpret_cast<const u32x4 *>(slot)[q];
 #pragma unroll
                     for (int p = 0; p < 4; ++p) xt[4 * q + p] = j < TU ? v[p] : 0u;
                 }
 #pragma unroll
-                for (int p = 0; p < TP; ++p) z = dot2(xt[p], XU::zweight(p), z);
-                xt[TP] = __builtin_bit_cast(uint32_t, z * -XU::kSeedScale);
-                if constexpr (AFF) {  // the unit's plain sum of x, in the accumulator unit
+                for (int p = 0; p < UL * TP; ++p) z = dot2(xt[p], XU::zweight(p % TP), z);
+                xt[UL * TP] = __builtin_bit_cast(uint32_t, z * -XU::kSeedScale);
+                if constexpr (AFF) {  // the units' plain sum of x, in the accumulator unit
                     float zs = 0.0f;
 #pragma unroll
-                    for (int p = 0; p < TP; ++p) zs = dot2(xt[p], 0x3C003C00u, zs);
-                    xt[TP + 1] = __builtin_bit_cast(uint32_t, zs * XU::kSeedScale);
+                    for (int p = 0; p < UL * TP; ++p) zs = dot2(xt[p], 0x3C003C00u, zs);
+                    xt[UL * TP + 1] = __builtin_bit_cast(uint32_t, zs * XU::kSeedScale);
                 }
             }
         };
@@ -730,8 +736,11 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
                 __builtin_amdgcn_sched_barrier(0);
             }
             if constexpr (TAIL) {
-                float a = __builtin_bit_cast(float, xt[TP]);
-                if constexpr (VARIANT == TQ_TERNARY) {
+                float a = __builtin_bit_cast(float, xt[UL * TP]);
+                if constexpr (UL == 2) {
+                    if constexpr (AFF) aff_acc32(ct[0], ct[1], xt, xt + TP, a, km);
+                    else tern_acc32(ct[0], ct[1], xt, xt + TP, a, km);
+                } else if constexpr (VARIANT == TQ_TERNARY) {
                     tern_acc16(ct, xt, a, km);
                 } else if constexpr (AFF) {
                     aff_acc16(ct, xt, a, km);
@@ -741,7 +750,8 @@ __global__ __launch_bounds__(64 * WAVES) void gemv_xreg_kernel(const uint8_t *__
                     bin_slots(ct >> 4, xt, 15, 4, a, km);
                 }
                 acc = __builtin_fmaf(half_bits(st >> hsh_t), a, acc);
-                if constexpr (AFF) acc = __builtin_fmaf(half_bits(bt >> hsh_t), __builtin_bit_cast(float, xt[TP + 1]), acc);
+                if constexpr (AFF)
+                    acc = __builtin_fmaf(half_bits(bt >> hsh_t), __builtin_bit_cast(float, xt[UL * TP + 1]), acc);
                 if constexpr (decltype(refill)::value) load_tail();
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -916,24 +926,24 @@ Config pick_xreg(int cpr) {
     return best;
 }
 
-template <int VARIANT, int LPR, int NU, bool TAIL = false>
+template <int VARIANT, int LPR, int NU, int TW = 0>
 constexpr size_t lds_bytes_xreg() {
-    return (size_t)(LPR * NU + (TAIL ? LPR / 4 : 0)) * XReg<VARIANT>::Unit::CHUNK_DW * sizeof(uint32_t);
+    return (size_t)(LPR * NU + LPR * TW / 64) * XReg<VARIANT>::Unit::CHUNK_DW * sizeof(uint32_t);
 }
 
 // A row of exactly LPR NU full chunk columns plus LPR / 4 chunks (one unit
 // per lane: 16 2-bit codes or affine levels, or 32 1-bit weights on half the
 // lanes): codes on the pipelined loop take the tail slot instead of a fifth,
 // mostly clamped, chunk column.
-template <int VARIANT, int LPR, int NU>
+template <int VARIANT, int LPR, int NU, int TW = 16>
 hipError_t launch_xreg_tail(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
                             const uint16_t *x, float *y, int N, hipStream_t stream) {
     constexpr int RS = 64 / LPR;
-    constexpr int K = (LPR * NU + LPR / 4) * 64;
+    constexpr int K = (LPR * NU + LPR * TW / 64) * 64;
     const int nblocks = (N + RS - 1) / RS;
     const int grid = max(1, min(device_cus(), (nblocks + kXregWaves - 1) / kXregWaves));
-    constexpr size_t lds = lds_bytes_xreg<VARIANT, LPR, NU, true>();
-    hipLaunchKernelGGL((gemv_xreg_kernel<VARIANT, LPR, NU, kXregWaves, false, true, true>), dim3(grid),
+    constexpr size_t lds = lds_bytes_xreg<VARIANT, LPR, NU, TW>();
+    hipLaunchKernelGGL((gemv_xreg_kernel<VARIANT, LPR, NU, kXregWaves, false, true, TW>), dim3(grid),
                        dim3(64 * kXregWaves), lds, stream, codes, scales, biases, x, y, N, K);
     return hipGetLastError();
 }
@@ -955,7 +965,9 @@ hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint1
                        dim3(64 * kXregWaves), lds, stream, codes, scales, biases, x, y, N, K)
     if constexpr (NU >= 2) {
         if (pipe && K == (LPR * (NU - 1) + LPR / 4) * 64)
-            return launch_xreg_tail<VARIANT, LPR, NU - 1>(codes, scales, biases, x, y, N, stream);
+            return launch_xreg_tail<VARIANT, LPR, NU - 1, 16>(codes, scales, biases, x, y, N, stream);
+        if (pipe && K == (LPR * (NU - 1) + LPR / 2) * 64)
+            return launch_xreg_tail<VARIANT, LPR, NU - 1, 32>(codes, scales, biases, x, y, N, stream);
     }
     // Few rows: a shape with several rows per wave block leaves at least half
     // the waves without a block, where one row per block over 64 lanes (full
@@ -966,9 +978,10 @@ hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint1
     if constexpr (LPR < 64) {
         if (pipe && (N + RS - 1) / RS <= kXregWaves / 2 * device_cus()) {
             switch (K) {
-                case (64 * 1 + 16) * 64: return launch_xreg_tail<VARIANT, 64, 1>(codes, scales, biases, x, y, N, stream);
-                case (64 * 2 + 16) * 64: return launch_xreg_tail<VARIANT, 64, 2>(codes, scales, biases, x, y, N, stream);
-                case (64 * 3 + 16) * 64: return launch_xreg_tail<VARIANT, 64, 3>(codes, scales, biases, x, y, N, stream);
+#define TQ_XT(n, tw) \
+    case (64 * n + tw) * 64: return launch_xreg_tail<VARIANT, 64, n, tw>(codes, scales, biases, x, y, N, stream);
+                TQ_XT(1, 16) TQ_XT(2, 16) TQ_XT(3, 16) TQ_XT(1, 32) TQ_XT(2, 32) TQ_XT(3, 32)
+#undef TQ_XT
                 default: break;
             }
         }
