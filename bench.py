@@ -36,7 +36,7 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E, vendor figure
 PEAK_F16_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA, vendor figure
 STACK_BYTES = 6_595_543_040  # packed bytes of the 64-layer 24.83B-weight stack
 COPY_BYTES = 1 << 30         # bytes read (and written) by the calibration copy
-GEMV_KERNEL_NAME = ("gemv_xreg_kernel<0,16,5,8,false,true,false> (ternary, pipelined) "
+GEMV_KERNEL_NAME = ("gemv_xreg_kernel<0,16,5,8,false,true,0> (ternary, pipelined) "
                     "on [gate;up] 34816x5120")
 
 
@@ -783,7 +783,7 @@ def pmc_summary(paths):
             print("    %-28s median %.6g  (n=%d)" % (cn, vs[len(vs) // 2], len(vs)))
 
 
-TRAFFIC_KERNEL = "gemv_xreg_kernel<0, 16, 5, 8, false, true, false>"   # the fused [gate;up] launch's template
+TRAFFIC_KERNEL = "gemv_xreg_kernel<0, 16, 5, 8, false, true, 0>"   # the fused [gate;up] launch's template
 TRAFFIC_GRID = "131072"
 
 
