@@ -78,6 +78,9 @@ def parse():
     p.add_argument("--pmc-summary", metavar="CSV", nargs="+",
                    help="summarise rocprofv3 counter_collection.csv files (median per kernel and grid) "
                         "and exit")
+    p.add_argument("--timed-steps-only", action="store_true",
+                   help="run the warm-up and the timed steps only (the fused [gate;up] and down launches "
+                        "and nothing else, for counter passes), print the step time and exit")
     p.add_argument("--traffic-json", metavar="CSV", nargs=4,
                    help="write the fused GEMV's HBM traffic summary from four rocprofv3 counter files: "
                         "FETCH_SIZE and WRITE_SIZE of `--only-step`, then of `--copy-calibration`; "
@@ -944,6 +947,10 @@ def main():
     gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
 
     log("timed step done: %.3f us/step" % (ms_per_step * 1e3))
+    if args.timed_steps_only:
+        print(json.dumps({"timed_steps_only": True, "steps": args.steps, "warmup_steps": warmup_steps,
+                          "us_per_step": round(ms_per_step * 1e3, 3), "gbs": round(gbs, 2)}), flush=True)
+        return
     # ---- dominant kernel: the fused 34816x5120 GEMV
     launches = 100
 
