@@ -126,10 +126,12 @@ def test_gemv_full_size(N, K, variant):
     assert np.array_equal(Y.astype(np.float64), Yref)
 
 
-def test_gemv_special_values():
+@pytest.mark.parametrize("K", [1024, 5120, 17408])
+def test_gemv_special_values(K):
     """Negative and subnormal scales, subnormal and zero activations, all-zero
-    and all-one trits."""
-    N, K = 64, 1024
+    and all-one trits (K = 5120 at 64 rows and K = 17408 run the tail-slot
+    layouts)."""
+    N = 64
     g = synth.rng(31)
     t = synth.trits(g, N, K, TERN)
     t[0] = 0
@@ -145,8 +147,9 @@ def test_gemv_special_values():
     Y = gpu_gemm(codes, s, X, TERN, N, K)
     Yref, A = oracle.gemm(codes, s, X, N, K, TERN)
     assert_tol(Y, Yref, A, "special")
-    # all-zero trits: only the rounding residue of the per-group offsets remains
-    assert abs(Y[0, 0]) <= 1e-6
+    # all-zero trits: only the rounding residue of the per-group offsets
+    # remains (it grows with the number of chunks summed)
+    assert abs(Y[0, 0]) <= (1e-6 if K <= 1024 else 1e-5)
 
 
 @pytest.mark.parametrize("p_zero", [0.9, 0.99, 1.0])
