@@ -931,10 +931,10 @@ constexpr size_t lds_bytes_xreg() {
     return (size_t)(LPR * NU + LPR * TW / 64) * XReg<VARIANT>::Unit::CHUNK_DW * sizeof(uint32_t);
 }
 
-// A row of exactly LPR NU full chunk columns plus LPR / 4 chunks (one unit
-// per lane: 16 2-bit codes or affine levels, or 32 1-bit weights on half the
-// lanes): codes on the pipelined loop take the tail slot instead of a fifth,
-// mostly clamped, chunk column.
+// A row of exactly LPR NU full chunk columns plus LPR TW / 64 chunks (TW = 16
+// or 32 weights per lane: one or two dwords of 2-bit codes or affine levels,
+// or one 1-bit dword on the first LPR TW / 32 lanes): codes on the pipelined
+// loop take the tail slot instead of an extra, mostly clamped, chunk column.
 template <int VARIANT, int LPR, int NU, int TW = 16>
 hipError_t launch_xreg_tail(const uint8_t *codes, const uint16_t *scales, const uint16_t *biases,
                             const uint16_t *x, float *y, int N, hipStream_t stream) {
