@@ -975,6 +975,20 @@ hipError_t launch_xreg(const uint8_t *codes, const uint16_t *scales, const uint1
     // 4.06 -> 2.93 us, 2048 x 5120 4.17 -> 3.12, 4096 x 5120 4.43 -> 3.95,
     // 2048 x 9216 4.55 -> 3.71.  From 6144 rows (three quarters of the waves
     // busy) the 64-lane rows, with their longer row sums, measured slower.
+    // At most one block per wave on 16 lanes per row (5120-wide rows: 4096 to
+    // 8192 rows): 32 lanes per row (two full columns and a 32-weight tail)
+    // halve the activation registers and give waves two blocks.  Two runs,
+    // same process: 2-bit 4100 x 5120 4.47 -> 3.84 us, 5120 x 5120 4.64 ->
+    // 4.22, 6144 x 5120 4.75 -> 4.31, 8192 x 5120 within 1 %; affine 6144
+    // and 8192 rows 5.06 -> 4.42 and 5.22 -> 4.97; 1-bit 6144 rows 4.37 ->
+    // 4.12 but 8192 rows (exactly one block per wave) 4.46 -> 4.81, so 1-bit
+    // codes stop below one block per wave.  12288 rows measured 0.5 us slower.
+    if constexpr (LPR == 16) {
+        const int nb = (N + RS - 1) / RS, waves = kXregWaves * device_cus();
+        if (pipe && K == (32 * 2 + 16) * 64 && nb > waves / 2 &&
+            (VARIANT == TQ_BINARY ? nb < waves : nb <= waves))
+            return launch_xreg_tail<VARIANT, 32, 2, 32>(codes, scales, biases, x, y, N, stream);
+    }
     if constexpr (LPR < 64) {
         if (pipe && (N + RS - 1) / RS <= kXregWaves / 2 * device_cus()) {
             switch (K) {

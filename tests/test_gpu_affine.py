@@ -41,7 +41,7 @@ def assert_tol(y, yref, A, what=""):
 
 
 SHAPES = [(1, 128), (7, 256), (33, 384), (100, 640), (1000, 1024), (257, 5120), (129, 6144),
-          (65, 17408), (3, 20480), (300, 2176), (300, 9216), (100, 4608), (2048, 6144)]
+          (65, 17408), (3, 20480), (300, 2176), (300, 9216), (100, 4608), (2048, 6144), (6144, 5120)]
 
 
 @pytest.mark.parametrize("N,K", SHAPES)

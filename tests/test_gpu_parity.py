@@ -52,7 +52,7 @@ def case(seed, N, K, M, variant, exact):
 SHAPES = [(1, 128), (7, 256), (33, 384), (100, 640), (1000, 1024), (257, 5120),
           (65, 17408), (9, 20480), (3, 29952), (129, 6144), (5, 65536), (70, 2176),
           (4096, 5120), (4100, 5120), (300, 9216), (97, 13312),
-          (100, 4608), (99, 4608), (40, 14336), (2048, 6144), (1000, 10240)]
+          (100, 4608), (99, 4608), (40, 14336), (2048, 6144), (1000, 10240), (6144, 5120), (8193, 5120)]
 
 
 @pytest.mark.parametrize("variant", [TERN, BIN])
