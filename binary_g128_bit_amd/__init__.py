@@ -10,6 +10,7 @@ Build the library first: ``python -m binary_g128_bit_amd.build``.  There is no
 fallback: calling a GPU entry point without the built library raises.
 """
 import ctypes
+import functools
 import os
 
 import numpy as np
@@ -166,12 +167,18 @@ def _stream(stream, tensor):
         return ctypes.c_void_p(torch.cuda.current_stream(tensor.device).cuda_stream)
 
 
+@functools.lru_cache(maxsize=1024)
+def _codes_bytes(N, K, variant):
+    # the library's byte count for a shape, asked once per shape: a ctypes
+    # call costs about a microsecond of host time on every launch
+    return lib().tq_codes_bytes(N, K, variant)
+
+
 def _shape_checks(codes, scales, K, variant):
-    import torch  # noqa: F401
     N = scales.shape[0]
     if scales.dim() != 2 or scales.shape[1] * GROUP != K:
         raise ValueError("scales must be [N][K/128] with K=%d" % K)
-    need = lib().tq_codes_bytes(N, K, variant)
+    need = _codes_bytes(N, K, variant)
     if codes.numel() != need:
         raise ValueError("codes holds %d bytes, %d needed for N=%d K=%d" % (codes.numel(), need, N, K))
     return N
