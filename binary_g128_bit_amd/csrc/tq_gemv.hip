@@ -196,6 +196,18 @@ __device__ __forceinline__ float dpp_f(float v) {
                                                                  0xF, 0xF, false));
 }
 
+// v + (v of the lane W = 16 or 32 away, within 2W-lane groups): a
+// v_permlane16/32_swap of v with itself leaves the lane's own value in one
+// result and its partner's in the other, so their sum is what a lane-xor
+// shuffle gives, on the VALU instead of through the LDS crossbar.
+template <int W>
+__device__ __forceinline__ float swap_sum(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto e = W == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                           : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)e[0]) + __builtin_bit_cast(float, (uint32_t)e[1]);
+}
+
 // Sum over aligned segments of LPR lanes; every lane of a segment gets the sum.
 template <int LPR>
 __device__ __forceinline__ float seg_sum(float v) {
@@ -203,8 +215,8 @@ __device__ __forceinline__ float seg_sum(float v) {
     if (LPR >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
     if (LPR >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
     if (LPR >= 16) v += dpp_f<0x140>(v); // row_mirror
-    if (LPR >= 32) v += __shfl_xor(v, 16);
-    if (LPR >= 64) v += __shfl_xor(v, 32);
+    if (LPR >= 32) v = swap_sum<16>(v);
+    if (LPR >= 64) v = swap_sum<32>(v);
     return v;
 }
 
