@@ -74,6 +74,31 @@ __device__ __forceinline__ half8 decode8(uint32_t w, uint32_t mask) {
 
 __device__ __forceinline__ float xor_max(float v, int m) { return fmaxf(v, __shfl_xor(v, m)); }
 
+// v with the value of the lane W = 16 or 32 away (within 2W-lane groups)
+// combined by sum or max: a v_permlane16/32_swap of v with itself leaves the
+// lane's own value in one result and its partner's in the other, so this is
+// the lane-xor shuffle's result on the VALU, without the LDS crossbar.
+template <int W>
+__device__ __forceinline__ void swap_pair(float v, float &a, float &b) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto e = W == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                           : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __builtin_bit_cast(float, (uint32_t)e[0]);
+    b = __builtin_bit_cast(float, (uint32_t)e[1]);
+}
+template <int W>
+__device__ __forceinline__ float swap_sum(float v) {
+    float a, b;
+    swap_pair<W>(v, a, b);
+    return a + b;
+}
+template <int W>
+__device__ __forceinline__ float swap_max(float v) {
+    float a, b;
+    swap_pair<W>(v, a, b);
+    return fmaxf(a, b);
+}
+
 // ---------------------------------------------------------------- append
 // One workgroup per (token, KV head), one thread per dimension.  A group of
 // 32 dimensions is half a wave: its maximum comes from xor shuffles.
@@ -217,8 +242,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
         sq = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v1), one2, sq, false);
         sq = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v2), one2, sq, false);
         sq = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, v3), one2, sq, false);
-        sq += __shfl_xor(sq, 16);
-        sq += __shfl_xor(sq, 32);
+        sq = swap_sum<16>(sq);
+        sq = swap_sum<32>(sq);
         qs24[g] = -24.0f * sq;
     }
 
@@ -272,8 +297,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
         // online softmax over the tile
         float mt = fmaxf(fmaxf(fmaxf(z[0][0], z[0][1]), fmaxf(z[0][2], z[0][3])),
                          fmaxf(fmaxf(z[1][0], z[1][1]), fmaxf(z[1][2], z[1][3])));
-        mt = xor_max(mt, 16);
-        mt = xor_max(mt, 32);
+        mt = swap_max<16>(mt);
+        mt = swap_max<32>(mt);
         const float mn = fmaxf(m, mt);
         // the running maximum moves only when a score passes it by more than
         // 2 (log2 domain): the probabilities below stay <= 4, so p d_V stays
@@ -351,12 +376,12 @@ __global__ __launch_bounds__(64 * kWaves) void attn_partial_kernel(
     // this wave's (max, sum, output) per head into LDS, over its own ring
     // once every load into it has landed: O = D - 24 cs
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lsum += __shfl_xor(lsum, 16);
-    lsum += __shfl_xor(lsum, 32);
+    lsum = swap_sum<16>(lsum);
+    lsum = swap_sum<32>(lsum);
 #pragma unroll
     for (int g = 0; g < 8; ++g) {
-        cs[g] += __shfl_xor(cs[g], 16);
-        cs[g] += __shfl_xor(cs[g], 32);
+        cs[g] = swap_sum<16>(cs[g]);
+        cs[g] = swap_sum<32>(cs[g]);
     }
     float *red = reinterpret_cast<float *>(ring);  // [16][kHD + 2]
 #pragma unroll
