@@ -99,6 +99,30 @@ __device__ __forceinline__ float swap_max(float v) {
     return fmaxf(a, b);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF,
+                                                                 false));
+}
+
+// Sum and maximum over the whole wave, every lane getting the result: DPP
+// within 16-lane rows (quad_perm [1,0,3,2], [2,3,0,1], row_half_mirror,
+// row_mirror), then the permlane exchanges across rows and halves.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_f<0xB1>(v);
+    v += dpp_f<0x4E>(v);
+    v += dpp_f<0x141>(v);
+    v += dpp_f<0x140>(v);
+    return swap_sum<32>(swap_sum<16>(v));
+}
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    return swap_max<32>(swap_max<16>(v));
+}
+
 // ---------------------------------------------------------------- append
 // One workgroup per (token, KV head), one thread per dimension.  A group of
 // 32 dimensions is half a wave: its maximum comes from xor shuffles.
@@ -461,14 +485,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float *__restri
 #pragma unroll
         for (int i = 0; i < kMergeRound; ++i) o[i] = base[(r + min(i, last)) * stride + dim];
         float mx = m;
-#pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) mx = fmaxf(mx, __shfl_xor(mx, s));
+        mx = wave_max(mx);
         const float mn = fmaxf(M, mx);
         const float alpha = exp2f(M - mn);  // 0 on the first round
         const float e = lane <= last ? exp2f(m - mn) : 0.0f;
         float dr = e * l;
-#pragma unroll
-        for (int s = 32; s >= 1; s >>= 1) dr += __shfl_xor(dr, s);
+        dr = wave_sum(dr);
         float nr = 0.0f;
 #pragma unroll
         for (int i = 0; i < kMergeRound; ++i)
