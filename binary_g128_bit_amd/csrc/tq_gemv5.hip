@@ -62,14 +62,25 @@ __device__ __forceinline__ float dpp_f(float v) {
                                                                  0xF, 0xF, false));
 }
 
+// v + (v of the lane W = 16 or 32 away, within 2W-lane groups) by a
+// v_permlane16/32_swap of v with itself (own and partner value, added), on
+// the VALU instead of the LDS crossbar of a lane shuffle.
+template <int W>
+__device__ __forceinline__ float swap_sum(float v) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, v);
+    const auto e = W == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                           : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, (uint32_t)e[0]) + __builtin_bit_cast(float, (uint32_t)e[1]);
+}
+
 template <int LPR>
 __device__ __forceinline__ float seg_sum(float v) {
     if (LPR >= 2) v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
     if (LPR >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
     if (LPR >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
     if (LPR >= 16) v += dpp_f<0x140>(v); // row_mirror
-    if (LPR >= 32) v += __shfl_xor(v, 16);
-    if (LPR >= 64) v += __shfl_xor(v, 32);
+    if (LPR >= 32) v = swap_sum<16>(v);
+    if (LPR >= 64) v = swap_sum<32>(v);
     return v;
 }
 
